@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 QLoRA linear hot path on one MI355X.
+
+One step = the whole path over one batch of the Llama-7B-shaped MLP workload
+(gate and up 4096->11008, down 11008->4096; M = 4096 tokens = batch 4 x seq
+1024; LoRA rank 64, alpha 16; weights fp32 N(0, 0.02^2)): for each of the three
+linears, NF4 quantization with double quantization of the fp32 weight, the
+fused dequant-GEMM forward (saving T) and the backward (dX, dA, dB).  Inputs are
+seeded synthetic data resident in HBM before the timed region.
+
+value = fwd+bwd algorithmic FLOP per step / step time (quantization time is in
+the denominator).  Algorithmic FLOP per linear: 4*M*N*K + 6*M*r*(K+N).
+
+Extra objects on the JSON line:
+  roofline      the dominant kernel (by total time) measured live with HIP
+                events recorded around its launches inside the timed steps;
+  gemv          the dequant-GEMV forward of the 4096x4096 q_proj at M = 1 and
+                M = 16, cycling through 64 quantized copies (about 0.55 GB, more
+                than twice the 256 MB last-level cache) so every launch streams
+                from HBM;
+  cpu_baseline  the oracle (numpy, fp64) on a bounded sample: the gate linear
+                alone (quantize + dequantize + forward + backward at M = 4096).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QLoRA NF4 linear fwd+bwd TFLOP/s @7B MLP M=4096; dequant-GEMV GB/s @M=1"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def linear_flops(M, N, K, r):
+    return 4 * M * N * K + 6 * M * r * (K + N)
+
+
+def gemv_kernel_bytes(M, N, K, r):
+    """Bytes the GEMV kernel must move: packed codes, e4m3 constants, group
+    scales, mean, X, B, T (fp32) in; Y (bf16) out."""
+    nb = N * K // 64
+    ng = (nb + 255) // 256
+    return N * K // 2 + nb + 4 * ng + 4 + 2 * M * K + 2 * N * r + 4 * M * r + 2 * M * N
+
+
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def timed_events(torch, n):
+    evs = []
+    s = torch.cuda.current_stream()
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)  # materialise the underlying HIP events
+        b.record(s)
+        evs.append((a, b))
+    return evs
+
+
+def run_mlp(torch, q, args):
+    from workloads import Inputs
+
+    w = Inputs(3)
+    M, r, alpha = w.w.tokens[0], w.w.rank, w.w.alpha
+    layers = []
+    for li, (name, N, K) in enumerate(w.w.layers):
+        t0 = time.time()
+        L = {"name": name, "N": N, "K": K}
+        L["W"] = torch.from_numpy(w.weight(li)).cuda()
+        L["X"] = dev_bf16(torch, w.X(li, M))
+        L["dY"] = dev_bf16(torch, w.dY(li, M))
+        L["A"] = dev_bf16(torch, w.lora_A(li))
+        L["B"] = dev_bf16(torch, w.lora_B(li))
+        sz = q.qlora_nf4_sizes(N, K, M, r)
+        L["qt"] = q.Nf4Tensor.empty(N, K)
+        L["wsq"] = q.workspace(sz["quantize_ws_bytes"])
+        L["wsf"] = q.workspace(sz["fwd_ws_bytes"])
+        L["wsb"] = q.workspace(sz["bwd_ws_bytes"])
+        L["Y"] = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        L["T"] = torch.empty(M, r, dtype=torch.float32, device="cuda")
+        L["dX"] = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        L["dA"] = torch.empty(r, K, dtype=torch.float32, device="cuda")
+        L["dB"] = torch.empty(N, r, dtype=torch.float32, device="cuda")
+        layers.append(L)
+        log(f"[bench] inputs of {name} {N}x{K} ready ({time.time() - t0:.1f}s)")
+
+    kinds = ("quantize", "fwd_gemm", "dx_gemm")
+    kid = {"quantize": q.QLORA_KERNEL_QUANTIZE, "fwd_gemm": q.QLORA_KERNEL_FWD_GEMM,
+           "dx_gemm": q.QLORA_KERNEL_DX_GEMM}
+    events = {k: timed_events(torch, args.steps * len(layers)) for k in kinds}
+
+    def step(i=None):
+        for li, L in enumerate(layers):
+            j = None if i is None else i * len(layers) + li
+            if j is not None:
+                q.qlora_time_next_launch(kid["quantize"], *events["quantize"][j])
+            q.qlora_nf4_quantize(L["W"], L["qt"], L["wsq"])
+            if j is not None:
+                q.qlora_time_next_launch(kid["fwd_gemm"], *events["fwd_gemm"][j])
+            q.qlora_linear_fwd(L["qt"], L["X"], L["A"], L["B"], r, alpha, L["Y"], L["T"], L["wsf"])
+            if j is not None:
+                q.qlora_time_next_launch(kid["dx_gemm"], *events["dx_gemm"][j])
+            q.qlora_linear_bwd(L["qt"], L["X"], L["dY"], L["A"], L["B"], r, alpha, L["T"],
+                               L["dX"], L["dA"], L["dB"], L["wsb"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+
+    flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
+    per_kernel = {}
+    for k in kinds:
+        durs = [a.elapsed_time(b) for a, b in events[k]]
+        per_kernel[k] = {"avg_ms": statistics.mean(durs), "total_ms_per_step": sum(durs) / args.steps,
+                         "launches_per_step": len(layers)}
+    # algorithmic work per launch, averaged over the step's launches of each kernel
+    fwd_flop = statistics.mean(2 * M * L["N"] * L["K"] + 2 * M * L["N"] * r for L in layers)
+    dx_flop = statistics.mean(2 * M * L["N"] * L["K"] + 2 * M * L["K"] * r for L in layers)
+    q_bytes = statistics.mean(L["N"] * L["K"] * (4 + 0.5 + 1 / 64) + 4 * (L["N"] * L["K"] // 16384) + 4
+                              for L in layers)
+    per_kernel["fwd_gemm"]["tflops"] = fwd_flop / (per_kernel["fwd_gemm"]["avg_ms"] * 1e-3) / 1e12
+    per_kernel["dx_gemm"]["tflops"] = dx_flop / (per_kernel["dx_gemm"]["avg_ms"] * 1e-3) / 1e12
+    per_kernel["quantize"]["gbs"] = q_bytes / (per_kernel["quantize"]["avg_ms"] * 1e-3) / 1e9
+    dom = max(("fwd_gemm", "dx_gemm"), key=lambda k: per_kernel[k]["total_ms_per_step"])
+    ach = per_kernel[dom]["tflops"]
+    roofline = {"bound": "mfma", "kernel": {"fwd_gemm": "fwd_gemm_kernel", "dx_gemm": "dx_gemm_kernel"}[dom],
+                "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(per_kernel[dom]["avg_ms"], 4),
+                "flop_per_launch": int(fwd_flop if dom == "fwd_gemm" else dx_flop)}
+    return {"ms_per_step": ms_per_step, "flops": flops, "M": M, "r": r, "alpha": alpha,
+            "layers": [[L["name"], L["N"], L["K"]] for L in layers], "per_kernel": per_kernel,
+            "roofline": roofline}
+
+
+def run_gemv(torch, q, args):
+    from workloads import Inputs
+
+    w = Inputs(2)
+    N, K = w.shape(0)
+    r, alpha = w.w.rank, w.w.alpha
+    W = torch.from_numpy(w.weight(0)).cuda()
+    sz = q.qlora_nf4_sizes(N, K, 16, r)
+    wsq = q.workspace(sz["quantize_ws_bytes"])
+    copies = []
+    for _ in range(args.gemv_copies):
+        qt = q.Nf4Tensor.empty(N, K)
+        q.qlora_nf4_quantize(W, qt, wsq)
+        copies.append(qt)
+    del W
+    A = dev_bf16(torch, w.lora_A(0))
+    B = dev_bf16(torch, w.lora_B(0))
+    wsf = q.workspace(sz["fwd_ws_bytes"])
+    out = {}
+    for M in (1, 16):
+        X = dev_bf16(torch, w.X(0, M))
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        T = torch.empty(M, r, dtype=torch.float32, device="cuda")
+        n = args.gemv_iters
+        evs = timed_events(torch, n)
+        for i in range(10):
+            q.qlora_linear_fwd(copies[i % len(copies)], X, A, B, r, alpha, Y, T, wsf)
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for i in range(n):
+            q.qlora_time_next_launch(q.QLORA_KERNEL_GEMV, *evs[i])
+            q.qlora_linear_fwd(copies[i % len(copies)], X, A, B, r, alpha, Y, T, wsf)
+        c1.record()
+        torch.cuda.synchronize()
+        durs = sorted(a.elapsed_time(b) for a, b in evs)
+        med = statistics.median(durs)
+        nbytes = gemv_kernel_bytes(M, N, K, r)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        out[f"M{M}"] = {"kernel_us_median": round(med * 1e3, 3),
+                        "kernel_us_p10": round(durs[n // 10] * 1e3, 3),
+                        "kernel_us_p90": round(durs[(9 * n) // 10] * 1e3, 3),
+                        "call_us_mean": round(c0.elapsed_time(c1) / n * 1e3, 3),
+                        "bytes": nbytes, "GB/s": round(gbs, 1),
+                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] GEMV M={M}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s")
+    return out
+
+
+def run_cpu_baseline():
+    """The oracle as it stands, timed on the host on the gate linear of the same
+    workload (one of its three layers): quantize + dequantize + fp64 forward +
+    fp64 backward at M = 4096."""
+    import numpy as np
+    from oracle import linalg, nf4
+    from workloads import Inputs
+
+    w = Inputs(3)
+    M, r, alpha = w.w.tokens[0], w.w.rank, w.w.alpha
+    _, N, K = w.w.layers[0]
+    W = w.weight(0)
+    Xb, dYb, Ab, Bb = w.X(0, M), w.dY(0, M), w.lora_A(0), w.lora_B(0)
+    f64 = linalg.bf16_to_f64
+    X, dY, A, B = f64(Xb), f64(dYb), f64(Ab), f64(Bb)
+    blas_threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((p.get("num_threads", 0) for p in threadpool_info()
+                            if p.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    ref = nf4.quantize(W)
+    wh = f64(nf4.dequantize(ref["codes"], ref["absmax_e4m3"], ref["dq_scale"],
+                            ref["dq_mean"])).reshape(N, K)
+    Y, T = linalg.linear_fwd(X, wh, A, B, alpha, r)
+    dX, dA, dB = linalg.linear_bwd(X, dY, wh, A, B, alpha, r)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(Y).all() and np.isfinite(dX).all()
+    flops = linear_flops(M, N, K, r)
+    cores = len(os.sched_getaffinity(0))
+    log(f"[bench] cpu oracle: {dt:.1f}s on the gate linear")
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads or cores,
+            "host_cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"gate linear {N}x{K} of the same workload, M={M}, r={r}: numpy NF4+DQ "
+                      "quantize and dequantize (single-threaded numpy) + fp64 forward and "
+                      "backward (BLAS on the listed threads); 1 of the 3 linears of a step"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--gemv-copies", type=int, default=64)
+    ap.add_argument("--gemv-iters", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_fine_tuning_amd as q
+
+    torch.cuda.set_device(0)
+    mlp = run_mlp(torch, q, args)
+    gemv = None if args.no_gemv else run_gemv(torch, q, args)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline()
+    value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mlp["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": "llama-7b MLP linears (gate, up 4096->11008; down 11008->4096), "
+                               "step = NF4+DQ quantize + fwd + bwd per linear",
+                   "global_batch": 4, "seq_len": 1024, "tokens": mlp["M"], "lora_rank": mlp["r"],
+                   "lora_alpha": mlp["alpha"], "layers": mlp["layers"],
+                   "flop_per_step": mlp["flops"], "parallelism": "single GPU"},
+        "roofline": mlp["roofline"],
+        "cpu_baseline": cpu,
+        "gemv": gemv,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in mlp["per_kernel"].items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * qlora_nf4.h -- C ABI of the NF4 QLoRA linear-layer library for MI355X
+ * (gfx950).  Every entry point is extern "C", takes plain pointers and sizes,
+ * and no type from any framework.
+ *
+ * Page tags used in the citations (see the oracle package for the full list):
+ *   P1 "QLoRA 的原理是什么？4-bit 量化权重真的参与训练吗？" (offer.aigcbaba.com)
+ *   P2 review of "QLoRA: Efficient Finetuning of Quantized LLMs" (ainexis.cn)
+ *   P3 "Ch.09 QLoRA 与量化：缩得更小再微调" (mdooai.com)
+ *   P4 "M5 · PEFT (LoRA / QLoRA / Prefix Tuning)" science-depth card (airsota.com)
+ *
+ * Conventions shared by all entry points
+ *   - Pointers named "device" are HIP device pointers owned by the caller; the
+ *     library never allocates, frees or keeps them.  Host pointers are read or
+ *     written before the call returns.
+ *   - Device pointers must be 16-byte aligned.  Tensors are dense row-major.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; no call synchronizes the stream.  Results are valid once
+ *     the stream has reached the enqueued work.
+ *   - Every argument is validated on the host before any HIP call is made; on
+ *     an invalid argument nothing is enqueued and an error status is returned.
+ *     qlora_last_error() then gives a text for the failing check (per thread).
+ *   - Calls are stateless and thread-safe.  Two calls that share output or
+ *     workspace memory must be ordered by the caller (same stream, or events).
+ *   - Floating-point results for non-finite inputs are unspecified.
+ *   - Shapes: W is [N, K] = [out_features, in_features] with K % 64 == 0 and
+ *     N % 8 == 0; X is [M, K]; Y and dY are [M, N]; LoRA A is [r, K], B is
+ *     [N, r], 1 <= r <= 256; s = alpha / r.  M may be 0.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qlora_status;
+#define QLORA_OK 0
+#define QLORA_ERR_INVALID_ARG 1        /* null pointer, bad size, misalignment */
+#define QLORA_ERR_UNSUPPORTED_DTYPE 2  /* dtype not accepted by this entry point */
+#define QLORA_ERR_WORKSPACE_TOO_SMALL 3
+#define QLORA_ERR_HIP 4                /* a HIP launch or runtime call failed */
+
+typedef int32_t qlora_dtype;
+#define QLORA_F32 0
+#define QLORA_BF16 1
+
+/* One NF4 + double-quantized weight (P4 §三 English derivation; P1 §二).
+ * All four arrays are device memory:
+ *   codes        uint8[N*K/2]: flattened element i is the low nibble of byte
+ *                i/2 if i is even, the high nibble if i is odd;
+ *   absmax_e4m3  uint8[N*K/64]: OCP FP8 E4M3 code of block b's mean-centred,
+ *                group-scaled absmax;
+ *   dq_scale     float[ceil(N*K/64/256)]: one fp32 scale per 256 constants;
+ *   dq_mean      float[1]: the tensor's mean of all block absmax values. */
+typedef struct {
+  int64_t n_rows; /* N = out_features */
+  int64_t n_cols; /* K = in_features, a multiple of 64 */
+  uint8_t* codes;
+  uint8_t* absmax_e4m3;
+  float* dq_scale;
+  float* dq_mean;
+} qlora_nf4_t;
+
+/* Byte counts for one layer.  Workspace sizes cover every M in [0, M_max]. */
+typedef struct {
+  size_t codes_bytes;       /* N*K/2 */
+  size_t absmax_bytes;      /* N*K/64 */
+  size_t scale_bytes;       /* 4*ceil(N*K/64/256) */
+  size_t mean_bytes;        /* 4 */
+  size_t quantize_ws_bytes; /* workspace of qlora_nf4_quantize */
+  size_t fwd_ws_bytes;      /* workspace of qlora_linear_fwd for M <= M_max */
+  size_t bwd_ws_bytes;      /* workspace of qlora_linear_bwd for M <= M_max */
+} qlora_sizes_t;
+
+/* Host-only size query.  Errors: N, K, r out of range (see conventions),
+ * M_max < 0, out == NULL. */
+qlora_status qlora_nf4_sizes(int64_t N, int64_t K, int64_t M_max, int32_t r,
+                             qlora_sizes_t* out);
+
+/* Blockwise NF4 quantization with double quantization of the constants.
+ * (P4 §三 English derivation: W_norm = W / max|W_block| over B = 64 elements,
+ * code = the nearest of 16 standard-normal-quantile levels that include an
+ * exact zero; the fp32 block constants are quantized to an 8-bit float with a
+ * second-level block of 256.  P4 §二: this saves about 0.37 bit/param.)
+ *   W        device, [N, K] fp32 (w_dtype QLORA_F32) or bf16 (QLORA_BF16);
+ *   out      host struct whose four device arrays receive the result;
+ *            out->n_rows/n_cols must equal N/K;
+ *   ws       device workspace of at least qlora_nf4_sizes().quantize_ws_bytes.
+ * Per block b: c_b = max|w|; x = fl32(w / c_b) (one correctly rounded
+ * division); code = argmin_j |x - q_j| with ties to the lower index; c_b == 0
+ * gives code 7 (the zero level).  mu = fl32(S / nb) with S the fp64 balanced
+ * pairwise sum of all c_b; per group g of 256 constants
+ * s_g = fl32(max|fl32(c_b - mu)| / 448) and e_b = E4M3(fl32(d_b / s_g)) with
+ * round-to-nearest-even and saturation at 448 (all zero if s_g == 0). */
+qlora_status qlora_nf4_quantize(const void* W, qlora_dtype w_dtype, int64_t N,
+                                int64_t K, const qlora_nf4_t* out, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* Dequantize to bf16 (P1 §七: the 4-bit base is dequantized block by block to
+ * BF16 before the matmul; P4 §四 ①: Ŵ = Dequant(W^NF4)·c).
+ *   q        host struct describing the quantized weight (device arrays);
+ *   out      device, [N, K] bf16; out_dtype must be QLORA_BF16.
+ * ŵ = RNE_bf16(fl32(q[code] * c')) with
+ * c' = fl32(fl32(dec(e) * s_g) + mu); bit-exact, signed zeros kept. */
+qlora_status qlora_dequantize(const qlora_nf4_t* q, void* out,
+                              qlora_dtype out_dtype, void* stream);
+
+/* QLoRA linear forward (P1 §七 dataflow figure; P3 公式导读 3: a frozen wide
+ * path plus a trainable low-rank path, summed):
+ *   Y = X·Ŵᵀ + (alpha/r)·(X·Aᵀ)·Bᵀ
+ *   W        host struct of the quantized weight [N, K];
+ *   X        device bf16 [M, K];  A device bf16 [r, K];  B device bf16 [N, r];
+ *   Y        device [M, N], bf16 (y_dtype QLORA_BF16) or fp32 (QLORA_F32);
+ *   T_save   device fp32 [M, r] receiving T = X·Aᵀ for the backward pass, or
+ *            NULL (T then lives in the workspace only);
+ *   ws       device workspace of at least qlora_nf4_sizes(..., M_max >= M,
+ *            r).fwd_ws_bytes.
+ * fp32 accumulation; M <= 16 takes a dequant-GEMV path, larger M a
+ * dequant-in-tile MFMA GEMM.  No bias, no dropout.  Y must not alias inputs. */
+qlora_status qlora_linear_fwd(const qlora_nf4_t* W, const void* X, int64_t M,
+                              const void* A, const void* B, int32_t r,
+                              float alpha, void* Y, qlora_dtype y_dtype,
+                              float* T_save, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* QLoRA linear backward (P1 简化版 and §七, P2 §4.4: the gradient passes
+ * through the dequantized frozen weight into the LoRA parameters only; the
+ * 4-bit codes and constants are never updated, so no weight gradient exists).
+ * With U = dY·B:
+ *   dX = dY·Ŵ + s·U·A;   dA = s·Uᵀ·X;   dB = s·dYᵀ·T,  T = X·Aᵀ.
+ *   dY       device bf16 [M, N];  X, A, B as in the forward pass;
+ *   T_saved  device fp32 [M, r] from qlora_linear_fwd, or NULL to recompute;
+ *   dX       device [M, K], bf16 or fp32 (dx_dtype);
+ *   dA       device fp32 [r, K] (overwritten, not accumulated);
+ *   dB       device fp32 [N, r] (overwritten, not accumulated);
+ *   ws       device workspace of at least .bwd_ws_bytes.
+ * With M == 0, dA and dB are set to zero. */
+qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X,
+                              const void* dY, int64_t M, const void* A,
+                              const void* B, int32_t r, float alpha,
+                              const float* T_saved, void* dX,
+                              qlora_dtype dx_dtype, float* dA, float* dB,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* Benchmark instrumentation.  The next launch of kernel `kernel_id` made by
+ * the calling thread is bracketed by hipEventRecord(start_event) and
+ * hipEventRecord(stop_event) on that launch's stream; then the request is
+ * cleared (one-shot).  Both events are hipEvent_t handles created and owned by
+ * the caller.  kernel_id: QLORA_KERNEL_NONE cancels a pending request.
+ * Errors: unknown kernel id; a NULL event with a kernel id other than NONE. */
+#define QLORA_KERNEL_NONE 0
+#define QLORA_KERNEL_FWD_GEMM 1   /* dequant-in-tile forward GEMM (M > 16) */
+#define QLORA_KERNEL_DX_GEMM 2    /* dequant-in-tile dX GEMM */
+#define QLORA_KERNEL_GEMV 3       /* dequant-GEMV forward (M <= 16) */
+#define QLORA_KERNEL_QUANTIZE 4   /* blockwise NF4 quantization kernel */
+qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event);
+
+/* The 16 fp32 NF4 levels as the library computes them (host memory, 16
+ * floats), ascending, index 7 = 0.  (P4 §三: levels at standard-normal
+ * quantiles with equal probability mass, an exact zero, ends at ±1.) */
+void qlora_nf4_codebook(float* out16);
+
+/* Text for a status code, and the detail of the calling thread's last error. */
+const char* qlora_status_string(qlora_status s);
+const char* qlora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,215 @@
+"""ctypes binding of libqlora_nf4.so (the C ABI in include/qlora_nf4.h).
+
+Argument marshalling only: every function here checks that tensors are
+contiguous and on the GPU, turns them into raw pointers and calls the C entry
+point of the same name on torch's current stream.  All computation happens in
+the library's HIP kernels.  There is no fallback: if the library is missing,
+importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = Path(os.environ.get("QLORA_NF4_LIB", PKG / "libqlora_nf4.so"))
+
+QLORA_OK = 0
+QLORA_ERR_INVALID_ARG = 1
+QLORA_ERR_UNSUPPORTED_DTYPE = 2
+QLORA_ERR_WORKSPACE_TOO_SMALL = 3
+QLORA_ERR_HIP = 4
+QLORA_F32 = 0
+QLORA_BF16 = 1
+
+EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_linear_fwd",
+           "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
+           "qlora_time_next_launch")
+
+QLORA_KERNEL_NONE = 0
+QLORA_KERNEL_FWD_GEMM = 1
+QLORA_KERNEL_DX_GEMM = 2
+QLORA_KERNEL_GEMV = 3
+QLORA_KERNEL_QUANTIZE = 4
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"status {status}: {text}")
+        self.status = status
+
+
+class qlora_nf4_t(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("absmax_e4m3", ctypes.c_void_p),
+                ("dq_scale", ctypes.c_void_p), ("dq_mean", ctypes.c_void_p)]
+
+
+class qlora_sizes_t(ctypes.Structure):
+    _fields_ = [("codes_bytes", ctypes.c_size_t), ("absmax_bytes", ctypes.c_size_t),
+                ("scale_bytes", ctypes.c_size_t), ("mean_bytes", ctypes.c_size_t),
+                ("quantize_ws_bytes", ctypes.c_size_t), ("fwd_ws_bytes", ctypes.c_size_t),
+                ("bwd_ws_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not LIB_PATH.exists():
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_fine_tuning_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    i64, i32, vp, sz, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    P = ctypes.POINTER
+    lib.qlora_nf4_sizes.argtypes = [i64, i64, i64, i32, P(qlora_sizes_t)]
+    lib.qlora_nf4_quantize.argtypes = [vp, i32, i64, i64, P(qlora_nf4_t), vp, sz, vp]
+    lib.qlora_dequantize.argtypes = [P(qlora_nf4_t), vp, i32, vp]
+    lib.qlora_linear_fwd.argtypes = [P(qlora_nf4_t), vp, i64, vp, vp, i32, f32, vp, i32, vp, vp,
+                                     sz, vp]
+    lib.qlora_linear_bwd.argtypes = [P(qlora_nf4_t), vp, vp, i64, vp, vp, i32, f32, vp, vp, i32,
+                                     vp, vp, vp, sz, vp]
+    for name in ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize",
+                 "qlora_linear_fwd", "qlora_linear_bwd"):
+        getattr(lib, name).restype = i32
+    lib.qlora_nf4_codebook.argtypes = [P(ctypes.c_float)]
+    lib.qlora_nf4_codebook.restype = None
+    lib.qlora_status_string.argtypes = [i32]
+    lib.qlora_status_string.restype = ctypes.c_char_p
+    lib.qlora_last_error.argtypes = []
+    lib.qlora_last_error.restype = ctypes.c_char_p
+    lib.qlora_time_next_launch.argtypes = [i32, vp, vp]
+    lib.qlora_time_next_launch.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != QLORA_OK:
+        raise QloraError(status, lib.qlora_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t, name: str) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return QLORA_F32
+    if t.dtype == torch.bfloat16:
+        return QLORA_BF16
+    raise ValueError(f"{name}: dtype {t.dtype} is neither float32 nor bfloat16")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Nf4Tensor:
+    """The four device arrays of one quantized weight [N, K] (torch tensors)."""
+
+    def __init__(self, n_rows: int, n_cols: int, codes, absmax_e4m3, dq_scale, dq_mean):
+        self.n_rows, self.n_cols = int(n_rows), int(n_cols)
+        self.codes, self.absmax_e4m3 = codes, absmax_e4m3
+        self.dq_scale, self.dq_mean = dq_scale, dq_mean
+
+    @classmethod
+    def empty(cls, n_rows: int, n_cols: int, device="cuda"):
+        torch = _torch()
+        s = qlora_nf4_sizes(n_rows, n_cols, 0, 1)
+        u8 = torch.uint8
+        return cls(n_rows, n_cols,
+                   torch.empty(s["codes_bytes"], dtype=u8, device=device),
+                   torch.empty(s["absmax_bytes"], dtype=u8, device=device),
+                   torch.empty(s["scale_bytes"] // 4, dtype=torch.float32, device=device),
+                   torch.empty(1, dtype=torch.float32, device=device))
+
+    def c_struct(self) -> qlora_nf4_t:
+        return qlora_nf4_t(self.n_rows, self.n_cols, _ptr(self.codes, "codes"),
+                           _ptr(self.absmax_e4m3, "absmax_e4m3"), _ptr(self.dq_scale, "dq_scale"),
+                           _ptr(self.dq_mean, "dq_mean"))
+
+
+def workspace(nbytes: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def qlora_nf4_sizes(N: int, K: int, M_max: int, r: int) -> dict:
+    out = qlora_sizes_t()
+    _check(lib.qlora_nf4_sizes(N, K, M_max, r, ctypes.byref(out)))
+    return {name: int(getattr(out, name)) for name, _ in qlora_sizes_t._fields_}
+
+
+def qlora_nf4_codebook() -> list:
+    buf = (ctypes.c_float * 16)()
+    lib.qlora_nf4_codebook(buf)
+    return list(buf)
+
+
+def qlora_nf4_quantize(W, out: Nf4Tensor, ws, stream=None) -> None:
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    N, K = W.shape
+    st = out.c_struct()
+    _check(lib.qlora_nf4_quantize(_ptr(W, "W"), _dtype(W, "W"), N, K, ctypes.byref(st),
+                                  _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                  _stream(stream)))
+
+
+def qlora_dequantize(q: Nf4Tensor, out, stream=None) -> None:
+    st = q.c_struct()
+    _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(out, "out"), _dtype(out, "out"),
+                                _stream(stream)))
+
+
+def qlora_linear_fwd(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, ws,
+                     stream=None) -> None:
+    M = X.shape[0]
+    st = W.c_struct()
+    _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X, "X"), M, _ptr(A, "A"), _ptr(B, "B"),
+                                r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
+                                _ptr(T_save, "T_save"), _ptr(ws, "ws"),
+                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qlora_linear_bwd(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,
+                     stream=None) -> None:
+    M = X.shape[0]
+    st = W.c_struct()
+    _check(lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X, "X"), _ptr(dY, "dY"), M, _ptr(A, "A"),
+                                _ptr(B, "B"), r, float(alpha), _ptr(T_saved, "T_saved"),
+                                _ptr(dX, "dX"), _dtype(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
+                                _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def qlora_time_next_launch(kernel_id: int, start_event=None, stop_event=None) -> None:
+    """Bracket the next launch of `kernel_id` with two torch.cuda.Event objects
+    (each must have been recorded once so that its HIP event exists)."""
+    s = ctypes.c_void_p(start_event.cuda_event) if start_event is not None else None
+    e = ctypes.c_void_p(stop_event.cuda_event) if stop_event is not None else None
+    _check(lib.qlora_time_next_launch(kernel_id, s, e))

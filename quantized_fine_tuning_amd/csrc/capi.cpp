@@ -1,0 +1,248 @@
+// C ABI of the NF4 QLoRA library: argument validation (entirely on the host,
+// before any HIP call), workspace sizing and dispatch to the kernel launchers.
+// The declarations and their contracts are in include/qlora_nf4.h.
+#include "../../include/qlora_nf4.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "host.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qlora_status fail(qlora_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+qlora_status fail(qlora_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+qlora_status ok() {
+  g_last_error.clear();
+  return QLORA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define CHECK_PTR(p)                                                                        \
+  do {                                                                                      \
+    if ((p) == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);        \
+    if (!aligned16(p)) return fail(QLORA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+#define CHECK_OPT_PTR(p)                                                                    \
+  do {                                                                                      \
+    if ((p) != nullptr && !aligned16(p))                                                    \
+      return fail(QLORA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p);           \
+  } while (0)
+
+qlora_status check_shape(const char* fn, int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: N=%lld and K=%lld must be positive", fn, (long long)N,
+                (long long)K);
+  if (K % 64 != 0)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: K=%lld is not a multiple of 64", fn, (long long)K);
+  if (N % 8 != 0)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: N=%lld is not a multiple of 8", fn, (long long)N);
+  if (N > (int64_t(1) << 40) / K)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: N*K too large", fn);
+  return QLORA_OK;
+}
+
+qlora_status check_rank(const char* fn, int32_t r) {
+  if (r < 1 || r > 256) return fail(QLORA_ERR_INVALID_ARG, "%s: r=%d outside [1, 256]", fn, r);
+  return QLORA_OK;
+}
+
+qlora_status check_tensor(const char* fn, const qlora_nf4_t* q) {
+  if (q == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: weight descriptor is NULL", fn);
+  qlora_status st = check_shape(fn, q->n_rows, q->n_cols);
+  if (st != QLORA_OK) return st;
+  const uint8_t* codes = q->codes;
+  const uint8_t* absmax_e4m3 = q->absmax_e4m3;
+  const float* dq_scale = q->dq_scale;
+  const float* dq_mean = q->dq_mean;
+  CHECK_PTR(codes);
+  CHECK_PTR(absmax_e4m3);
+  CHECK_PTR(dq_scale);
+  CHECK_PTR(dq_mean);
+  return QLORA_OK;
+}
+
+qlora_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(QLORA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+qnf4::Nf4View view(const qlora_nf4_t* q) {
+  return qnf4::Nf4View{q->codes, q->absmax_e4m3, q->dq_scale, q->dq_mean, q->n_rows, q->n_cols};
+}
+
+}  // namespace
+
+namespace qnf4 {
+TimingHook& timing_hook() {
+  thread_local TimingHook h{0, nullptr, nullptr};
+  return h;
+}
+}  // namespace qnf4
+
+extern "C" {
+
+qlora_status qlora_nf4_sizes(int64_t N, int64_t K, int64_t M_max, int32_t r, qlora_sizes_t* out) {
+  const char* fn = "qlora_nf4_sizes";
+  if (out == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  qlora_status st = check_shape(fn, N, K);
+  if (st != QLORA_OK) return st;
+  if ((st = check_rank(fn, r)) != QLORA_OK) return st;
+  if (M_max < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M_max=%lld < 0", fn, (long long)M_max);
+  const int64_t nb = N * K / 64;
+  out->codes_bytes = (size_t)(N * K / 2);
+  out->absmax_bytes = (size_t)nb;
+  out->scale_bytes = (size_t)(4 * ((nb + 255) / 256));
+  out->mean_bytes = 4;
+  out->quantize_ws_bytes = qnf4::quant_layout(N, K).total;
+  out->fwd_ws_bytes = qnf4::fwd_layout(M_max, N, K, r).total;
+  out->bwd_ws_bytes = qnf4::bwd_layout(M_max, N, K, r).total;
+  return ok();
+}
+
+qlora_status qlora_nf4_quantize(const void* W, qlora_dtype w_dtype, int64_t N, int64_t K,
+                                const qlora_nf4_t* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "qlora_nf4_quantize";
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: w_dtype=%d (expected F32 or BF16)", fn, w_dtype);
+  qlora_status st = check_shape(fn, N, K);
+  if (st != QLORA_OK) return st;
+  CHECK_PTR(W);
+  if ((st = check_tensor(fn, out)) != QLORA_OK) return st;
+  if (out->n_rows != N || out->n_cols != K)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: descriptor shape %lldx%lld != %lldx%lld", fn,
+                (long long)out->n_rows, (long long)out->n_cols, (long long)N, (long long)K);
+  const qnf4::QuantLayout L = qnf4::quant_layout(N, K);
+  if (ws_bytes < L.total)
+    return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
+                L.total);
+  CHECK_PTR(ws);
+  return hip_status(fn, qnf4::launch_quantize(W, w_dtype == QLORA_BF16, N, K, out->codes,
+                                              out->absmax_e4m3, out->dq_scale, out->dq_mean,
+                                              static_cast<char*>(ws), L,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_dequantize(const qlora_nf4_t* q, void* out, qlora_dtype out_dtype,
+                              void* stream) {
+  const char* fn = "qlora_dequantize";
+  qlora_status st = check_tensor(fn, q);
+  if (st != QLORA_OK) return st;
+  if (out_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype=%d (only BF16)", fn, out_dtype);
+  CHECK_PTR(out);
+  return hip_status(fn, qnf4::launch_dequantize(q->codes, q->absmax_e4m3, q->dq_scale, q->dq_mean,
+                                                q->n_rows, q->n_cols, static_cast<uint16_t*>(out),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
+                              const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
+                              float* T_save, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "qlora_linear_fwd";
+  qlora_status st = check_tensor(fn, W);
+  if (st != QLORA_OK) return st;
+  if ((st = check_rank(fn, r)) != QLORA_OK) return st;
+  if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
+  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: y_dtype=%d", fn, y_dtype);
+  CHECK_PTR(A);
+  CHECK_PTR(B);
+  if (M > 0) {
+    CHECK_PTR(X);
+    CHECK_PTR(Y);
+  }
+  CHECK_OPT_PTR(T_save);
+  const qnf4::FwdLayout L = qnf4::fwd_layout(M, W->n_rows, W->n_cols, r);
+  if (ws_bytes < L.total)
+    return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
+                L.total);
+  if (M > 0) CHECK_PTR(ws);
+  return hip_status(fn, qnf4::launch_forward(
+                            view(W), static_cast<const uint16_t*>(X), M,
+                            static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), r,
+                            alpha / (float)r, Y, y_dtype == QLORA_BF16, T_save,
+                            static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* dY, int64_t M,
+                              const void* A, const void* B, int32_t r, float alpha,
+                              const float* T_saved, void* dX, qlora_dtype dx_dtype, float* dA,
+                              float* dB, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "qlora_linear_bwd";
+  qlora_status st = check_tensor(fn, W);
+  if (st != QLORA_OK) return st;
+  if ((st = check_rank(fn, r)) != QLORA_OK) return st;
+  if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
+  if (dx_dtype != QLORA_F32 && dx_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: dx_dtype=%d", fn, dx_dtype);
+  CHECK_PTR(A);
+  CHECK_PTR(B);
+  CHECK_PTR(dA);
+  CHECK_PTR(dB);
+  if (M > 0) {
+    CHECK_PTR(X);
+    CHECK_PTR(dY);
+    CHECK_PTR(dX);
+  }
+  CHECK_OPT_PTR(T_saved);
+  const qnf4::BwdLayout L = qnf4::bwd_layout(M, W->n_rows, W->n_cols, r);
+  if (ws_bytes < L.total)
+    return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
+                L.total);
+  CHECK_PTR(ws);
+  return hip_status(fn, qnf4::launch_backward(
+                            view(W), static_cast<const uint16_t*>(X),
+                            static_cast<const uint16_t*>(dY), M, static_cast<const uint16_t*>(A),
+                            static_cast<const uint16_t*>(B), r, alpha / (float)r, T_saved, dX,
+                            dx_dtype == QLORA_BF16, dA, dB, static_cast<char*>(ws), L,
+                            static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event) {
+  const char* fn = "qlora_time_next_launch";
+  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_QUANTIZE)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: unknown kernel id %d", fn, kernel_id);
+  if (kernel_id != QLORA_KERNEL_NONE && (start_event == nullptr || stop_event == nullptr))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: NULL event", fn);
+  qnf4::TimingHook& h = qnf4::timing_hook();
+  h.kernel = kernel_id;
+  h.start = static_cast<hipEvent_t>(start_event);
+  h.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
+void qlora_nf4_codebook(float* out16) {
+  if (out16 == nullptr) return;
+  std::memcpy(out16, qnf4::codebook().q, 16 * sizeof(float));
+}
+
+const char* qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case QLORA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QLORA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* qlora_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

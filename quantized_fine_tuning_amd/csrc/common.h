@@ -1,0 +1,109 @@
+// Device helpers shared by the gfx950 kernels of the NF4 QLoRA library.
+//
+// Arithmetic rules kept everywhere (they make the results bit-reproducible
+// against an independent implementation): one IEEE fp32 rounding per
+// operation, no contraction into fused multiply-add (-ffp-contract=off plus
+// the pragma below), correctly rounded fp32 division, fp32 denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace qnf4 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 64;     // NF4 absmax block (elements)
+constexpr int kDqBlock = 256;  // constants per double-quantization group
+
+// NF4 levels and the 15 decision thresholds, passed to kernels by value.
+struct Codebook {
+  float q[16];
+  float t[15];  // largest fp32 <= midpoint of q[j], q[j+1]
+};
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+
+// Two fp32 values rounded to bf16 (nearest, ties to even) and packed; `lo`
+// lands in bits 0..15.  Lowers to v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p;
+  p.x = (__bf16)lo;
+  p.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float((uint32_t)v << 16);
+}
+
+// ---------------------------------------------------------------------------
+// OCP FP8 E4M3 (bias 7, 3 mantissa bits, max 448, subnormals to 2^-9)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t e) {
+  const uint32_t sign = (e & 0x80u) << 24;
+  const uint32_t ex = (e >> 3) & 15u;
+  const uint32_t m = e & 7u;
+  const float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (m << 20))
+                       : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(mag) | sign);
+}
+
+// Nearest E4M3 of a finite fp32 value, ties to the even mantissa, magnitudes
+// >= 448 saturate to 448; the sign bit is the sign of y (-0 -> 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    // subnormal grid of spacing 2^-9: a * 512 is exact, rintf rounds half-even
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    // keep 3 mantissa bits with round-to-nearest-even on the fp32 pattern; a
+    // carry moves into the exponent, which is the right result
+    const uint32_t ua = u & 0x7fffffffu;
+    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return code | sign;
+}
+
+// c' = fl32(fl32(dec(e) * s) + mu): two roundings, no fused multiply-add.
+__device__ __forceinline__ float decode_constant(uint32_t e, float s, float mu) {
+  const float p = __fmul_rn(e4m3_to_f32(e), s);
+  return __fadd_rn(p, mu);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA: D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16)
+// Lane l supplies A row (l % 16) and B column (l % 16), 8 consecutive
+// reduction elements each (the same reduction slots for A and B), and
+// receives D rows 4*(l/16) + v, v = 0..3, of column l % 16.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace qnf4

@@ -1,0 +1,96 @@
+// Internal interface between the C-ABI layer (capi.hip) and the kernel
+// launchers.  Launchers assume validated arguments and only enqueue work; they
+// return the status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qnf4 {
+
+const Codebook& codebook();
+
+// One-shot timing request of the calling thread (see qlora_time_next_launch).
+struct TimingHook {
+  int kernel;
+  hipEvent_t start, stop;
+};
+TimingHook& timing_hook();
+
+// Brackets one launch with the pending events if `kernel` was requested.
+struct TimedLaunch {
+  bool on;
+  hipEvent_t stop;
+  hipStream_t st;
+  TimedLaunch(int kernel, hipStream_t s) : on(false), stop(nullptr), st(s) {
+    TimingHook& h = timing_hook();
+    if (h.kernel == kernel) {
+      on = true;
+      stop = h.stop;
+      h.kernel = 0;
+      (void)hipEventRecord(h.start, st);
+    }
+  }
+  ~TimedLaunch() {
+    if (on) (void)hipEventRecord(stop, st);
+  }
+};
+enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4 };
+
+// Round `x` up to a multiple of `a`.
+constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Padded LoRA rank: the hi/lo split of s·T (and s·U) occupies [M, 2*Rp] bf16
+// with hi in columns [0, r), lo in [Rp, Rp + r), zeros elsewhere.
+inline int64_t lora_rp(int32_t r) { return round_up(r, 32); }
+
+// Quantize ---------------------------------------------------------------
+struct QuantLayout {
+  int64_t nb, ng, chunks;   // blocks, DQ groups, 256-block chunks
+  int64_t lvl_len[8];       // lengths of the tree-reduction levels (0-terminated)
+  size_t off_absmax, off_partial, off_lvl_a, off_lvl_b, total;
+};
+QuantLayout quant_layout(int64_t N, int64_t K);
+
+hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* e, float* s, float* mu, char* ws, const QuantLayout& L,
+                           hipStream_t st);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* e, const float* s,
+                             const float* mu, int64_t N, int64_t K, uint16_t* out,
+                             hipStream_t st);
+
+// Shared view of a quantized weight for the GEMM kernels.
+struct Nf4View {
+  const uint8_t* codes;
+  const uint8_t* e;
+  const float* s;
+  const float* mu;
+  int64_t N, K;
+};
+
+// Forward ------------------------------------------------------------------
+struct FwdLayout {
+  size_t off_T, off_sT, total;  // fp32 T [M, r] (if not saved by caller), bf16 sT [M, 2Rp]
+};
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+
+hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
+                          const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16,
+                          float* T, char* ws, const FwdLayout& L, hipStream_t st);
+
+// Backward -----------------------------------------------------------------
+struct BwdLayout {
+  int64_t splitA, splitB;  // M-slices of the dA / dB reductions
+  size_t off_T, off_sT, off_sU, off_pA, off_pB, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+
+hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                           const float* T_saved, void* dX, bool dx_bf16, float* dA, float* dB,
+                           char* ws, const BwdLayout& L, hipStream_t st);
+
+}  // namespace qnf4

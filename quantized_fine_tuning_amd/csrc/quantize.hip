@@ -1,0 +1,285 @@
+// NF4 blockwise quantization, double quantization of the block constants and
+// standalone dequantization, for gfx950.
+//
+// Quantization (P4 §三 English derivation): per block of 64 consecutive
+// elements c = max|w|, x = w / c, code = the nearest of 16 levels (ties to the
+// lower index; a zero block gets the zero level).  Double quantization (P4 §二
+// and §三): the fp32 block constants are re-quantized to an 8-bit float with a
+// second-level block of 256 — here OCP E4M3 of the mean-centred constants with
+// one fp32 scale per 256 and one fp32 mean per tensor.
+//
+// Kernels
+//   nf4_quantize_kernel   one workgroup per 256 consecutive blocks (the DQ
+//                         group size, a power of two); 16-byte coalesced loads,
+//                         16 (fp32 input) or 8 (bf16 input) lanes per block,
+//                         absmax by xor shuffles; writes packed codes, the fp32
+//                         absmax (workspace) and the chunk's fp64 pairwise sum.
+//   tree_level_kernel     fp64 pairwise sums of aligned groups of 1024 values;
+//                         the last level writes mu = fl32(S / nb).
+//   dq_encode_kernel      one wave per 256 constants: d = c - mu, group max,
+//                         s = max / 448, e = E4M3(d / s).
+//   nf4_dequant_kernel    32 elements per thread, 16-byte loads of codes,
+//                         64-byte contiguous stores of bf16.
+#include "host.h"
+
+namespace qnf4 {
+namespace {
+
+constexpr int kChunkBlocks = 256;  // blocks per quantize workgroup
+constexpr int kLevelGroup = 1024;  // values per tree_level workgroup
+
+template <typename WT>
+struct QTraits;
+template <>
+struct QTraits<float> {
+  static constexpr int kEpl = 4;  // elements per lane (16 bytes)
+  __device__ static float to_f32(float v) { return v; }
+};
+template <>
+struct QTraits<uint16_t> {
+  static constexpr int kEpl = 8;
+  __device__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+
+template <typename WT>
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict__ W, int64_t nb,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax,
+                                                           double* __restrict__ partial,
+                                                           Codebook cb) {
+  constexpr int EPL = QTraits<WT>::kEpl;
+  constexpr int LPB = kBlock / EPL;      // lanes per block
+  constexpr int BPW = 64 / LPB;          // blocks per wave per iteration
+  constexpr int BPI = 4 * BPW;           // blocks per workgroup per iteration
+  constexpr int ITERS = kChunkBlocks / BPI;
+  typedef uint32_t load_t __attribute__((ext_vector_type(4)));
+
+  __shared__ float s_c[kChunkBlocks];
+  __shared__ double s_w[4];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int sub = lane % LPB, bl = lane / LPB;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kChunkBlocks;
+
+  // issue every load of the chunk first
+  load_t raw[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int64_t b = chunk0 + it * BPI + wave * BPW + bl;
+    if (b < nb) {
+      raw[it] = *reinterpret_cast<const load_t*>(W + b * kBlock + sub * EPL);
+    } else {
+      raw[it] = load_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int local = it * BPI + wave * BPW + bl;
+    const int64_t b = chunk0 + local;
+    WT v[EPL];
+    __builtin_memcpy(v, &raw[it], sizeof(v));
+    float w[EPL];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      w[i] = QTraits<WT>::to_f32(v[i]);
+      m = fmaxf(m, fabsf(w[i]));
+    }
+#pragma unroll
+    for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      uint32_t code = 7u;
+      if (m != 0.0f) {
+        const float x = w[i] / m;  // one correctly rounded fp32 division
+        code = 0u;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) code += (x > cb.t[j]) ? 1u : 0u;
+      }
+      packed |= code << (4 * i);
+    }
+    if (b < nb) {
+      uint8_t* dst = codes + b * (kBlock / 2) + sub * (EPL / 2);
+      if constexpr (EPL == 4) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+      }
+      if (sub == 0) absmax[b] = m;
+    }
+    if (sub == 0) s_c[local] = (b < nb) ? m : 0.0f;
+  }
+  __syncthreads();
+
+  // fp64 balanced pairwise sum of the chunk's 256 constants (block order)
+  double v = (double)s_c[tid];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) s_w[wave] = v;
+  __syncthreads();
+  if (tid == 0) partial[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+}
+
+// Pairwise fp64 sums of aligned groups of 1024 inputs (zero beyond n_in).  If
+// `mu` is non-null the launch has a single group and writes fl32(S / nb).
+__global__ __launch_bounds__(256) void tree_level_kernel(const double* __restrict__ in, int64_t n_in,
+                                                         double* __restrict__ out, float* mu,
+                                                         int64_t nb) {
+  __shared__ double s_w[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kLevelGroup + 4 * tid;
+  double x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (base + i < n_in) ? in[base + i] : 0.0;
+  double v = (x[0] + x[1]) + (x[2] + x[3]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) s_w[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    const double S = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+    out[blockIdx.x] = S;
+    if (mu) *mu = (float)(S / (double)nb);
+  }
+}
+
+__global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ absmax, int64_t nb,
+                                                        const float* __restrict__ mu_p,
+                                                        uint8_t* __restrict__ e,
+                                                        float* __restrict__ s_out, int64_t ng) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ng) return;
+  const float mu = *mu_p;
+  const int64_t i0 = g * kDqBlock + 4 * lane;
+  float d[4];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d[i] = (i0 + i < nb) ? __fsub_rn(absmax[i0 + i], mu) : 0.0f;
+    m = fmaxf(m, fabsf(d[i]));
+  }
+  m = wave_max(m);
+  const float s = m / 448.0f;
+  uint32_t word = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word |= f32_to_e4m3(d[i] / s) << (8 * i);
+  }
+  if (i0 + 4 <= nb) {
+    *reinterpret_cast<uint32_t*>(e + i0) = word;
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (i0 + i < nb) e[i0 + i] = (uint8_t)(word >> (8 * i));
+  }
+  if (lane == 0) s_out[g] = s;
+}
+
+// 32 elements (16 bytes of codes, half a block) per thread.
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ e,
+                                                          const float* __restrict__ s,
+                                                          const float* __restrict__ mu_p,
+                                                          int64_t n_units, uint16_t* __restrict__ out,
+                                                          Codebook cb) {
+  __shared__ float s_q[16];
+  if (threadIdx.x < 16) s_q[threadIdx.x] = cb.q[threadIdx.x];
+  __syncthreads();
+  const float mu = *mu_p;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(codes + u * 16);
+    const int64_t b = u >> 1;  // 2 units per 64-block
+    const float cp = decode_constant(e[b], s[b / kDqBlock], mu);
+    u32x4_t o[4];
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      uint32_t r[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float a = __fmul_rn(s_q[(w[wi] >> (8 * p)) & 15u], cp);
+        const float c = __fmul_rn(s_q[(w[wi] >> (8 * p + 4)) & 15u], cp);
+        r[p] = pack_bf16x2(a, c);
+      }
+      o[wi] = u32x4_t{r[0], r[1], r[2], r[3]};
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + u * 32);
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) dst[wi] = o[wi];
+  }
+}
+
+}  // namespace
+
+QuantLayout quant_layout(int64_t N, int64_t K) {
+  QuantLayout L{};
+  L.nb = N * K / kBlock;
+  L.ng = (L.nb + kDqBlock - 1) / kDqBlock;
+  L.chunks = (L.nb + kChunkBlocks - 1) / kChunkBlocks;
+  int64_t n = L.chunks;
+  int i = 0;
+  do {
+    n = (n + kLevelGroup - 1) / kLevelGroup;
+    L.lvl_len[i++] = n;
+  } while (n > 1 && i < 7);
+  L.lvl_len[i] = 0;
+  size_t off = 0;
+  L.off_absmax = off;
+  off += round_up(L.chunks * kChunkBlocks * 4, 256);
+  L.off_partial = off;
+  off += round_up(L.chunks * 8, 256);
+  L.off_lvl_a = off;
+  off += round_up(L.lvl_len[0] * 8, 256);
+  L.off_lvl_b = off;
+  off += round_up(L.lvl_len[0] * 8, 256);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uint8_t* codes,
+                           uint8_t* e, float* s, float* mu, char* ws, const QuantLayout& L,
+                           hipStream_t st) {
+  float* absmax = reinterpret_cast<float*>(ws + L.off_absmax);
+  double* partial = reinterpret_cast<double*>(ws + L.off_partial);
+  double* lvl[2] = {reinterpret_cast<double*>(ws + L.off_lvl_a),
+                    reinterpret_cast<double*>(ws + L.off_lvl_b)};
+  const Codebook& cb = codebook();
+  {
+    TimedLaunch tl(kKernQuantize, st);
+    if (w_bf16) {
+      nf4_quantize_kernel<uint16_t><<<(unsigned)L.chunks, 256, 0, st>>>(
+          static_cast<const uint16_t*>(W), L.nb, codes, absmax, partial, cb);
+    } else {
+      nf4_quantize_kernel<float><<<(unsigned)L.chunks, 256, 0, st>>>(
+          static_cast<const float*>(W), L.nb, codes, absmax, partial, cb);
+    }
+  }
+  const double* in = partial;
+  int64_t n_in = L.chunks;
+  for (int i = 0; L.lvl_len[i] != 0; ++i) {
+    const int64_t n_out = L.lvl_len[i];
+    double* out = lvl[i & 1];
+    tree_level_kernel<<<(unsigned)n_out, 256, 0, st>>>(in, n_in, out, n_out == 1 ? mu : nullptr,
+                                                       L.nb);
+    in = out;
+    n_in = n_out;
+  }
+  dq_encode_kernel<<<(unsigned)((L.ng + 3) / 4), 256, 0, st>>>(absmax, L.nb, mu, e, s, L.ng);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* e, const float* s,
+                             const float* mu, int64_t N, int64_t K, uint16_t* out,
+                             hipStream_t st) {
+  const int64_t units = N * K / 32;
+  int64_t grid = (units + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  nf4_dequant_kernel<<<(unsigned)grid, 256, 0, st>>>(codes, e, s, mu, units, out, codebook());
+  return hipGetLastError();
+}
+
+}  // namespace qnf4

@@ -1,0 +1,103 @@
+"""GPU parity of quantization, double quantization and dequantization against
+the oracle: bit-exact codes, E4M3 constants, group scales, mean and
+dequantized bf16 weights.  Every call goes through the C ABI."""
+
+import numpy as np
+import pytest
+
+from oracle import nf4
+from tests import gpu_util as G
+from workloads import Inputs, random_f32, to_bf16_bits, bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def check_full(W32: np.ndarray, W_dev):
+    qt = G.gpu_quantize(W_dev)
+    ref = nf4.quantize(W32)
+    assert np.array_equal(G.host(qt.codes), ref["codes"]), "codes"
+    assert np.array_equal(G.host(qt.absmax_e4m3), ref["absmax_e4m3"]), "e4m3 constants"
+    assert np.array_equal(G.host(qt.dq_scale).view(np.uint32), ref["dq_scale"].view(np.uint32)), "scales"
+    assert G.host(qt.dq_mean).view(np.uint32)[0] == np.float32(ref["dq_mean"]).view(np.uint32), "mean"
+    w_hat = G.host_bf16(G.gpu_dequantize(qt)).reshape(-1)
+    assert np.array_equal(w_hat, G.oracle_w_hat(ref)), "dequantized weight"
+    return qt
+
+
+def test_tiny_layer_fp32():
+    w = Inputs(1)
+    W = w.weight(0)
+    print("tiny 256x256 fp32", flush=True)
+    check_full(W, G.dev_f32(W))
+
+
+def test_qproj_4096_fp32_with_outliers():
+    w = Inputs(2)
+    W = w.weight(0)
+    print("q_proj 4096x4096 fp32", flush=True)
+    check_full(W, G.dev_f32(W))
+
+
+def test_bf16_input_attention_shape():
+    w = Inputs(4)
+    Wb = w.weight(0)  # bf16 bits, 4096x4096
+    print("7b q 4096x4096 bf16", flush=True)
+    check_full(bf16_bits_to_f32(Wb), G.dev_bf16(Wb))
+
+
+@pytest.mark.parametrize("n,k", [(8, 64), (8, 320), (24, 192), (4096, 4160)])
+def test_ragged_group_and_tree_shapes(n, k):
+    # nb = 8 (one partial group), 40, 72 and 266240 (1040 chunks: two levels of
+    # the pairwise mean)
+    W = random_f32((n, k), seed=1000 + n + k, scale=0.02)
+    print(f"shape {n}x{k}", flush=True)
+    check_full(W, G.dev_f32(W))
+
+
+def test_edge_values():
+    rng = np.random.default_rng(77)
+    W = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    W[0, :] = 0.0                        # zero blocks
+    W[1, :64] = -0.0
+    W[2, :] *= np.float32(1e-39)         # subnormal weights
+    W[3, :64] = np.float32(1.0)          # constant block
+    W[4, :] = np.abs(W[4, :])            # one-signed blocks
+    W[5, 7] = np.float32(3.0)            # isolated outlier
+    q = nf4.codebook()
+    m = nf4.midpoints(q)
+    W[6, :15] = [np.float32(v) for v in m]  # x exactly at midpoints (block max 1.0 below)
+    W[6, 15] = 1.0
+    print("edge values", flush=True)
+    check_full(W, G.dev_f32(W))
+
+
+def test_mlp_weight_sampled():
+    # full-size 11008x4096 fp32 weight: mean, all constants and scales exact;
+    # codes and dequantized values exact on 4000 sampled blocks
+    w = Inputs(3)
+    W = w.weight(0)
+    print("7b gate 11008x4096 fp32", flush=True)
+    qt = G.gpu_quantize(G.dev_f32(W))
+    c = nf4.block_absmax(W)
+    e, s, mu = nf4.double_quant(c)
+    assert G.host(qt.dq_mean).view(np.uint32)[0] == np.float32(mu).view(np.uint32)
+    assert np.array_equal(G.host(qt.absmax_e4m3), e)
+    assert np.array_equal(G.host(qt.dq_scale).view(np.uint32), s.view(np.uint32))
+    blocks = np.random.default_rng(5).choice(c.shape[0], 4000, replace=False)
+    codes_gpu = G.host(qt.codes).reshape(-1, 32)[blocks]
+    wb = W.reshape(-1, 64)[blocks]
+    codes_ref, _ = nf4.quantize_codes(wb)
+    assert np.array_equal(codes_gpu.reshape(-1), nf4.pack_nibbles(codes_ref))
+    w_hat = G.host_bf16(G.gpu_dequantize(qt)).reshape(-1, 64)[blocks]
+    cp = nf4.decode_constants(e, s, mu)[blocks]
+    ref = nf4.bf16_bits((nf4.codebook()[codes_ref.reshape(-1, 64)] * cp[:, None]).astype(np.float32))
+    assert np.array_equal(w_hat, ref)
+
+
+def test_deterministic():
+    W = random_f32((1024, 1024), seed=9, scale=0.02)
+    Wd = G.dev_f32(W)
+    a = G.gpu_quantize(Wd)
+    b = G.gpu_quantize(Wd)
+    for name in ("codes", "absmax_e4m3", "dq_scale", "dq_mean"):
+        assert np.array_equal(G.host(getattr(a, name)), G.host(getattr(b, name))), name
