@@ -51,10 +51,20 @@ def linear_bwd(X, dY, W_hat, A, B, alpha: float, r: int):
     s = float(alpha) / float(r)
     U = dY @ B
     dX = dY @ W_hat + s * (U @ A)
-    dA = s * (U.T @ X)
-    T = X @ A.T
-    dB = s * (dY.T @ T)
+    dA, dB = lora_grads(X, dY, A, B, alpha, r)
     return dX, dA, dB
+
+
+def lora_grads(X, dY, A, B, alpha: float, r: int):
+    """dA = s·(dY·B)ᵀ·X and dB = s·dYᵀ·(X·Aᵀ) in fp64 (they do not involve Ŵ)."""
+    X = np.asarray(X, dtype=np.float64)
+    dY = np.asarray(dY, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    s = float(alpha) / float(r)
+    U = dY @ B
+    T = X @ A.T
+    return s * (U.T @ X), s * (dY.T @ T)
 
 
 def matmul_fsum(a, b):
