@@ -43,16 +43,20 @@ def linear_bwd(X, dY, W_hat, A, B, alpha: float, r: int):
     U = dY·B;  dX = dY·Ŵ + s·U·A;  dA = s·Uᵀ·X;  dB = s·dYᵀ·(X·Aᵀ).
     Returns (dX, dA, dB).  T is recomputed here, never taken from elsewhere.
     """
-    X = np.asarray(X, dtype=np.float64)
+    dX = linear_dx(dY, W_hat, A, B, alpha, r)
+    dA, dB = lora_grads(X, dY, A, B, alpha, r)
+    return dX, dA, dB
+
+
+def linear_dx(dY, W_hat, A, B, alpha: float, r: int):
+    """dX = dY·Ŵ + s·(dY·B)·A in fp64.  Columns of dX depend only on the same
+    columns of Ŵ and A."""
     dY = np.asarray(dY, dtype=np.float64)
     W_hat = np.asarray(W_hat, dtype=np.float64)
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
     s = float(alpha) / float(r)
-    U = dY @ B
-    dX = dY @ W_hat + s * (U @ A)
-    dA, dB = lora_grads(X, dY, A, B, alpha, r)
-    return dX, dA, dB
+    return dY @ W_hat + s * ((dY @ B) @ A)
 
 
 def lora_grads(X, dY, A, B, alpha: float, r: int):

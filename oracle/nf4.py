@@ -293,12 +293,21 @@ def dequantize(packed: np.ndarray, e: np.ndarray, s: np.ndarray, mu,
     """ŵ_i = RNE_bf16(fl32(q[code_i] * c'_b)); returns uint16 bf16 bits,
     flattened row-major.  Signed zeros follow IEEE (code 7 with c' < 0 gives
     -0)."""
+    codes = unpack_nibbles(packed).reshape(-1, BLOCK)
+    return dequantize_blocks(codes, np.arange(codes.shape[0]), e, s, mu, q32).reshape(-1)
+
+
+def dequantize_blocks(codes: np.ndarray, block_ids: np.ndarray, e: np.ndarray, s: np.ndarray,
+                      mu, q32: np.ndarray | None = None) -> np.ndarray:
+    """The same dequantization for a subset of blocks: ``codes`` holds the
+    unpacked codes of the listed blocks ([len(block_ids), 64]); ``e``, ``s`` and
+    ``mu`` are the whole tensor's constants.  Returns uint16 bf16 bits
+    [len(block_ids), 64].  (Blocks dequantize independently of each other.)"""
     if q32 is None:
         q32 = codebook()
-    codes = unpack_nibbles(packed)
-    cp = decode_constants(e, s, mu)
-    blk = np.arange(codes.shape[0]) // BLOCK
-    w32 = (q32[codes] * cp[blk]).astype(np.float32)
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1, BLOCK)
+    cp = decode_constants(e, s, mu)[np.asarray(block_ids)]
+    w32 = (q32[codes] * cp[:, None]).astype(np.float32)
     return bf16_bits(w32)
 
 

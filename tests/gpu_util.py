@@ -103,3 +103,33 @@ def oracle_quantized(W32: np.ndarray):
 def oracle_w_hat(qt_ref) -> np.ndarray:
     return nf4.dequantize(qt_ref["codes"], qt_ref["absmax_e4m3"], qt_ref["dq_scale"],
                           qt_ref["dq_mean"])
+
+
+class SampledOracle:
+    """The oracle's Ŵ for a subset of a large weight.  Blocks quantize and
+    dequantize independently; only the mean and the group scales are global,
+    and those come from the oracle's full double quantization of all block
+    constants (cheap)."""
+
+    def __init__(self, W32: np.ndarray):
+        self.W = np.ascontiguousarray(W32, dtype=np.float32)
+        self.N, self.K = self.W.shape
+        c = nf4.block_absmax(self.W)
+        self.e, self.s, self.mu = nf4.double_quant(c)
+
+    def _blocks(self, rows, kb0, kb1):
+        rows = np.asarray(rows)
+        sub = self.W[rows][:, 64 * kb0:64 * kb1]
+        codes, _ = nf4.quantize_codes(sub)
+        kpr = self.K // 64
+        ids = (rows[:, None] * kpr + np.arange(kb0, kb1)[None, :]).reshape(-1)
+        bits = nf4.dequantize_blocks(codes.reshape(-1, 64), ids, self.e, self.s, self.mu)
+        return bits.reshape(len(rows), 64 * (kb1 - kb0))
+
+    def rows(self, rows) -> np.ndarray:
+        """Ŵ[rows, :] in fp64."""
+        return bf16_f64(self._blocks(rows, 0, self.K // 64))
+
+    def cols(self, kb0: int, kb1: int) -> np.ndarray:
+        """Ŵ[:, 64*kb0 : 64*kb1] in fp64."""
+        return bf16_f64(self._blocks(np.arange(self.N), kb0, kb1))

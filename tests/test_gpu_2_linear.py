@@ -141,27 +141,70 @@ def test_zero_tokens():
     assert Y.numel() == 0
 
 
-def test_mlp_7b_full_size_sampled():
-    # the full-size layers, in the launch configuration the benchmark times;
-    # Y and dX checked on 48 sampled token rows, dA and dB in full
+class BigLayer:
+    """A full-size layer on the device; the oracle works on samples of it."""
+
+    def __init__(self, idx, layer, M):
+        w = Inputs(idx)
+        self.r, self.alpha = w.w.rank, w.w.alpha
+        Wst = w.weight(layer)
+        if w.w.weight_dtype == "bf16":
+            self.W32 = (Wst.astype(np.uint32) << 16).view(np.float32)
+            w_dev = G.dev_bf16(Wst)
+        else:
+            self.W32 = Wst
+            w_dev = G.dev_f32(Wst)
+        self.qt = G.gpu_quantize(w_dev)
+        del w_dev
+        self.X, self.A, self.B, self.dY = w.X(layer, M), w.lora_A(layer), w.lora_B(layer), w.dY(layer, M)
+        self.Xd, self.Ad, self.Bd, self.dYd = (G.dev_bf16(a) for a in (self.X, self.A, self.B, self.dY))
+        self.oracle = G.SampledOracle(self.W32)
+
+
+def run_big(L, seed, n_tok=32, n_rows=256, n_stripes=3):
+    """Y on sampled (token, weight-row) pairs, dX on sampled (token, 64-column
+    stripe) pairs, dA and dB in full; bf16 and fp32 outputs."""
+    t = torch()
+    rng = np.random.default_rng(seed)
+    M = L.X.shape[0]
+    N, K = L.W32.shape
+    r, alpha = L.r, L.alpha
+    tok = np.sort(rng.choice(M, n_tok, replace=False))
+    wrows = np.sort(rng.choice(N, n_rows, replace=False))
+    stripes = np.sort(rng.choice(K // 64, n_stripes, replace=False))
+    Yb, T = G.gpu_forward(L.qt, L.Xd, L.Ad, L.Bd, r, alpha, t.bfloat16)
+    Yf, _ = G.gpu_forward(L.qt, L.Xd, L.Ad, L.Bd, r, alpha, t.float32, save_T=False)
+    X, A, B, dY = (G.bf16_f64(a) for a in (L.X, L.A, L.B, L.dY))
+    Y_ref, _ = linalg.linear_fwd(X[tok], L.oracle.rows(wrows), A, B[wrows], alpha, r)
+    e1 = G.assert_close(G.out_f64(Yb)[np.ix_(tok, wrows)], Y_ref, G.TOL_BF16, "Y bf16")
+    e2 = G.assert_close(G.out_f64(Yf)[np.ix_(tok, wrows)], Y_ref, G.TOL_F32, "Y fp32")
+    dXb, dA, dB = G.gpu_backward(L.qt, L.Xd, L.dYd, L.Ad, L.Bd, r, alpha, T, t.bfloat16)
+    dXf, _, _ = G.gpu_backward(L.qt, L.Xd, L.dYd, L.Ad, L.Bd, r, alpha, None, t.float32)
+    cols = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in stripes])
+    w_cols = np.concatenate([L.oracle.cols(b, b + 1) for b in stripes], axis=1)
+    dX_ref = linalg.linear_dx(dY[tok], w_cols, A[:, cols], B, alpha, r)
+    e3 = G.assert_close(G.out_f64(dXb)[np.ix_(tok, cols)], dX_ref, G.TOL_BF16, "dX bf16")
+    e4 = G.assert_close(G.out_f64(dXf)[np.ix_(tok, cols)], dX_ref, G.TOL_F32, "dX fp32")
+    dA_ref, dB_ref = linalg.lora_grads(X, dY, A, B, alpha, r)
+    e5 = G.assert_close(G.out_f64(dA), dA_ref, G.TOL_F32, "dA")
+    e6 = G.assert_close(G.out_f64(dB), dB_ref, G.TOL_F32, "dB")
+    print(f"  Y bf16 {e1:.2e} fp32 {e2:.2e}  dX bf16 {e3:.2e} fp32 {e4:.2e}  "
+          f"dA {e5:.2e}  dB {e6:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_mlp_7b_full_size_sampled(layer):
+    # the full-size layers of the benchmark, in the launch configuration it times
     w = Inputs(3)
-    rows = np.sort(np.random.default_rng(11).choice(4096, 48, replace=False))
-    for layer in range(3):
-        print(f"7b MLP {w.w.layers[layer]} M=4096 r=64", flush=True)
-        L = Layer.from_workload(3, layer, 4096)
-        T = run_fwd(L, w.w.rank, w.w.alpha, rows)
-        run_bwd(L, w.w.rank, w.w.alpha, T, rows)
-        del L
+    print(f"7b MLP {w.w.layers[layer]} M=4096 r=64", flush=True)
+    run_big(BigLayer(3, layer, 4096), seed=layer)
 
 
 @pytest.mark.parametrize("idx,layer,M", [(4, 0, 8192), (4, 6, 8192), (5, 0, 2048), (5, 4, 2048)])
 def test_bf16_weight_layers_sampled(idx, layer, M):
     w = Inputs(idx)
-    rows = np.sort(np.random.default_rng(12).choice(M, 32, replace=False))
     print(f"workload {idx} {w.w.layers[layer]} M={M}", flush=True)
-    L = Layer.from_workload(idx, layer, M)
-    T = run_fwd(L, w.w.rank, w.w.alpha, rows)
-    run_bwd(L, w.w.rank, w.w.alpha, T, rows)
+    run_big(BigLayer(idx, layer, M), seed=100 + layer)
 
 
 def test_forward_backward_deterministic():
