@@ -55,8 +55,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t e) {
   const uint32_t sign = (e & 0x80u) << 24;
   const uint32_t ex = (e >> 3) & 15u;
   const uint32_t m = e & 7u;
-  const float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (m << 20))
-                       : (float)m * 0x1p-9f;
+  // normal: exponent ex - 7, mantissa m/8; subnormal (ex == 0): m * 2^-9
+  const float normal = __uint_as_float(((ex + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0x1p-9f;
+  const float mag = ex ? normal : sub;
   return __uint_as_float(__float_as_uint(mag) | sign);
 }
 
@@ -99,6 +101,44 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+
+// ---------------------------------------------------------------------------
+// Buffer loads: a scalar resource (base, size in bytes) plus a per-lane 32-bit
+// byte offset and a scalar byte offset.  Reads at or past `bytes` return zero
+// and never fault, which is how ragged tile edges are handled without
+// per-lane branches.
+// ---------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// Asynchronous copy of 16 bytes per lane from a buffer straight into LDS:
+// lane i's bytes land at lds + 16*i (the whole wave fills 1 KB starting at the
+// wave-uniform `lds`).  Reads past the resource's size deliver zeros.
+__device__ __forceinline__ void buf_load_lds16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)voff, (int)soff, 0, 0);
+}
+
+// Waits until every vector-memory load issued by this wave has completed
+// (including copies into LDS, which the compiler does not track).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

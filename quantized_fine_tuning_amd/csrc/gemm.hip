@@ -408,57 +408,6 @@ __device__ __forceinline__ void load_codebook_lds(float* sq, const Codebook& cb)
 // Kernels
 // ---------------------------------------------------------------------------
 
-constexpr int FWD_MT = 256, FWD_NT = 128;
-
-// Y[M, N] = [X | sT] · [Ŵ | B_ext]ᵀ.  Grid (ceil(N/128), ceil(M/256)).
-__global__ __launch_bounds__(256) void fwd_gemm_kernel(Nf4View W, const uint16_t* __restrict__ X,
-                                                       int64_t M, const uint16_t* __restrict__ sT,
-                                                       const uint16_t* __restrict__ B, int r,
-                                                       int64_t Rp, void* __restrict__ Y, int y_bf16,
-                                                       Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (FWD_MT + FWD_NT) * ROW_BYTES];
-  __shared__ float sq[16];
-  load_codebook_lds(sq, cb);
-  __syncthreads();
-  const int64_t m0 = (int64_t)blockIdx.y * FWD_MT, n0 = (int64_t)blockIdx.x * FWD_NT;
-  const int ksteps = (int)(W.K / KS);
-  const int lsteps = (int)(2 * Rp / KS);
-  RowLoader<FWD_MT> la;
-  la.p0 = X + m0 * W.K;
-  la.ld0 = W.K;
-  la.k0 = W.K;
-  la.p1 = sT + m0 * 2 * Rp;
-  la.ld1 = 2 * Rp;
-  la.k1 = 2 * Rp;
-  la.rows = M - m0;
-  la.steps0 = ksteps;
-  Nf4RowLoader<FWD_NT> lb;
-  lb.codes = W.codes;
-  lb.e = W.e;
-  lb.s = W.s;
-  lb.mu = W.mu;
-  lb.q = sq;
-  lb.B = B;
-  lb.n0 = n0;
-  lb.N = W.N;
-  lb.K = W.K;
-  lb.Rp = Rp;
-  lb.r = r;
-  lb.ksteps = ksteps;
-  Core<FWD_MT, FWD_NT, 2, 2> core;
-  run_tiles(core, la, lb, ksteps + lsteps, smem);
-  const int64_t N = W.N;
-  for_each_acc(core, [&](int i, int j, float v) {
-    const int64_t m = m0 + i, n = n0 + j;
-    if (m < M && n < N) {
-      if (y_bf16)
-        static_cast<uint16_t*>(Y)[m * N + n] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
-      else
-        static_cast<float*>(Y)[m * N + n] = v;
-    }
-  });
-}
-
 constexpr int DX_MT = 256, DX_NT = 128;
 
 // dX[M, K] = [dY | sU] · [Ŵ ; A_ext].  Grid (ceil(K/128), ceil(M/256)).
@@ -657,13 +606,15 @@ unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
-// The M <= 16 forward path lives in gemv.hip.
+// The forward GEMM lives in fwd.hip, the M <= 16 forward path in gemv.hip.
+hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
+                           const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
+                           bool y_bf16, hipStream_t st);
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
                        const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
                        hipStream_t st);
 
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
-  (void)N;
   (void)K;
   FwdLayout L{};
   const int64_t Rp = lora_rp(r);
@@ -672,6 +623,8 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   off += round_up(M * r * 4, 256);
   L.off_sT = off;
   off += round_up(M * 2 * Rp * 2, 256);
+  L.off_B2 = off;
+  off += M > 16 ? round_up(N * 2 * Rp * 2, 256) : 0;
   L.total = off;
   return L;
 }
@@ -715,12 +668,8 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
   uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
   lora_down_kernel<<<dim3(cdiv(Rp, 64), cdiv(M, 64)), 256, 0, st>>>(X, M, W.K, A, r, Rp, scale, T,
                                                                    sT);
-  {
-    TimedLaunch tl(kKernFwdGemm, st);
-    fwd_gemm_kernel<<<dim3(cdiv(W.N, FWD_NT), cdiv(M, FWD_MT)), 256, 0, st>>>(
-        W, X, M, sT, B, r, Rp, Y, y_bf16 ? 1 : 0, codebook());
-  }
-  return hipGetLastError();
+  uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
+  return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y_bf16, st);
 }
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,

@@ -73,7 +73,8 @@ struct Nf4View {
 
 // Forward ------------------------------------------------------------------
 struct FwdLayout {
-  size_t off_T, off_sT, total;  // fp32 T [M, r] (if not saved by caller), bf16 sT [M, 2Rp]
+  // fp32 T [M, r] (if not saved by the caller), bf16 sT [M, 2Rp], bf16 B2 [N, 2Rp]
+  size_t off_T, off_sT, off_B2, total;
 };
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
