@@ -18,7 +18,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libqlora_nf4.so"
-SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "gemm.hip", "fwd.hip", "gemv.hip"]
+SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "gemm.hip", "fwd.hip", "dx.hip", "gemv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -1,4 +1,4 @@
-// MFMA GEMMs of the QLoRA linear layer for gfx950.
+// Low-rank side products of the QLoRA linear layer for gfx950.
 //
 // P1 §七 (dataflow figure): the frozen 4-bit weight is dequantized to BF16 and
 // multiplied with the BF16 activation, and the trainable LoRA path is added to
@@ -11,12 +11,14 @@
 //     rows are contiguous along the reduction (128 bytes per row, 16-byte chunks
 //     XOR-swizzled by row to keep fragment reads free of bank conflicts),
 //     double buffered, one barrier per step;
-//   * "loaders" fill a tile from global memory: plain bf16 rows, bf16 read
-//     across rows (transposed on the way into LDS), NF4 codes dequantized on the
-//     way into LDS (row-wise for the forward product, transposed for dX);
-//   * the LoRA terms are folded into the big products as extra reduction steps
-//     over [s·T_hi | s·T_lo] and [s·U_hi | s·U_lo] (bf16 hi/lo splits of the fp32
-//     intermediates, so the low-rank path keeps ~16 significant bits).
+//   * "loaders" fill a tile from global memory: plain bf16 rows, or bf16 read
+//     across rows (transposed on the way into LDS).
+// The kernels here are the low-rank side products (T = X·Aᵀ, U = dY·B, and the
+// split-M reductions of dA and dB); the two big dequantizing products live in
+// fwd.hip and dx.hip.  Their LoRA terms are extra reduction steps over
+// [s·T_hi | s·T_lo] and [s·U_hi | s·U_lo] (bf16 hi/lo splits of the fp32
+// intermediates, so the low-rank path keeps ~16 significant bits), which the
+// kernels here produce.
 #include "host.h"
 
 namespace qnf4 {
@@ -154,174 +156,6 @@ struct RowLoader {
   }
 };
 
-// NF4 weight rows (n) with the reduction along k: the forward product's B
-// operand.  Steps [0, K/64) dequantize codes; later steps read the LoRA factor
-// B_ext[n][j] = B[n][j mod Rp] (zero where j mod Rp >= r).  Tile of R rows;
-// each thread owns 64*R/256 consecutive elements of one row.
-template <int R>
-struct Nf4RowLoader {
-  static constexpr int EPT = KS * R / 256;   // elements per thread (32 or 64)
-  static constexpr int TPR = KS / EPT;       // threads per row (2 or 1)
-  static_assert(EPT == 32 || EPT == 64, "tile rows");
-  const uint8_t* codes;
-  const uint8_t* e;
-  const float* s;
-  const float* mu;
-  const float* q;  // LDS copy of the levels
-  const uint16_t* B;
-  int64_t n0, N, K, Rp;
-  int r, ksteps;
-  u32x4_t w[EPT / 32];
-  uint32_t eb;
-  float sg;
-  uint32_t lora[EPT / 2];
-  bool is_lora;
-
-  __device__ void load(int step) {
-    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    const int64_t n = n0 + row;
-    is_lora = step >= ksteps;
-    if (!is_lora) {
-      if (n < N) {
-        const uint8_t* src = codes + n * (K / 2) + (int64_t)step * (KS / 2) + part * (EPT / 2);
-#pragma unroll
-        for (int i = 0; i < EPT / 32; ++i) w[i] = reinterpret_cast<const u32x4_t*>(src)[i];
-        const int64_t b = n * (K / KS) + step;
-        eb = e[b];
-        sg = s[b / kDqBlock];
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPT / 32; ++i) w[i] = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        eb = 0;
-        sg = 0.0f;
-      }
-    } else {
-      const int64_t j0 = (int64_t)(step - ksteps) * KS + part * EPT;
-#pragma unroll
-      for (int i = 0; i < EPT / 2; ++i) {
-        uint32_t pr[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t j = (j0 + 2 * i + h) % Rp;
-          pr[h] = (n < N && j < r) ? B[n * r + j] : 0u;
-        }
-        lora[i] = pr[0] | (pr[1] << 16);
-      }
-    }
-  }
-
-  __device__ void store(char* t) const {
-    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    if (!is_lora) {
-      const float cp = decode_constant(eb, sg, *mu);
-#pragma unroll
-      for (int i = 0; i < EPT / 32; ++i) {
-#pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          const uint32_t x = w[i][wi];
-          u32x4_t o;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const float a = __fmul_rn(q[(x >> (8 * p)) & 15u], cp);
-            const float b = __fmul_rn(q[(x >> (8 * p + 4)) & 15u], cp);
-            o[p] = pack_bf16x2(a, b);
-          }
-          const int chunk = part * (EPT / 8) + i * 4 + wi;
-          *reinterpret_cast<u32x4_t*>(t + swz(row, chunk)) = o;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < EPT / 8; ++c) {
-        const u32x4_t o{lora[4 * c], lora[4 * c + 1], lora[4 * c + 2], lora[4 * c + 3]};
-        *reinterpret_cast<u32x4_t*>(t + swz(row, part * (EPT / 8) + c)) = o;
-      }
-    }
-  }
-};
-
-// NF4 weight read across rows for dX = dY·Ŵ: the tile's rows are output
-// columns k (R of them), the reduction runs over weight rows n.  Each thread
-// owns 8 consecutive n by 4*R/128 consecutive k; the values are transposed on
-// the way into LDS.  Steps >= nsteps_w read the LoRA factor A_ext[j][k] =
-// A[j mod Rp][k] instead (zero where j mod Rp >= r).
-template <int R>
-struct Nf4TransLoader {
-  static constexpr int KPT = R * KS / 256 / 8;  // k per thread
-  static_assert(KPT == 4, "tile rows");
-  const uint8_t* codes;
-  const uint8_t* e;
-  const float* s;
-  const float* mu;
-  const float* q;
-  const uint16_t* A;
-  int64_t k0, N, K, Rp;
-  int r, nsteps_w;
-  uint32_t cw[8];  // codes: 4 nibbles of each of 8 rows; LoRA: bf16 pairs (k, k+1)
-  uint32_t eb[8];  // codes: e4m3 byte of each row; LoRA: bf16 pairs (k+2, k+3)
-  float sg[8];
-  bool is_lora;
-
-  __device__ void load(int step) {
-    const int ng = threadIdx.x / (R / KPT), kg = threadIdx.x % (R / KPT);
-    const int64_t k = k0 + (int64_t)kg * KPT;
-    is_lora = step >= nsteps_w;
-    if (!is_lora) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t n = (int64_t)step * KS + ng * 8 + i;
-        if (n < N && k < K) {
-          cw[i] = *reinterpret_cast<const uint16_t*>(codes + n * (K / 2) + k / 2);
-          const int64_t b = n * (K / KS) + k / KS;
-          eb[i] = e[b];
-          sg[i] = s[b / kDqBlock];
-        } else {
-          cw[i] = 0x7777u;
-          eb[i] = 0;
-          sg[i] = 0.0f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t j = ((int64_t)(step - nsteps_w) * KS + ng * 8 + i) % Rp;
-        u32x2_t v{0u, 0u};
-        if (j < r && k < K) v = *reinterpret_cast<const u32x2_t*>(A + j * K + k);
-        cw[i] = v[0];
-        eb[i] = v[1];
-      }
-    }
-  }
-
-  __device__ void store(char* t) const {
-    const int ng = threadIdx.x / (R / KPT), kg = threadIdx.x % (R / KPT);
-    float vals[8][KPT];
-    if (!is_lora) {
-      const float m = *mu;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float c = decode_constant(eb[i], sg[i], m);
-#pragma unroll
-        for (int kk = 0; kk < KPT; ++kk) vals[i][kk] = __fmul_rn(q[(cw[i] >> (4 * kk)) & 15u], c);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        vals[i][0] = bf16lo(cw[i]);
-        vals[i][1] = bf16hi(cw[i]);
-        vals[i][2] = bf16lo(eb[i]);
-        vals[i][3] = bf16hi(eb[i]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < KPT; ++kk) {
-      const u32x4_t o{pack_bf16x2(vals[0][kk], vals[1][kk]), pack_bf16x2(vals[2][kk], vals[3][kk]),
-                      pack_bf16x2(vals[4][kk], vals[5][kk]), pack_bf16x2(vals[6][kk], vals[7][kk])};
-      *reinterpret_cast<u32x4_t*>(t + swz(kg * KPT + kk, ng)) = o;
-    }
-  }
-};
-
 // bf16 matrix L[m][p] (p contiguous, leading dimension ld) read with the
 // reduction over m: tile rows are p (R of them), each thread owns 8
 // consecutive m by 4 consecutive p, transposed on the way into LDS.  Rows
@@ -407,57 +241,6 @@ __device__ __forceinline__ void load_codebook_lds(float* sq, const Codebook& cb)
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
-
-constexpr int DX_MT = 256, DX_NT = 128;
-
-// dX[M, K] = [dY | sU] · [Ŵ ; A_ext].  Grid (ceil(K/128), ceil(M/256)).
-__global__ __launch_bounds__(256) void dx_gemm_kernel(Nf4View W, const uint16_t* __restrict__ dY,
-                                                      int64_t M, const uint16_t* __restrict__ sU,
-                                                      const uint16_t* __restrict__ A, int r,
-                                                      int64_t Rp, void* __restrict__ dX, int dx_bf16,
-                                                      Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (DX_MT + DX_NT) * ROW_BYTES];
-  __shared__ float sq[16];
-  load_codebook_lds(sq, cb);
-  __syncthreads();
-  const int64_t m0 = (int64_t)blockIdx.y * DX_MT, k0 = (int64_t)blockIdx.x * DX_NT;
-  const int nsteps_w = (int)((W.N + KS - 1) / KS);
-  const int lsteps = (int)(2 * Rp / KS);
-  RowLoader<DX_MT> la;
-  la.p0 = dY + m0 * W.N;
-  la.ld0 = W.N;
-  la.k0 = W.N;
-  la.p1 = sU + m0 * 2 * Rp;
-  la.ld1 = 2 * Rp;
-  la.k1 = 2 * Rp;
-  la.rows = M - m0;
-  la.steps0 = nsteps_w;
-  Nf4TransLoader<DX_NT> lb;
-  lb.codes = W.codes;
-  lb.e = W.e;
-  lb.s = W.s;
-  lb.mu = W.mu;
-  lb.q = sq;
-  lb.A = A;
-  lb.k0 = k0;
-  lb.N = W.N;
-  lb.K = W.K;
-  lb.Rp = Rp;
-  lb.r = r;
-  lb.nsteps_w = nsteps_w;
-  Core<DX_MT, DX_NT, 2, 2> core;
-  run_tiles(core, la, lb, nsteps_w + lsteps, smem);
-  const int64_t K = W.K;
-  for_each_acc(core, [&](int i, int j, float v) {
-    const int64_t m = m0 + i, k = k0 + j;
-    if (m < M && k < K) {
-      if (dx_bf16)
-        static_cast<uint16_t*>(dX)[m * K + k] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu);
-      else
-        static_cast<float*>(dX)[m * K + k] = v;
-    }
-  });
-}
 
 // T[M, r] = X · Aᵀ (fp32, optional) and sT = hi/lo(s·T) [M, 2Rp] bf16.
 // Grid (ceil(Rp/64), ceil(M/64)).
@@ -606,7 +389,11 @@ unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
-// The forward GEMM lives in fwd.hip, the M <= 16 forward path in gemv.hip.
+// The forward GEMM lives in fwd.hip, the dX GEMM in dx.hip, the M <= 16
+// forward path in gemv.hip.
+hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
+                          const uint16_t* A, int32_t r, int64_t Rp, uint16_t* AT2, void* dX,
+                          bool dx_bf16, hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
                            bool y_bf16, hipStream_t st);
@@ -648,6 +435,8 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   off += round_up(M * 2 * Rp * 2, 256);
   L.off_sU = off;
   off += round_up(M * 2 * Rp * 2, 256);
+  L.off_AT2 = off;
+  off += round_up(K * 2 * Rp * 2, 256);
   L.off_pA = off;
   off += round_up(L.splitA * 2 * Rp * K * 4, 256);
   L.off_pB = off;
@@ -694,11 +483,9 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
                                                                      nullptr, sT);
   }
   lora_up_kernel<<<dim3(cdiv(Rp, 64), cdiv(M, 64)), 256, 0, st>>>(dY, M, N, B, r, Rp, scale, sU);
-  {
-    TimedLaunch tl(kKernDxGemm, st);
-    dx_gemm_kernel<<<dim3(cdiv(K, DX_NT), cdiv(M, DX_MT)), 256, 0, st>>>(
-        W, dY, M, sU, A, r, Rp, dX, dx_bf16 ? 1 : 0, codebook());
-  }
+  uint16_t* AT2 = reinterpret_cast<uint16_t*>(ws + L.off_AT2);
+  hipError_t e = launch_dx_gemm(W, dY, M, sU, A, r, Rp, AT2, dX, dx_bf16, st);
+  if (e != hipSuccess) return e;
   // dA' [2Rp, K] = sUᵀ · X ;  dB' [N, 2Rp] = dYᵀ · sT
   const int64_t mA = round_up((M + L.splitA - 1) / L.splitA, KS);
   tn_partial_kernel<<<dim3(cdiv(K, 128), cdiv(2 * Rp, 128), (unsigned)L.splitA), 256, 0, st>>>(

@@ -85,7 +85,7 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
 // Backward -----------------------------------------------------------------
 struct BwdLayout {
   int64_t splitA, splitB;  // M-slices of the dA / dB reductions
-  size_t off_T, off_sT, off_sU, off_pA, off_pB, total;
+  size_t off_T, off_sT, off_sU, off_AT2, off_pA, off_pB, total;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
