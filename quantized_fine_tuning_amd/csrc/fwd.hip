@@ -253,11 +253,18 @@ __global__ void pad_lora_b_kernel(const uint16_t* __restrict__ B, int64_t N, int
 
 }  // namespace
 
+hipError_t launch_pad_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp, uint16_t* B2,
+                             hipStream_t st) {
+  const int64_t n2 = N * 2 * Rp;
+  pad_lora_b_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, st>>>(B, N, r, Rp, B2);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
                            bool y_bf16, hipStream_t st) {
-  const int64_t n2 = W.N * 2 * Rp;
-  pad_lora_b_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, st>>>(B, W.N, r, Rp, B2);
+  hipError_t e = launch_pad_lora_b(B, W.N, r, Rp, B2, st);
+  if (e != hipSuccess) return e;
   const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
   const unsigned grid = tile_grid(tm, tn);
   const int yb = y_bf16 ? 1 : 0;

@@ -73,8 +73,10 @@ struct Nf4View {
 
 // Forward ------------------------------------------------------------------
 struct FwdLayout {
-  // fp32 T [M, r] (if not saved by the caller), bf16 sT [M, 2Rp], bf16 B2 [N, 2Rp]
-  size_t off_T, off_sT, off_B2, total;
+  // fp32 T [M, r] (if not saved by the caller), bf16 sT [M, 2Rp], bf16 B2
+  // [N, 2Rp], fp32 partial sums of T over reduction slices of length sliceT
+  size_t off_T, off_sT, off_B2, off_P, total;
+  int64_t sliceT;
 };
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
@@ -84,8 +86,10 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
 
 // Backward -----------------------------------------------------------------
 struct BwdLayout {
-  int64_t splitA, splitB;  // M-slices of the dA / dB reductions
-  size_t off_T, off_sT, off_sU, off_AT2, off_pA, off_pB, total;
+  // bf16 sT, sU [M, 2Rp]; bf16 B2 [N, 2Rp]; bf16 AT2 [K, 2Rp]; one fp32
+  // partial-sum area reused by the T, U, dA and dB reductions
+  size_t off_sT, off_sU, off_B2, off_AT2, off_P, total;
+  int64_t sliceT, sliceU, sliceA, sliceB;  // reduction slice lengths
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
