@@ -55,6 +55,13 @@ class qlora_sizes_t(ctypes.Structure):
 
 
 def _load():
+    # The library must share torch's HIP runtime: it is handed torch's device
+    # pointers, streams and events.  torch ships its own libamdhip64 with the
+    # same soname, so loading torch first makes the dynamic loader bind this
+    # library to that copy; loading this library first would map a second,
+    # separate HIP runtime into the process.
+    import torch  # noqa: F401
+
     if not LIB_PATH.exists():
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m quantized_fine_tuning_amd.build` (hipcc, gfx950)")

@@ -136,6 +136,20 @@ __device__ __forceinline__ void buf_load_lds16(rsrc_t r, void* lds, uint32_t vof
                                            (int)voff, (int)soff, 0, 0);
 }
 
+// LDS as explicit 32-bit byte addresses: lets table lookups be formed as
+// base | (code * 2) (two VALU ops) when the table base is 32-byte aligned.
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(p);
+}
+__device__ __forceinline__ uint16_t lds_read_u16(uint32_t a) {
+  return *(const lds_u16_t*)(uintptr_t)a;
+}
+// 2 * (4-bit code at bit `pos` of w), as a byte offset into a bf16 table.
+__device__ __forceinline__ uint32_t code_x2(uint32_t w, int pos) {
+  return pos == 0 ? ((w << 1) & 0x1Eu) : ((w >> (pos - 1)) & 0x1Eu);
+}
+
 // Waits until every vector-memory load issued by this wave has completed
 // (including copies into LDS, which the compiler does not track).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

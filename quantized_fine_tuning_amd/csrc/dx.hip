@@ -34,6 +34,12 @@ constexpr int TM = 256, TK = 256, NSTEP = 64;
 __device__ __forceinline__ int swz128(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
+// [k][n] weight tile: the chunk is XORed with (row ^ row/8) & 7 so that both
+// the transposing writes (8 lanes per chunk column, rows 8 apart) and the
+// fragment reads (16 consecutive rows) spread over all banks.
+__device__ __forceinline__ int wswz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
 
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
@@ -108,11 +114,13 @@ __global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16
   };
 
   char* lut = slut[wave];
+  const uint32_t lut_addr = lds_offset(lut);
   char* wt = swt[wave];
-  // table of row `lane` at slot ((lane & 7) << 3) | (lane >> 3): the 8 rows a
-  // lookup instruction touches (8rg + i for rg = 0..7) sit in distinct banks
-  const int my_slot = ((lane & 7) << 3) | (lane >> 3);
-  const int look_base = rg * 32;  // + i*256 selects row 8rg + i
+  // Table of row t (= lane) at slot 8*(t & 7) + ((t ^ (t >> 3)) & 7): slot mod
+  // 8 (the bank group of a 32-byte table) differs across 8 consecutive t (the
+  // table writes) and across t = 8rg + i for fixed i (one lookup instruction).
+  const int my_slot = 8 * (lane & 7) + ((lane ^ (lane >> 3)) & 7);
+  // row 8rg + i sits at slot 8i + (i ^ rg): byte offset 256i + 32(i ^ rg)
   u32x4_t bf[2][4][2];
   // Dequantize step s (codes already in cw/eraw/sraw) into bf[1].
   auto dequant = [&](int s) {
@@ -128,27 +136,27 @@ __global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16
     *reinterpret_cast<u32x4_t*>(lut + my_slot * 32 + 16) = t1;
     // look up 8 rows x 8 columns, pairing rows (2p, 2p+1) in one register;
     // one column at a time keeps few lookups in flight (register pressure)
-    const char* tab = lut + look_base;
+    uint32_t tab[8];  // table of row 8rg + i: 32-byte aligned LDS address
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tab[i] = lut_addr + 256u * i + 32u * (uint32_t)(i ^ rg);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       u32x4_t o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t c0 = (cw[2 * p] >> (4 * c)) & 15u;
-        const uint32_t c1 = (cw[2 * p + 1] >> (4 * c)) & 15u;
         u16x2_t v;
-        v.x = *reinterpret_cast<const uint16_t*>(tab + (2 * p) * 256 + 2 * c0);
-        v.y = *reinterpret_cast<const uint16_t*>(tab + (2 * p + 1) * 256 + 2 * c1);
+        v.x = lds_read_u16(tab[2 * p] | code_x2(cw[2 * p], 4 * c));
+        v.y = lds_read_u16(tab[2 * p + 1] | code_x2(cw[2 * p + 1], 4 * c));
         o[p] = __builtin_bit_cast(uint32_t, v);
       }
-      *reinterpret_cast<u32x4_t*>(wt + swz128(8 * cg + c, rg)) = o;
+      *reinterpret_cast<u32x4_t*>(wt + wswz(8 * cg + c, rg)) = o;
       if (c & 1) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        bf[1][j][ks] = *reinterpret_cast<const u32x4_t*>(wt + swz128(16 * j + lr, 2 * kq + ks));
+        bf[1][j][ks] = *reinterpret_cast<const u32x4_t*>(wt + wswz(16 * j + lr, 2 * kq + ks));
   };
   // LoRA B fragments of tail step l: AT2[kw0 + 16j + lr][64l + 16kq + 8ks ..]
   const uint32_t vat = (uint32_t)((lr * 2 * Rp + 16 * kq) * 2);

@@ -6,11 +6,15 @@
 // Design
 //   * 256x256 output tile per workgroup, 4 waves; wave w owns the 64 weight
 //     rows [64w, 64w+64) of the tile and all 256 token rows, so every weight
-//     element is dequantized exactly once per workgroup and never goes through
-//     LDS: each lane turns 8 bytes of codes (16 consecutive k of one weight
-//     row) into the bf16 B operand of two v_mfma_f32_16x16x32_bf16 directly in
-//     registers.  Within a 64-wide reduction step lane group q = lane/16 holds
-//     k in [16q, 16q+16); the A operand (X from LDS) uses the same k slots.
+//     element is dequantized exactly once per workgroup, straight into
+//     registers: each lane turns 8 bytes of codes (16 consecutive k of one
+//     weight row) into the bf16 B operand of two v_mfma_f32_16x16x32_bf16.
+//     Within a 64-wide reduction step lane group q = lane/16 holds k in
+//     [16q, 16q+16); the A operand (X from LDS) uses the same k slots.
+//   * Dequantization goes through a per-row table: per step lane t writes
+//     the 16 values RNE_bf16(fl32(q_j * c')) of weight row 64w + t to LDS, and
+//     each code then costs one 2-byte table read (bit-identical to
+//     multiplying per element, since the value depends only on code and row).
 //   * X goes through a double-buffered LDS tile (256 rows x 64 k, 16-byte
 //     chunks XOR-swizzled by row) filled by buffer-to-LDS copies one step
 //     ahead (no staging registers); the codes of the next step are loaded one
@@ -31,27 +35,10 @@ namespace {
 
 constexpr int TM = 256, TN = 256, KSTEP = 64;
 
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ int xswz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
-
-__device__ __forceinline__ void dequant_pair(u32x2_t cw, float cp, const float* sq, u32x4_t& b0,
-                                             u32x4_t& b1) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const uint32_t w = cw[ks];
-    u32x4_t o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float a = __fmul_rn(sq[(w >> (8 * p)) & 15u], cp);
-      const float c = __fmul_rn(sq[(w >> (8 * p + 4)) & 15u], cp);
-      o[p] = pack_bf16x2(a, c);
-    }
-    if (ks == 0)
-      b0 = o;
-    else
-      b1 = o;
-  }
 }
 
 template <int LSTEPS>
@@ -62,6 +49,9 @@ __global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint1
                                                           int y_bf16, int tiles_m, int tiles_n,
                                                           Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sx[2][TM * 128];
+  // per-wave tables: 64 weight rows x 16 bf16 (32 bytes); 256-byte alignment
+  // lets the compiler OR a table offset into a table base
+  __shared__ __attribute__((aligned(256))) char slut[4][64 * 32];
   __shared__ float sq[16];
   int tmi, tni;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni)) return;
@@ -108,30 +98,56 @@ __global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint1
   // B operand: this lane's weight rows are 64*wave + 16j + lr (tile-local)
   const int brow = 64 * wave + lr;
   const uint32_t vc = (uint32_t)(brow * (K / 2) + 8 * kq);
-  const uint32_t ve = (uint32_t)brow * kpr;
   const uint32_t vb = (uint32_t)((brow * 2 * Rp + 16 * kq) * 2);
-  const uint32_t c_rstride = (uint32_t)(16 * (K / 2)), e_rstride = 16u * kpr;
+  const uint32_t c_rstride = (uint32_t)(16 * (K / 2));
   const uint32_t b_rstride = (uint32_t)(16 * 2 * Rp * 2);
-  const uint32_t blk0 = (uint32_t)(n0 + brow) * kpr;  // global block index of row start
   u32x2_t craw[4];
-  uint32_t eraw[4];
-  float sraw[4];
+  uint32_t eraw;
+  float sraw;
+  // codes of rows 16j + lr (16 consecutive k each); the e4m3 byte and group
+  // scale of this lane's table row 64*wave + lane
+  const uint32_t ve_me = (uint32_t)(64 * wave + lane) * kpr;
+  const uint32_t blk_me = (uint32_t)(n0 + 64 * wave + lane) * kpr;
   auto load_codes = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      craw[j] = buf_load8(rc, vc, j * c_rstride + (uint32_t)s * 32u);
-      eraw[j] = buf_load1(re, ve, j * e_rstride + (uint32_t)s);
-      const uint32_t g = (blk0 + j * e_rstride + (uint32_t)s) / kDqBlock;
-      sraw[j] = __uint_as_float(buf_load4(rs, g * 4u, 0u));
-    }
+    for (int j = 0; j < 4; ++j) craw[j] = buf_load8(rc, vc, j * c_rstride + (uint32_t)s * 32u);
+    eraw = buf_load1(re, ve_me, (uint32_t)s);
+    sraw = __uint_as_float(buf_load4(rs, ((blk_me + (uint32_t)s) / kDqBlock) * 4u, 0u));
   };
   // B fragments of two consecutive steps (ping-pong, no copies)
   u32x4_t bf[2][4][2];
+  char* lut = slut[wave];
+  const uint32_t lut_base = lds_offset(lut) + (uint32_t)lr * 32u;  // row 16j + lr adds 512j
+  // Dequantize: lane t writes the table RNE_bf16(fl32(q_j * c')) of row t,
+  // then every code is one 2-byte lookup in the table of its row; pairs of
+  // consecutive k share a register.  (Rows past N only feed output columns
+  // past N, which are not stored.)
   auto make_b = [&](u32x4_t (&b)[4][2]) {
+    const float cp = decode_constant(eraw, sraw, mu);
+    u32x4_t t0, t1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      t0[p] = pack_bf16x2(__fmul_rn(sq[2 * p], cp), __fmul_rn(sq[2 * p + 1], cp));
+      t1[p] = pack_bf16x2(__fmul_rn(sq[8 + 2 * p], cp), __fmul_rn(sq[9 + 2 * p], cp));
+    }
+    *reinterpret_cast<u32x4_t*>(lut + lane * 32) = t0;
+    *reinterpret_cast<u32x4_t*>(lut + lane * 32 + 16) = t1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float cp = decode_constant(eraw[j], sraw[j], mu);
-      dequant_pair(craw[j], cp, sq, b[j][0], b[j][1]);
+      const uint32_t tab = lut_base + (uint32_t)(16 * j) * 32u;  // 32-byte aligned
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t w = craw[j][ks];
+        u32x4_t o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          u16x2_t v;
+          v.x = lds_read_u16(tab | code_x2(w, 8 * p));
+          v.y = lds_read_u16(tab | code_x2(w, 8 * p + 4));
+          o[p] = __builtin_bit_cast(uint32_t, v);
+        }
+        b[j][ks] = o;
+      }
     }
   };
   auto load_b2 = [&](u32x4_t (&b)[4][2], int l) {

@@ -178,3 +178,13 @@ def test_product_path_never_imports_the_oracle():
     for src in (ROOT / "quantized_fine_tuning_amd").rglob("*"):
         if src.suffix in (".py", ".hip", ".cpp", ".h"):
             assert "oracle" not in src.read_text(), src
+
+
+def test_single_hip_runtime_whatever_the_import_order():
+    # the library is handed torch's streams and device pointers, so both must
+    # use one HIP runtime
+    code = ("import quantized_fine_tuning_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = sorted(set(l.split()[-1] for l in maps if 'libamdhip64' in l))\n"
+            "assert len(libs) == 1, libs\n")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
