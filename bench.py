@@ -18,13 +18,21 @@ Extra objects on the JSON line:
                 M = 16, cycling through 64 quantized copies (about 0.55 GB, more
                 than twice the 256 MB last-level cache) so every launch streams
                 from HBM;
-  cpu_baseline  the oracle (numpy, fp64) on a bounded sample: the gate linear
-                alone (quantize + dequantize + forward + backward at M = 4096).
+  cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
+                of the same workload (quantize + dequantize + forward +
+                backward of the three linears at M = 4096).
+
+roofline.traffic is the HBM traffic (bytes per launch) of the dominant kernel
+as rocprofv3's FETCH_SIZE and WRITE_SIZE counters read it, scaled by what the
+same counters read for a plain copy of known size (--copy-calibration).  It
+is taken from the summary under profiles/ and reported only while the
+kernel's sources are byte-identical to the ones profiled; otherwise null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -42,6 +50,45 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Sources each GEMM kernel is compiled from (its traffic figure is tied to them).
+KERNEL_SOURCES = {
+    "fwd_gemm_kernel": ("fwd.hip", "common.h", "tiling.h"),
+    "dx_gemm_kernel": ("dx.hip", "common.h", "tiling.h"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_mlp7b.txt")
+
+
+def kernel_source_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "quantized_fine_tuning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel):
+    """Copy-calibrated FETCH_SIZE + WRITE_SIZE bytes per launch of `kernel`
+    from the committed counter summary, or None when the summary is missing or
+    was taken on other sources."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    rec, cur = {}, None
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) != 2 or ln.startswith("#"):
+            continue
+        if parts[0] == "kernel":
+            cur = rec.setdefault(parts[1], {})
+        elif cur is not None:
+            cur[parts[0]] = parts[1]
+    r = rec.get(kernel)
+    if not r or r.get("sources_sha256") != kernel_source_digest(kernel):
+        return None
+    return int(r["fetch_bytes_per_launch"]) + int(r["write_bytes_per_launch"])
 
 
 def linear_flops(M, N, K, r):
@@ -150,9 +197,10 @@ def run_mlp(torch, q, args):
     per_kernel["quantize"]["gbs"] = q_bytes / (per_kernel["quantize"]["avg_ms"] * 1e-3) / 1e9
     dom = max(("fwd_gemm", "dx_gemm"), key=lambda k: per_kernel[k]["total_ms_per_step"])
     ach = per_kernel[dom]["tflops"]
-    roofline = {"bound": "mfma", "kernel": {"fwd_gemm": "fwd_gemm_kernel", "dx_gemm": "dx_gemm_kernel"}[dom],
+    kname = {"fwd_gemm": "fwd_gemm_kernel", "dx_gemm": "dx_gemm_kernel"}[dom]
+    roofline = {"bound": "mfma", "kernel": kname,
                 "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(kname),
                 "avg_launch_ms": round(per_kernel[dom]["avg_ms"], 4),
                 "flop_per_launch": int(fwd_flop if dom == "fwd_gemm" else dx_flop)}
     return {"ms_per_step": ms_per_step, "flops": flops, "M": M, "r": r, "alpha": alpha,
@@ -211,20 +259,16 @@ def run_gemv(torch, q, args):
 
 
 def run_cpu_baseline():
-    """The oracle as it stands, timed on the host on the gate linear of the same
-    workload (one of its three layers): quantize + dequantize + fp64 forward +
-    fp64 backward at M = 4096."""
+    """The oracle as it stands, timed on the host over one whole step of the
+    same workload: for each of the three linears, quantize + dequantize + fp64
+    forward + fp64 backward at M = 4096."""
     import numpy as np
     from oracle import linalg, nf4
     from workloads import Inputs
 
     w = Inputs(3)
     M, r, alpha = w.w.tokens[0], w.w.rank, w.w.alpha
-    _, N, K = w.w.layers[0]
-    W = w.weight(0)
-    Xb, dYb, Ab, Bb = w.X(0, M), w.dY(0, M), w.lora_A(0), w.lora_B(0)
     f64 = linalg.bf16_to_f64
-    X, dY, A, B = f64(Xb), f64(dYb), f64(Ab), f64(Bb)
     blas_threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -232,22 +276,41 @@ def run_cpu_baseline():
                             if p.get("user_api") == "blas"), default=None)
     except Exception:
         pass
-    t0 = time.perf_counter()
-    ref = nf4.quantize(W)
-    wh = f64(nf4.dequantize(ref["codes"], ref["absmax_e4m3"], ref["dq_scale"],
-                            ref["dq_mean"])).reshape(N, K)
-    Y, T = linalg.linear_fwd(X, wh, A, B, alpha, r)
-    dX, dA, dB = linalg.linear_bwd(X, dY, wh, A, B, alpha, r)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(Y).all() and np.isfinite(dX).all()
-    flops = linear_flops(M, N, K, r)
+    dt, flops = 0.0, 0
+    for li, (name, N, K) in enumerate(w.w.layers):
+        W = w.weight(li)
+        X, dY = f64(w.X(li, M)), f64(w.dY(li, M))
+        A, B = f64(w.lora_A(li)), f64(w.lora_B(li))
+        t0 = time.perf_counter()
+        ref = nf4.quantize(W)
+        wh = f64(nf4.dequantize(ref["codes"], ref["absmax_e4m3"], ref["dq_scale"],
+                                ref["dq_mean"])).reshape(N, K)
+        Y, T = linalg.linear_fwd(X, wh, A, B, alpha, r)
+        dX, dA, dB = linalg.linear_bwd(X, dY, wh, A, B, alpha, r)
+        dt += time.perf_counter() - t0
+        assert np.isfinite(Y).all() and np.isfinite(dX).all()
+        flops += linear_flops(M, N, K, r)
+        log(f"[bench] cpu oracle: {name} done ({dt:.1f}s so far)")
     cores = len(os.sched_getaffinity(0))
-    log(f"[bench] cpu oracle: {dt:.1f}s on the gate linear")
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads or cores,
             "host_cores": cores, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"gate linear {N}x{K} of the same workload, M={M}, r={r}: numpy NF4+DQ "
-                      "quantize and dequantize (single-threaded numpy) + fp64 forward and "
-                      "backward (BLAS on the listed threads); 1 of the 3 linears of a step"}
+            "sample": f"one whole step of the same workload (gate, up, down; M={M}, r={r}): "
+                      "numpy NF4+DQ quantize and dequantize (single-threaded numpy) + fp64 "
+                      "forward and backward (BLAS on the listed threads); input generation "
+                      "not timed"}
+
+
+def copy_calibration(torch, mib):
+    """A plain device copy of known size, three times, for scaling the HBM
+    byte counters of a profiled run (the copy reads and writes `mib` MiB)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 copies of {mib} MiB")
+    del src, dst
 
 
 def main():
@@ -259,6 +322,8 @@ def main():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain copy of MIB MiB first (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -269,6 +334,8 @@ def main():
     import quantized_fine_tuning_amd as q
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
     mlp = run_mlp(torch, q, args)
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
