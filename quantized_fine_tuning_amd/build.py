@@ -13,10 +13,12 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
+INCLUDE = PKG.parent / "include"  # the C ABI header
 LIB = PKG / "libqlora_nf4.so"
 SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "gemm.hip", "fwd.hip", "dx.hip", "gemv.hip"]
 ARCH = "gfx950"
@@ -39,23 +41,38 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> Path:
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), *FLAGS, "-I", str(CSRC), "-o", str(tmp)]
-    for s in SOURCES:
-        src = CSRC / s
-        if src.suffix == ".cpp":
-            cmd += ["-x", "hip", str(src)]
-        else:
-            cmd += ["-x", "hip", str(src)]
+def build(verbose: bool = False, csrc: Path = CSRC, out: Path = LIB) -> Path:
+    """Compiles every source to an object (in parallel), then links."""
+    objdir = out.parent / "_build"
+    objdir.mkdir(exist_ok=True)
+    cc = hipcc()
+
+    def compile_one(name: str) -> Path:
+        obj = objdir / (name + ".o")
+        cmd = [cc, *[f for f in FLAGS if f != "-shared"], "-c", "-I", str(csrc), "-I", str(INCLUDE), "-x", "hip",
+               str(csrc / name), "-o", str(obj)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed on {name} with status {res.returncode}")
+        return obj
+
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = out.with_suffix(".so.tmp")
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc", "-o", str(tmp),
+           *map(str, objs)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"link failed with status {res.returncode}")
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,7 +1,7 @@
 // C ABI of the NF4 QLoRA library: argument validation (entirely on the host,
 // before any HIP call), workspace sizing and dispatch to the kernel launchers.
 // The declarations and their contracts are in include/qlora_nf4.h.
-#include "../../include/qlora_nf4.h"
+#include "qlora_nf4.h"
 
 #include <cstdarg>
 #include <cstdio>

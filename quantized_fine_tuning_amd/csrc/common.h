@@ -136,6 +136,12 @@ __device__ __forceinline__ void buf_load_lds16(rsrc_t r, void* lds, uint32_t vof
                                            (int)voff, (int)soff, 0, 0);
 }
 
+// The same for 4 bytes per lane: lane i's dword lands at lds + 4*i.
+__device__ __forceinline__ void buf_load_lds4(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           (int)voff, (int)soff, 0, 0);
+}
+
 // LDS as explicit 32-bit byte addresses: lets table lookups be formed as
 // base | (code * 2) (two VALU ops) when the table base is 32-byte aligned.
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
@@ -150,9 +156,54 @@ __device__ __forceinline__ uint32_t code_x2(uint32_t w, int pos) {
   return pos == 0 ? ((w << 1) & 0x1Eu) : ((w >> (pos - 1)) & 0x1Eu);
 }
 
+// Copies into LDS written as inline assembly.  The compiler does not see
+// their LDS writes, so it inserts no waits of its own in front of LDS reads
+// (with the builtins above it must assume any LDS read may alias a copy in
+// flight and waits for all of them); the caller orders every read of copied
+// data after wait_vmem()/wait_vmem_le<>() and, across waves, a barrier.
+// The resource is passed as its four descriptor words (held in SGPRs).
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int32_t)((a >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int32_t)b);                       // bytes
+  r.w = 0x00020000;                                                      // raw dwords
+  return r;
+}
+// lane i's 16 bytes at (voff + soff) land at lds + 16*i (lds wave-uniform)
+__device__ __forceinline__ void dma_lds16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r), "s"(so)
+               : "memory", "m0");
+}
+// lane i's dword at (voff + soff) lands at lds + 4*i
+__device__ __forceinline__ void dma_lds4(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r), "s"(so)
+               : "memory", "m0");
+}
+
 // Waits until every vector-memory load issued by this wave has completed
 // (including copies into LDS, which the compiler does not track).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order, so the older ones are done).  N < 16.
+// Written as assembly with a memory clobber, so that no LDS read of copied
+// data is moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

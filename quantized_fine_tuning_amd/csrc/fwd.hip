@@ -4,26 +4,31 @@
 // matmul and the LoRA path is added to the output.)
 //
 // Design
-//   * 256x256 output tile per workgroup, 4 waves; wave w owns the 64 weight
-//     rows [64w, 64w+64) of the tile and all 256 token rows, so every weight
-//     element is dequantized exactly once per workgroup, straight into
-//     registers: each lane turns 8 bytes of codes (16 consecutive k of one
-//     weight row) into the bf16 B operand of two v_mfma_f32_16x16x32_bf16.
-//     Within a 64-wide reduction step lane group q = lane/16 holds k in
-//     [16q, 16q+16); the A operand (X from LDS) uses the same k slots.
-//   * Dequantization goes through a per-row table: per step lane t writes
-//     the 16 values RNE_bf16(fl32(q_j * c')) of weight row 64w + t to LDS, and
-//     each code then costs one 2-byte table read (bit-identical to
-//     multiplying per element, since the value depends only on code and row).
-//   * X goes through a double-buffered LDS tile (256 rows x 64 k, 16-byte
-//     chunks XOR-swizzled by row) filled by buffer-to-LDS copies one step
-//     ahead (no staging registers); the codes of the next step are loaded one
-//     step ahead and dequantized after the current step's MFMAs are issued.
+//   * 256x256 output tile per workgroup of 8 waves, two per SIMD: while one
+//     wave of a SIMD issues MFMAs the other can issue its dequantization
+//     arithmetic (within one wave the two largely serialize).
+//   * Per 64-wide reduction step every wave dequantizes 32 of the tile's 256
+//     weight rows into a shared bf16 tile Ŵ[n][k] in LDS; then wave (wm, wn)
+//     multiplies token rows [128wm, +128) by weight rows [64wn, +64): 64
+//     v_mfma_f32_16x16x32_bf16 per wave and step, operands read from LDS.
+//   * Dequantization goes through a per-row table: lane t < 32 writes the 16
+//     values RNE_bf16(fl32(q_j * c')) of row t to LDS, and every code is one
+//     2-byte table read (bit-identical to multiplying per element, since the
+//     value depends only on code and row).  Lane l reads rows 8q + (l >> 3),
+//     k = 8(l & 7) + 0..7: the 8 lanes of one row hit its table, the 8 rows
+//     of one read hit 8 different groups of 8 banks, so reads never conflict.
+//   * Tiles are stored with 16-byte chunks XOR-swizzled by row (xswz) so that
+//     MFMA operand reads of 16 rows cover the 64 LDS banks once.
+//   * X and the weight data (packed codes, e4m3 bytes, group scales) of the
+//     next steps are loaded into registers at the top of an iteration and
+//     stored to LDS at its end, so no loaded register lives across
+//     iterations; the MFMAs of step s are interleaved in issue order with
+//     the dequantization of step s+1 into the other Ŵ buffer.
 //   * All operand reads are buffer loads whose resources end at the tensor's
 //     last row, so ragged tiles read zeros without per-lane branches.
 //   * The LoRA up-projection is 2*Rp/64 extra reduction steps whose A operand
 //     is the bf16 hi/lo split of s·T and whose B operand is the padded copy
-//     B2 = [B | 0 | B | 0] ([N, 2Rp] bf16).
+//     B2 = [B | 0 | B | 0] ([N, 2Rp] bf16), both copied straight into LDS.
 //   * Workgroups are mapped to tiles so that each XCD (workgroup id mod 8)
 //     walks a contiguous run of a grouped tile order (4 M-tiles per group):
 //     the ~32 workgroups resident on one XCD share X and code rows in its L2.
@@ -34,24 +39,34 @@ namespace qnf4 {
 namespace {
 
 constexpr int TM = 256, TN = 256, KSTEP = 64;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
 
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
+// A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
+// physical chunk c ^ ((r >> 1) & 7).  An MFMA operand read takes 16-byte
+// chunks of 16 consecutive rows per LDS cycle (64 banks of 4 bytes): the
+// pairs (r & 1, (r >> 1) & 7) are then all distinct, so the 16 chunks cover
+// the 64 banks once.
 __device__ __forceinline__ int xswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 template <int LSTEPS>
-__global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint16_t* __restrict__ X,
-                                                          int64_t M, const uint16_t* __restrict__ sT,
-                                                          const uint16_t* __restrict__ B2,
-                                                          int64_t Rp, void* __restrict__ Y,
-                                                          int y_bf16, int tiles_m, int tiles_n,
-                                                          Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char sx[2][TM * 128];
-  // per-wave tables: 64 weight rows x 16 bf16 (32 bytes); 256-byte alignment
-  // lets the compiler OR a table offset into a table base
-  __shared__ __attribute__((aligned(256))) char slut[4][64 * 32];
+__global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const uint16_t* __restrict__ X,
+                                                               int64_t M, const uint16_t* __restrict__ sT,
+                                                               const uint16_t* __restrict__ B2,
+                                                               int64_t Rp, void* __restrict__ Y,
+                                                               int y_bf16, int tiles_m, int tiles_n,
+                                                               Codebook cb) {
+  __shared__ __attribute__((aligned(16))) char sx[2][TM * 128];  // A tiles: X, then sT
+  __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
+  // per wave: tables of its 32 rows (row t at 32(t % 8) + 256(t / 8)), the
+  // packed codes of its rows (32 bytes each) and, per row, the dword holding
+  // its e4m3 byte and its group scale; code data double-buffered by step
+  __shared__ __attribute__((aligned(256))) char slut[kWaves][32 * 32];
+  __shared__ __attribute__((aligned(16))) char scode[2][kWaves][32 * 32];
+  __shared__ __attribute__((aligned(16))) uint32_t sconst[2][kWaves][2][32];
   __shared__ float sq[16];
   int tmi, tni;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni)) return;
@@ -59,6 +74,7 @@ __global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, n0 = (int64_t)tni * TN;
   const int ksteps = (int)(K / KSTEP);
@@ -75,167 +91,200 @@ __global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint1
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
 
-  // X tile: wave w copies tile rows [64w, 64w+64) straight into LDS, 8 rows
-  // (1 KB) per instruction.  Lane i lands in physical chunk i & 7 of row
-  // (i >> 3) of the group, so it fetches logical chunk (i & 7) ^ (i >> 3),
-  // which keeps the XOR swizzle of xswz().
-  const int lrow = 64 * wave + (lane >> 3);
-  const int lch = (lane & 7) ^ ((lane >> 3) & 7);
-  const uint32_t vx = (uint32_t)((lrow * K + 8 * lch) * 2);
-  const uint32_t vt = (uint32_t)((lrow * 2 * Rp + 8 * lch) * 2);
-  const uint32_t x_gstride = (uint32_t)(8 * K * 2), t_gstride = (uint32_t)(8 * 2 * Rp * 2);
-  auto copy_x = [&](char* t, int s) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      buf_load_lds16(rx, t + (64 * wave + 8 * c) * 128, vx, c * x_gstride + (uint32_t)s * 128u);
+  // X tile: thread τ moves 16 bytes of rows 64c + (τ >> 3), c = 0..3, into
+  // physical chunk τ & 7, so it fetches logical chunk (τ & 7) ^ ((τ >> 4) & 7)
+  // ((row >> 1) & 7 does not depend on c).  LDS offset 64c*128 + 16τ.
+  const int xlch = (tid & 7) ^ ((tid >> 4) & 7);
+  const uint32_t vx = (uint32_t)(((tid >> 3) * K + 8 * xlch) * 2);
+  const uint32_t x_gstride = (uint32_t)(64 * K * 2);
+  struct XRegs {
+    u32x4_t v[4];
   };
-  auto copy_t = [&](char* t, int l) {
+  auto load_x = [&](XRegs& r, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      buf_load_lds16(rt, t + (64 * wave + 8 * c) * 128, vt, c * t_gstride + (uint32_t)l * 128u);
+    for (int c = 0; c < 4; ++c) r.v[c] = buf_load16(rx, vx, c * x_gstride + (uint32_t)s * 128u);
+  };
+  auto store_x = [&](char* t, const XRegs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(t + 64 * c * 128 + 16 * tid) = r.v[c];
+  };
+  // LoRA tiles (sT rows, B2 rows) copied straight into LDS: wave w copies rows
+  // 32w + 8c + (i >> 3), c = 0..3; (row >> 1) & 7 = 4(c & 1) + (i >> 4), so
+  // odd c fetch logical chunk ^ 4 (byte offset ^ 64; row strides are
+  // multiples of 128 bytes).
+  const int llch = (lane & 7) ^ (lane >> 4);
+  const uint32_t vl = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * llch) * 2);
+  const uint32_t l_gstride = (uint32_t)(8 * 2 * Rp * 2);
+  auto copy_lora = [&](rsrc_t r, char* t, int l) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      buf_load_lds16(r, t + (32 * wave + 8 * c) * 128, (c & 1) ? (vl ^ 64u) : vl,
+                     c * l_gstride + (uint32_t)l * 128u);
   };
 
-  // B operand: this lane's weight rows are 64*wave + 16j + lr (tile-local)
-  const int brow = 64 * wave + lr;
-  const uint32_t vc = (uint32_t)(brow * (K / 2) + 8 * kq);
-  const uint32_t vb = (uint32_t)((brow * 2 * Rp + 16 * kq) * 2);
-  const uint32_t c_rstride = (uint32_t)(16 * (K / 2));
-  const uint32_t b_rstride = (uint32_t)(16 * 2 * Rp * 2);
-  u32x2_t craw[4];
-  uint32_t eraw;
-  float sraw;
-  // codes of rows 16j + lr (16 consecutive k each); the e4m3 byte and group
-  // scale of this lane's table row 64*wave + lane
-  const uint32_t ve_me = (uint32_t)(64 * wave + lane) * kpr;
-  const uint32_t blk_me = (uint32_t)(n0 + 64 * wave + lane) * kpr;
-  auto load_codes = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) craw[j] = buf_load8(rc, vc, j * c_rstride + (uint32_t)s * 32u);
-    eraw = buf_load1(re, ve_me, (uint32_t)s);
-    sraw = __uint_as_float(buf_load4(rs, ((blk_me + (uint32_t)s) / kDqBlock) * 4u, 0u));
+  // Weight data of the wave's rows [32w, 32w+32) for step t: lane l loads 16
+  // code bytes of row l/2 (half l%2); lane l < 32 the dword holding the e4m3
+  // byte of row l and that row's group scale (lanes >= 32 repeat them).
+  const uint32_t vcd = (uint32_t)((32 * wave + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
+  const int crow = 32 * wave + (lane & 31);
+  const uint32_t ve_me = (uint32_t)crow * kpr;
+  const uint32_t blk_me = (uint32_t)(n0 + crow) * kpr;
+  struct WRegs {
+    u32x4_t c;
+    uint32_t e, s;
   };
-  // B fragments of two consecutive steps (ping-pong, no copies)
-  u32x4_t bf[2][4][2];
+  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
+    r.c = buf_load16(rc, vcd, (uint32_t)t * 32u);
+    r.e = buf_load4(re, (ve_me + (uint32_t)t) & ~3u, 0u);
+    r.s = buf_load4(rs, ((blk_me + (uint32_t)t) / kDqBlock) * 4u, 0u);
+  };
+  auto store_w = [&](int slot, const WRegs& r) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4_t*>(scode[slot][wave] + 16 * lane) = r.c;
+    if (lane < 32) {
+      sconst[slot][wave][0][lane] = r.e;
+      sconst[slot][wave][1][lane] = r.s;
+    }
+  };
+
+  // Dequantization of step t (weight data in slot) into the tile `dst`.
   char* lut = slut[wave];
-  const uint32_t lut_base = lds_offset(lut) + (uint32_t)lr * 32u;  // row 16j + lr adds 512j
-  // Dequantize: lane t writes the table RNE_bf16(fl32(q_j * c')) of row t,
-  // then every code is one 2-byte lookup in the table of its row; pairs of
-  // consecutive k share a register.  (Rows past N only feed output columns
-  // past N, which are not stored.)
-  auto make_b = [&](u32x4_t (&b)[4][2]) {
-    const float cp = decode_constant(eraw, sraw, mu);
-    u32x4_t t0, t1;
+  const int dr = lane >> 3, dc = lane & 7;  // row 8q + dr of the wave, k-chunk dc
+  const uint32_t lut_lane = lds_offset(lut) + (uint32_t)dr * 32u;
+  auto build_table = [&](int t, int slot) __attribute__((always_inline)) {
+    if (lane < 32) {
+      const uint32_t e = (sconst[slot][wave][0][lane] >> (8 * ((ve_me + (uint32_t)t) & 3u))) & 0xffu;
+      const float cp = decode_constant(e, __uint_as_float(sconst[slot][wave][1][lane]), mu);
+      u32x4_t t0, t1;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        t0[p] = pack_bf16x2(__fmul_rn(sq[2 * p], cp), __fmul_rn(sq[2 * p + 1], cp));
+        t1[p] = pack_bf16x2(__fmul_rn(sq[8 + 2 * p], cp), __fmul_rn(sq[9 + 2 * p], cp));
+      }
+      char* row = lut + 32 * (lane & 7) + 256 * (lane >> 3);
+      *reinterpret_cast<u32x4_t*>(row) = t0;
+      *reinterpret_cast<u32x4_t*>(row + 16) = t1;
+    }
+  };
+  // rows 8q + dr: the code dword of k-chunk dc, its 8 table lookups, one
+  // 16-byte store of 8 consecutive bf16
+  auto dequant_group = [&](int slot, char* dst, int q) __attribute__((always_inline)) {
+    const uint32_t w =
+        *reinterpret_cast<const uint32_t*>(scode[slot][wave] + (8 * q + dr) * 32 + dc * 4);
+    const uint32_t tab = lut_lane + 256u * (uint32_t)q;  // 32-byte aligned
+    u32x4_t o;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      t0[p] = pack_bf16x2(__fmul_rn(sq[2 * p], cp), __fmul_rn(sq[2 * p + 1], cp));
-      t1[p] = pack_bf16x2(__fmul_rn(sq[8 + 2 * p], cp), __fmul_rn(sq[9 + 2 * p], cp));
+      u16x2_t v;
+      v.x = lds_read_u16(tab | code_x2(w, 8 * p));
+      v.y = lds_read_u16(tab | code_x2(w, 8 * p + 4));
+      o[p] = __builtin_bit_cast(uint32_t, v);
     }
-    *reinterpret_cast<u32x4_t*>(lut + lane * 32) = t0;
-    *reinterpret_cast<u32x4_t*>(lut + lane * 32 + 16) = t1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t tab = lut_base + (uint32_t)(16 * j) * 32u;  // 32-byte aligned
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint32_t w = craw[j][ks];
-        u32x4_t o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          u16x2_t v;
-          v.x = lds_read_u16(tab | code_x2(w, 8 * p));
-          v.y = lds_read_u16(tab | code_x2(w, 8 * p + 4));
-          o[p] = __builtin_bit_cast(uint32_t, v);
-        }
-        b[j][ks] = o;
-      }
-    }
-  };
-  auto load_b2 = [&](u32x4_t (&b)[4][2], int l) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b[j][0] = buf_load16(rb, vb, j * b_rstride + (uint32_t)l * 128u);
-      b[j][1] = buf_load16(rb, vb, j * b_rstride + (uint32_t)l * 128u + 16u);
-    }
+    *reinterpret_cast<u32x4_t*>(dst + xswz(32 * wave + 8 * q + dr, dc)) = o;
   };
 
-  f32x4_t acc[16][4];
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto mfma_step = [&](const char* t, const u32x4_t (&b)[4][2]) {
+  // MFMA group g (0..15) of a step: k-half ks = g / 8, token block i = g % 8;
+  // B fragments of the k-half are read at its first group.
+  const int arow = 128 * wm + lr, brow = 64 * wn + lr;
+  u32x4_t bfr[4];
+  auto mfma_group = [&](const char* xa, const char* wb, int g) __attribute__((always_inline)) {
+    const int ks = g >> 3, i = g & 7;
+    if (i == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + xswz(brow + 16 * j, 2 * kq + ks));
+    }
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xa + xswz(arow + 16 * i, 2 * kq + ks));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(t + xswz(16 * i + lr, 2 * kq + ks));
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+  };
+  auto mfma_step = [&](const char* xa, const char* wb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, b[j][ks], acc[i][j]);
-      }
+    for (int g = 0; g < 16; ++g) mfma_group(xa, wb, g);
+  };
+  // The MFMAs of one step interleaved with the dequantization of step t:
+  // table build next to the first groups, one row group of lookups every
+  // three MFMA groups.
+  auto mfma_step_dequant = [&](const char* xa, const char* wb, int t, int slot, char* dst)
+      __attribute__((always_inline)) {
+    build_table(t, slot);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      mfma_group(xa, wb, g);
+      if (g == 2 || g == 5 || g == 8 || g == 11) dequant_group(slot, dst, (g - 2) / 3);
     }
   };
 
-  auto roll = [&]() {
+  // prologue: X and weight data of step 0, weight data of step 1 (K >= 64,
+  // so step 0 is a weight step); dequantize step 0
+  {
+    XRegs xr;
+    WRegs w0, w1;
+    load_x(xr, 0);
+    load_w(w0, 0);
+    load_w(w1, 1);
+    store_x(sx[0], xr);
+    store_w(0, w0);
+    store_w(1, w1);
+  }
+  __syncthreads();
+  build_table(0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[0][j][0] = bf[1][j][0];
-      bf[0][j][1] = bf[1][j][1];
-    }
-  };
-
-  // prologue: step 0 (K >= 64, so step 0 is a weight step)
-  copy_x(sx[0], 0);
-  load_codes(0);
-  __syncthreads();  // codebook in LDS
-  make_b(bf[0]);
-  wait_vmem();
+  for (int q = 0; q < 4; ++q) dequant_group(0, sw[0], q);
   __syncthreads();
 
-  // Weight steps 0 .. ksteps-2: prefetch step s+1 (X into the other LDS
-  // buffer, codes into registers), MFMAs of step s, dequantize step s+1.
+  // Weight steps 0 .. ksteps-2: load X of step s+1 and the weight data of
+  // step s+2 into registers, issue the MFMAs of step s interleaved with the
+  // dequantization of step s+1 into the other Ŵ buffer, then store the
+  // loaded data into the other X buffer and weight slot s % 2 (both last read
+  // in the previous iteration).  (Weight data of step ksteps may be loaded:
+  // its reads stay inside the buffers or return zeros, and it is not used.)
   // One step per iteration and no other loop carrying the accumulators:
   // anything else makes the register allocator shuffle or spill them.
   for (int s = 0; s + 1 < ksteps; ++s) {
-    copy_x(sx[(s + 1) & 1], s + 1);
-    load_codes(s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(sx[s & 1], bf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    make_b(bf[1]);
-    wait_vmem();
+    XRegs xr;
+    WRegs wr;
+    load_x(xr, s + 1);
+    load_w(wr, s + 2);
+    mfma_step_dequant(sx[s & 1], sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
+    store_x(sx[(s + 1) & 1], xr);
+    store_w(s & 1, wr);
     __syncthreads();
-    roll();
   }
-  // Last weight step, prefetching LoRA step 0; then the LoRA steps, unrolled
-  // (A = [sT_hi | sT_lo] from LDS, B = B2 fragments loaded into registers).
-  copy_t(sx[ksteps & 1], 0);
-  load_b2(bf[1], 0);
-  mfma_step(sx[(ksteps - 1) & 1], bf[0]);
+  // Last weight step, copying LoRA step 0 (sT and B2 tiles) into the other
+  // buffers; then the LoRA steps, unrolled.
+  copy_lora(rt, sx[ksteps & 1], 0);
+  copy_lora(rb, sw[ksteps & 1], 0);
+  mfma_step(sx[(ksteps - 1) & 1], sw[(ksteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int l = 0; l < LSTEPS; ++l) {
     const int s = ksteps + l;
     if (l + 1 < LSTEPS) {
-      copy_t(sx[(s + 1) & 1], l + 1);
-      load_b2(bf[l & 1], l + 1);
+      copy_lora(rt, sx[(s + 1) & 1], l + 1);
+      copy_lora(rb, sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sx[s & 1], bf[(l + 1) & 1]);
+    mfma_step(sx[s & 1], sw[s & 1]);
     wait_vmem();
     __syncthreads();
   }
 
-  // epilogue: lane holds rows 16i + 4*kq + v of column 64*wave + 16j + lr.
+  // epilogue: lane holds rows 128wm + 16i + 4kq + v of column 64wn + 16j + lr.
   // The row/column bases go through an empty asm so that their address
   // arithmetic is not hoisted above the main loop (it would stay live there).
-  int row0 = 4 * kq, col0 = 64 * wave + lr;
+  int row0 = 128 * wm + 4 * kq, col0 = 64 * wn + lr;
   asm volatile("" : "+v"(row0), "+v"(col0));
   const bool full = (m0 + TM <= M) && (n0 + TN <= N);
   if (y_bf16) {
     uint16_t* Yb = static_cast<uint16_t*>(Y) + (m0 + row0) * N + n0 + col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
@@ -247,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void fwd_gemm_kernel(Nf4View W, const uint1
   } else {
     float* Yf = static_cast<float*>(Y) + (m0 + row0) * N + n0 + col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
@@ -288,7 +337,7 @@ hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const
   switch (2 * Rp / KSTEP) {
 #define QNF4_FWD_CASE(LS) \
   case LS:                \
-    fwd_gemm_kernel<LS><<<grid, 256, 0, st>>>(W, X, M, sT, B2, Rp, Y, yb, tm, tn, codebook()); \
+    fwd_gemm_kernel<LS><<<grid, kThreads, 0, st>>>(W, X, M, sT, B2, Rp, Y, yb, tm, tn, codebook()); \
     break;
     QNF4_FWD_CASE(1)
     QNF4_FWD_CASE(2)
