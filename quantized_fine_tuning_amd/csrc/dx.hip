@@ -6,23 +6,29 @@
 // The reduction runs over the weight's rows n while the codes are contiguous
 // along k, so the dequantized weight has to be transposed on its way to the
 // MFMA B operand.  Design:
-//   * 256x256 output tile per workgroup (token rows x input features), 4
-//     waves; wave w owns the 64 output columns [64w, 64w+64), which lie in one
-//     NF4 block per weight row.
-//   * dY tiles (256 rows x 64 n) stream into double-buffered LDS by
-//     buffer-to-LDS copies, as X does in the forward product.
-//   * Per reduction step each wave dequantizes its 64 n x 64 k weight tile:
-//       - lane i builds the 16-entry bf16 table RNE_bf16(fl32(q_j * c')) of
-//         weight row i (the block's scaled codebook) in LDS;
-//       - lane (rg, cg) owns rows 8rg..8rg+7 by columns 8cg..8cg+7; every
-//         code becomes one 2-byte table read (two VALU ops for the address),
-//         consecutive rows are paired in one register, so the values come
-//         out already transposed (pairs along n) and go to a per-wave [k][n]
-//         LDS tile;
-//       - the wave reads its B fragments back from that tile.
-//     Rows past N get an all-zero table, so a ragged last step adds nothing.
-//   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B read
-//     from AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A).
+//   * 256x256 output tile per workgroup (token rows x input features) of 8
+//     waves, two per SIMD, so that one wave's dequantization arithmetic can
+//     issue while the other wave's MFMAs run.
+//   * Per 64-row reduction step every wave dequantizes 32 of the tile's 256
+//     columns (half an NF4 block column) for all 64 weight rows into a shared
+//     transposed bf16 tile Ŵᵀ[k][n] in LDS; then wave (wm, wk) multiplies
+//     token rows [128wm, +128) by columns [64wk, +64): 64
+//     v_mfma_f32_16x16x32_bf16 per wave and step, operands read from LDS.
+//   * Dequantization goes through a per-row table: lane t writes the 16
+//     values RNE_bf16(fl32(q_j * c')) of weight row t (its block's scaled
+//     codebook) to LDS; lane (rg, cg) then owns rows 8rg..8rg+7 by columns
+//     4cg..4cg+3 of the wave's slice, each code one 2-byte table read, and
+//     packs 8 consecutive rows of one column into one 16-byte store: the
+//     values come out already transposed.  Table slots, tile swizzles and
+//     lane maps are chosen so that lookups, stores and fragment reads are
+//     free of LDS bank conflicts (32 banks of 4 bytes).
+//   * dY and the weight data of the next steps are loaded into registers at
+//     the top of an iteration and stored to LDS at its end; the MFMAs of
+//     step s are interleaved in issue order with the dequantization of step
+//     s+1 into the other Ŵᵀ buffer.  Rows past N get an all-zero table.
+//   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
+//     AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A), both
+//     copied straight into LDS.
 #include "host.h"
 #include "tiling.h"
 
@@ -30,46 +36,52 @@ namespace qnf4 {
 namespace {
 
 constexpr int TM = 256, TK = 256, NSTEP = 64;
-
-__device__ __forceinline__ int swz128(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
-// [k][n] weight tile: the chunk is XORed with (row ^ row/8) & 7 so that both
-// the transposing writes (8 lanes per chunk column, rows 8 apart) and the
-// fragment reads (16 consecutive rows) spread over all banks.
-__device__ __forceinline__ int wswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
 
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
+// dY tile (token rows, 64 n each): chunk c of row r at physical c ^ (r & 7);
+// a fragment read gives the 8 lanes of one LDS cycle 8 consecutive rows.
+__device__ __forceinline__ int xswz(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+// Ŵᵀ tile (k rows, 64 n each): chunk c of row r at physical
+// c ^ ((r ^ (r >> 2)) & 7), distinct both for 8 consecutive rows (fragment
+// reads) and for rows 4cg + c, cg = 0..7 (the dequantization stores).
+__device__ __forceinline__ int wswz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row ^ (row >> 2)) & 7)) << 4);
+}
+
 template <int LSTEPS>
-__global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16_t* __restrict__ dY,
-                                                         int64_t M, const uint16_t* __restrict__ sU,
-                                                         const uint16_t* __restrict__ AT2,
-                                                         int64_t Rp, void* __restrict__ dX,
-                                                         int dx_bf16, int tiles_m, int tiles_k,
-                                                         Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char sa[2][TM * 128];   // dY tiles
-  __shared__ __attribute__((aligned(16))) char swt[4][64 * 128];  // per-wave [k][n] weight tile
-  // per-wave tables, 64 rows of 32 bytes; 256-byte alignment lets the
-  // compiler OR (not add) a table offset into a table base
-  __shared__ __attribute__((aligned(256))) char slut[4][64 * 32];
+__global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const uint16_t* __restrict__ dY,
+                                                              int64_t M, const uint16_t* __restrict__ sU,
+                                                              const uint16_t* __restrict__ AT2,
+                                                              int64_t Rp, void* __restrict__ dX,
+                                                              int dx_bf16, int tiles_m, int tiles_k,
+                                                              Codebook cb) {
+  __shared__ __attribute__((aligned(16))) char sa[2][TM * 128];  // A tiles: dY, then sU
+  __shared__ __attribute__((aligned(16))) char sw[2][TK * 128];  // B tiles: Ŵᵀ, then AT2
+  // per wave (all wave-private, so one buffer each): 64 row tables of 32
+  // bytes, the 16 code bytes of each weight row for the wave's 32 columns,
+  // and each table row's e4m3 byte and group scale
+  __shared__ __attribute__((aligned(256))) char slut[kWaves][64 * 32];
+  __shared__ __attribute__((aligned(16))) char scode[kWaves][64 * 16];
+  __shared__ __attribute__((aligned(16))) uint32_t sconst[kWaves][2][64];
   __shared__ float sq[16];
   int tmi, tki;
   if (!tile_of(blockIdx.x, tiles_m, tiles_k, tmi, tki)) return;
   if (threadIdx.x < 16) sq[threadIdx.x] = cb.q[threadIdx.x];
-  __syncthreads();
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
+  const int wm = wave >> 2, wk = wave & 3;
   const int rg = lane >> 3, cg = lane & 7;
   const int64_t K = W.K, N = W.N;
-  const int64_t m0 = (int64_t)tmi * TM;
-  const int64_t kw0 = (int64_t)tki * TK + 64 * wave;  // first output column of this wave
+  const int64_t m0 = (int64_t)tmi * TM, k0 = (int64_t)tki * TK;
+  const int64_t kw0 = k0 + 32 * wave;  // first column of this wave's dequantization slice
   const int nsteps = (int)((N + NSTEP - 1) / NSTEP);
   const uint32_t kpr = (uint32_t)(K / kBlock);
-  const uint32_t kbw = (uint32_t)(kw0 / kBlock);  // the wave's block column
+  const uint32_t kbw = (uint32_t)(kw0 / kBlock);  // the slice's block column
   const bool wave_cols_ok = kw0 < K;
   const float mu = *W.mu;
 
@@ -78,54 +90,72 @@ __global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16
   const rsrc_t rc = make_rsrc(W.codes, N * (K / 2));
   const rsrc_t re = make_rsrc(W.e, N * kpr);
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
-  const rsrc_t rat = make_rsrc(AT2 + kw0 * 2 * Rp, (K - kw0) * 2 * Rp * 2);
+  const rsrc_t rat = make_rsrc(AT2 + k0 * 2 * Rp, (K - k0) * 2 * Rp * 2);
 
-  // ---- dY (or sU) tile copies: wave w fills tile rows [64w, 64w+64)
-  const int lrow = 64 * wave + (lane >> 3);
-  const int lch = (lane & 7) ^ ((lane >> 3) & 7);
-  const uint32_t vdy = (uint32_t)((lrow * N + 8 * lch) * 2);
-  const uint32_t vsu = (uint32_t)((lrow * 2 * Rp + 8 * lch) * 2);
-  const uint32_t dy_gstride = (uint32_t)(8 * N * 2), su_gstride = (uint32_t)(8 * 2 * Rp * 2);
-  auto copy_dy = [&](char* t, int s) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      buf_load_lds16(rdy, t + (64 * wave + 8 * c) * 128, vdy, c * dy_gstride + (uint32_t)s * 128u);
+  // dY tile: thread τ moves 16 bytes of rows 64c + (τ >> 3), c = 0..3, into
+  // physical chunk τ & 7: logical chunk (τ & 7) ^ ((τ >> 3) & 7).
+  const int ylch = (tid & 7) ^ ((tid >> 3) & 7);
+  const uint32_t vy = (uint32_t)(((tid >> 3) * N + 8 * ylch) * 2);
+  const uint32_t y_gstride = (uint32_t)(64 * N * 2);
+  struct YRegs {
+    u32x4_t v[4];
   };
-  auto copy_su = [&](char* t, int l) {
+  auto load_y = [&](YRegs& r, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      buf_load_lds16(rsu, t + (64 * wave + 8 * c) * 128, vsu, c * su_gstride + (uint32_t)l * 128u);
+    for (int c = 0; c < 4; ++c) r.v[c] = buf_load16(rdy, vy, c * y_gstride + (uint32_t)s * 128u);
+  };
+  auto store_y = [&](char* t, const YRegs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(t + 64 * c * 128 + 16 * tid) = r.v[c];
+  };
+  // LoRA tiles copied straight into LDS: wave w copies rows 32w + 8c + (i >> 3),
+  // lane i into physical chunk i & 7.  sU rows use xswz, AT2 rows wswz.
+  const uint32_t vsu = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  auto copy_su = [&](char* t, int l) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      buf_load_lds16(rsu, t + (32 * wave + 8 * c) * 128, vsu, c * (uint32_t)(8 * 2 * Rp * 2) + (uint32_t)l * 128u);
+  };
+  auto copy_at = [&](char* t, int l) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = 32 * wave + 8 * c + (lane >> 3);
+      const int lch = (lane & 7) ^ ((row ^ (row >> 2)) & 7);
+      buf_load_lds16(rat, t + (32 * wave + 8 * c) * 128, (uint32_t)((row * 2 * Rp + 8 * lch) * 2),
+                     (uint32_t)l * 128u);
+    }
   };
 
-  // ---- weight codes of step s: rows s*64 + 8rg + i, columns kw0 + 8cg .. +7
-  const uint32_t vcode = (uint32_t)(8 * rg * (K / 2) + (kw0 + 8 * cg) / 2);
-  const uint32_t code_rstride = (uint32_t)(K / 2);
+  // Weight data for step t: lane l loads the 16 code bytes of weight row
+  // t*64 + l over the wave's 32 columns, the e4m3 byte of block (row, kbw)
+  // and that block's group scale.
+  const uint32_t vcode = (uint32_t)(lane * (K / 2) + kw0 / 2);
   const uint32_t code_sstride = (uint32_t)(NSTEP * (K / 2));
-  uint32_t cw[8];
-  uint32_t eraw;
-  float sraw;
-  auto load_codes = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cw[i] = buf_load4(rc, vcode, (uint32_t)s * code_sstride + i * code_rstride);
-    // this lane's table row: n = s*64 + lane, block column kbw
-    const uint32_t blk = ((uint32_t)s * NSTEP + lane) * kpr + kbw;
-    eraw = buf_load1(re, blk, 0u);
-    sraw = __uint_as_float(buf_load4(rs, (blk / kDqBlock) * 4u, 0u));
+  struct WRegs {
+    u32x4_t c;
+    uint32_t e, s;
+  };
+  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
+    r.c = buf_load16(rc, vcode, (uint32_t)t * code_sstride);
+    const uint32_t blk = ((uint32_t)t * NSTEP + lane) * kpr + kbw;
+    r.e = buf_load1(re, blk, 0u);
+    r.s = buf_load4(rs, (blk / kDqBlock) * 4u, 0u);
+  };
+  auto store_w = [&](const WRegs& r) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4_t*>(scode[wave] + 16 * lane) = r.c;
+    sconst[wave][0][lane] = r.e;
+    sconst[wave][1][lane] = r.s;
   };
 
+  // Dequantization of step t (weight data in the wave's buffers) into dst.
   char* lut = slut[wave];
   const uint32_t lut_addr = lds_offset(lut);
-  char* wt = swt[wave];
-  // Table of row t (= lane) at slot 8*(t & 7) + ((t ^ (t >> 3)) & 7): slot mod
-  // 8 (the bank group of a 32-byte table) differs across 8 consecutive t (the
-  // table writes) and across t = 8rg + i for fixed i (one lookup instruction).
+  // table of row t (= lane) at slot 8(t & 7) + ((t ^ (t >> 3)) & 7): row 8rg + i
+  // sits at slot 8i + (i ^ rg), byte offset 256i + 32(i ^ rg)
   const int my_slot = 8 * (lane & 7) + ((lane ^ (lane >> 3)) & 7);
-  // row 8rg + i sits at slot 8i + (i ^ rg): byte offset 256i + 32(i ^ rg)
-  u32x4_t bf[2][4][2];
-  // Dequantize step s (codes already in cw/eraw/sraw) into bf[1].
-  auto dequant = [&](int s) {
-    const bool row_ok = wave_cols_ok && ((int64_t)s * NSTEP + lane < N);
-    const float cp = decode_constant(eraw, sraw, mu);
+  auto build_table = [&](int t) __attribute__((always_inline)) {
+    const bool row_ok = wave_cols_ok && ((int64_t)t * NSTEP + lane < N);
+    const float cp = decode_constant(sconst[wave][0][lane], __uint_as_float(sconst[wave][1][lane]), mu);
     u32x4_t t0, t1;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -134,88 +164,108 @@ __global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16
     }
     *reinterpret_cast<u32x4_t*>(lut + my_slot * 32) = t0;
     *reinterpret_cast<u32x4_t*>(lut + my_slot * 32 + 16) = t1;
-    // look up 8 rows x 8 columns, pairing rows (2p, 2p+1) in one register;
-    // one column at a time keeps few lookups in flight (register pressure)
-    uint32_t tab[8];  // table of row 8rg + i: 32-byte aligned LDS address
+  };
+  // Column pair cp2 (columns 4cg + 2cp2, +1) of rows 8rg..8rg+7: 16
+  // lookups, two 16-byte stores of 8 rows each.
+  auto dequant_cols = [&](char* dst, int cp2) __attribute__((always_inline)) {
+    uint32_t w2[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tab[i] = lut_addr + 256u * i + 32u * (uint32_t)(i ^ rg);
+    for (int i = 0; i < 8; ++i)
+      w2[i] = *reinterpret_cast<const uint16_t*>(scode[wave] + (8 * rg + i) * 16 + 2 * cg);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int cc = 0; cc < 2; ++cc) {
+      const int c = 2 * cp2 + cc;
       u32x4_t o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         u16x2_t v;
-        v.x = lds_read_u16(tab[2 * p] | code_x2(cw[2 * p], 4 * c));
-        v.y = lds_read_u16(tab[2 * p + 1] | code_x2(cw[2 * p + 1], 4 * c));
+        v.x = lds_read_u16((lut_addr + 256u * (2 * p) + 32u * (uint32_t)((2 * p) ^ rg)) |
+                           code_x2(w2[2 * p], 4 * c));
+        v.y = lds_read_u16((lut_addr + 256u * (2 * p + 1) + 32u * (uint32_t)((2 * p + 1) ^ rg)) |
+                           code_x2(w2[2 * p + 1], 4 * c));
         o[p] = __builtin_bit_cast(uint32_t, v);
       }
-      *reinterpret_cast<u32x4_t*>(wt + wswz(8 * cg + c, rg)) = o;
-      if (c & 1) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        bf[1][j][ks] = *reinterpret_cast<const u32x4_t*>(wt + wswz(16 * j + lr, 2 * kq + ks));
-  };
-  // LoRA B fragments of tail step l: AT2[kw0 + 16j + lr][64l + 16kq + 8ks ..]
-  const uint32_t vat = (uint32_t)((lr * 2 * Rp + 16 * kq) * 2);
-  const uint32_t at_jstride = (uint32_t)(16 * 2 * Rp * 2);
-  auto load_at = [&](u32x4_t (&b)[4][2], int l) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b[j][0] = buf_load16(rat, vat, j * at_jstride + (uint32_t)l * 128u);
-      b[j][1] = buf_load16(rat, vat, j * at_jstride + (uint32_t)l * 128u + 16u);
-    }
-  };
-  auto roll = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf[0][j][0] = bf[1][j][0];
-      bf[0][j][1] = bf[1][j][1];
+      *reinterpret_cast<u32x4_t*>(dst + wswz(32 * wave + 4 * cg + c, rg)) = o;
     }
   };
 
-  f32x4_t acc[16][4];
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mfma_step = [&](const char* t, const u32x4_t (&b)[4][2]) {
+
+  // MFMA group g (0..15): n-half ks = g / 8, token block i = g % 8; the B
+  // fragments of the half are read at its first group.
+  const int arow = 128 * wm + lr, brow = 64 * wk + lr;
+  u32x4_t bfr[4];
+  auto mfma_group = [&](const char* ya, const char* wb, int g) __attribute__((always_inline)) {
+    const int ks = g >> 3, i = g & 7;
+    if (i == 0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + wswz(brow + 16 * j, 2 * kq + ks));
+    }
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ya + xswz(arow + 16 * i, 2 * kq + ks));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(t + swz128(16 * i + lr, 2 * kq + ks));
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+  };
+  auto mfma_step = [&](const char* ya, const char* wb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, b[j][ks], acc[i][j]);
-      }
+    for (int g = 0; g < 16; ++g) mfma_group(ya, wb, g);
+  };
+  auto mfma_step_dequant = [&](const char* ya, const char* wb, int t, char* dst)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      mfma_group(ya, wb, g);
+      if (g == 0) build_table(t);
+      if (g == 4 || g == 10) dequant_cols(dst, (g - 4) / 6);
     }
   };
 
-  // prologue: step 0
-  copy_dy(sa[0], 0);
-  load_codes(0);
-  dequant(0);
-  roll();
-  wait_vmem();
+  // prologue: dY and weight data of step 0; dequantize step 0; weight data
+  // of step 1
+  {
+    YRegs yr;
+    WRegs w0;
+    load_y(yr, 0);
+    load_w(w0, 0);
+    store_y(sa[0], yr);
+    store_w(w0);
+  }
+  __syncthreads();  // codebook, dY of step 0
+  build_table(0);
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) dequant_cols(sw[0], c2);
+  {
+    WRegs w1;
+    load_w(w1, 1);
+    store_w(w1);
+  }
   __syncthreads();
 
+  // Reduction steps 0 .. nsteps-2: load dY of step s+1 and the weight data
+  // of step s+2, issue the MFMAs of step s interleaved with the
+  // dequantization of step s+1 into the other Ŵᵀ buffer, then store the
+  // loaded data (the weight buffers are wave-private and were last read
+  // earlier in this iteration).  Weight data of step nsteps may be loaded:
+  // its reads stay inside the buffers or return zeros, and it is not used.
   for (int s = 0; s + 1 < nsteps; ++s) {
-    copy_dy(sa[(s + 1) & 1], s + 1);
-    load_codes(s + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(sa[s & 1], bf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    dequant(s + 1);
-    wait_vmem();
+    YRegs yr;
+    WRegs wr;
+    load_y(yr, s + 1);
+    load_w(wr, s + 2);
+    mfma_step_dequant(sa[s & 1], sw[s & 1], s + 1, sw[(s + 1) & 1]);
+    store_y(sa[(s + 1) & 1], yr);
+    store_w(wr);
     __syncthreads();
-    roll();
   }
-  // last weight step, prefetching LoRA step 0; then the unrolled LoRA tail
+  // last reduction step, copying LoRA step 0 (sU and AT2 tiles) into the
+  // other buffers; then the LoRA steps, unrolled
   copy_su(sa[nsteps & 1], 0);
-  load_at(bf[1], 0);
-  mfma_step(sa[(nsteps - 1) & 1], bf[0]);
+  copy_at(sw[nsteps & 1], 0);
+  mfma_step(sa[(nsteps - 1) & 1], sw[(nsteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
 #pragma unroll
@@ -223,38 +273,38 @@ __global__ __launch_bounds__(256, 1) void dx_gemm_kernel(Nf4View W, const uint16
     const int s = nsteps + l;
     if (l + 1 < LSTEPS) {
       copy_su(sa[(s + 1) & 1], l + 1);
-      load_at(bf[l & 1], l + 1);
+      copy_at(sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sa[s & 1], bf[(l + 1) & 1]);
+    mfma_step(sa[s & 1], sw[s & 1]);
     wait_vmem();
     __syncthreads();
   }
 
-  // epilogue: lane holds rows 16i + 4*kq + v of column kw0 + 16j + lr
-  int row0 = 4 * kq, col0 = lr;
+  // epilogue: lane holds rows 128wm + 16i + 4kq + v of column k0 + 64wk + 16j + lr
+  int row0 = 128 * wm + 4 * kq, col0 = 64 * wk + lr;
   asm volatile("" : "+v"(row0), "+v"(col0));
-  const bool full = (m0 + TM <= M) && (kw0 + 64 <= K);
+  const bool full = (m0 + TM <= M) && (k0 + TK <= K);
   if (dx_bf16) {
-    uint16_t* D = static_cast<uint16_t*>(dX) + (m0 + row0) * K + kw0 + col0;
+    uint16_t* D = static_cast<uint16_t*>(dX) + (m0 + row0) * K + k0 + col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, k = kw0 + col0 + 16 * j;
+          const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
           if (full || (m < M && k < K))
             D[(16 * i + v) * K + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
         }
   } else {
-    float* D = static_cast<float*>(dX) + (m0 + row0) * K + kw0 + col0;
+    float* D = static_cast<float*>(dX) + (m0 + row0) * K + k0 + col0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, k = kw0 + col0 + 16 * j;
+          const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
           if (full || (m < M && k < K)) D[(16 * i + v) * K + 16 * j] = acc[i][j][v];
         }
   }
@@ -283,7 +333,7 @@ hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const
   switch (2 * Rp / NSTEP) {
 #define QNF4_DX_CASE(LS) \
   case LS:               \
-    dx_gemm_kernel<LS><<<grid, 256, 0, st>>>(W, dY, M, sU, AT2, Rp, dX, db, tm, tk, codebook()); \
+    dx_gemm_kernel<LS><<<grid, kThreads, 0, st>>>(W, dY, M, sU, AT2, Rp, dX, db, tm, tk, codebook()); \
     break;
     QNF4_DX_CASE(1)
     QNF4_DX_CASE(2)

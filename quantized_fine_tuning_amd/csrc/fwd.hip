@@ -15,10 +15,11 @@
 //     values RNE_bf16(fl32(q_j * c')) of row t to LDS, and every code is one
 //     2-byte table read (bit-identical to multiplying per element, since the
 //     value depends only on code and row).  Lane l reads rows 8q + (l >> 3),
-//     k = 8(l & 7) + 0..7: the 8 lanes of one row hit its table, the 8 rows
-//     of one read hit 8 different groups of 8 banks, so reads never conflict.
+//     k = 8(l & 7) + 0..7: the 8 lanes of one row hit its table, and the 4
+//     rows of each half-wave (served in one LDS cycle) hit 4 different
+//     groups of 8 of the 32 banks, so lookups never conflict.
 //   * Tiles are stored with 16-byte chunks XOR-swizzled by row (xswz) so that
-//     MFMA operand reads of 16 rows cover the 64 LDS banks once.
+//     MFMA operand reads of 8 rows cover the 32 LDS banks once.
 //   * X and the weight data (packed codes, e4m3 bytes, group scales) of the
 //     next steps are loaded into registers at the top of an iteration and
 //     stored to LDS at its end, so no loaded register lives across
@@ -44,12 +45,11 @@ constexpr int kWaves = 8, kThreads = 64 * kWaves;
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
 // A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
-// physical chunk c ^ ((r >> 1) & 7).  An MFMA operand read takes 16-byte
-// chunks of 16 consecutive rows per LDS cycle (64 banks of 4 bytes): the
-// pairs (r & 1, (r >> 1) & 7) are then all distinct, so the 16 chunks cover
-// the 64 banks once.
+// physical chunk c ^ (r & 7).  LDS has 32 banks of 4 bytes and serves a
+// 16-byte read for 8 lanes per cycle: an MFMA operand read gives those 8
+// lanes 8 consecutive rows, whose chunks then cover the 32 banks once.
 __device__ __forceinline__ int xswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
 
 template <int LSTEPS>
@@ -92,9 +92,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
 
   // X tile: thread τ moves 16 bytes of rows 64c + (τ >> 3), c = 0..3, into
-  // physical chunk τ & 7, so it fetches logical chunk (τ & 7) ^ ((τ >> 4) & 7)
-  // ((row >> 1) & 7 does not depend on c).  LDS offset 64c*128 + 16τ.
-  const int xlch = (tid & 7) ^ ((tid >> 4) & 7);
+  // physical chunk τ & 7, so it fetches logical chunk (τ & 7) ^ ((τ >> 3) & 7)
+  // (row & 7 does not depend on c).  LDS offset 64c*128 + 16τ.
+  const int xlch = (tid & 7) ^ ((tid >> 3) & 7);
   const uint32_t vx = (uint32_t)(((tid >> 3) * K + 8 * xlch) * 2);
   const uint32_t x_gstride = (uint32_t)(64 * K * 2);
   struct XRegs {
@@ -109,17 +109,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(t + 64 * c * 128 + 16 * tid) = r.v[c];
   };
   // LoRA tiles (sT rows, B2 rows) copied straight into LDS: wave w copies rows
-  // 32w + 8c + (i >> 3), c = 0..3; (row >> 1) & 7 = 4(c & 1) + (i >> 4), so
-  // odd c fetch logical chunk ^ 4 (byte offset ^ 64; row strides are
-  // multiples of 128 bytes).
-  const int llch = (lane & 7) ^ (lane >> 4);
+  // 32w + 8c + (i >> 3), c = 0..3, lane i into physical chunk i & 7, so it
+  // fetches logical chunk (i & 7) ^ (i >> 3).
+  const int llch = (lane & 7) ^ (lane >> 3);
   const uint32_t vl = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * llch) * 2);
   const uint32_t l_gstride = (uint32_t)(8 * 2 * Rp * 2);
   auto copy_lora = [&](rsrc_t r, char* t, int l) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      buf_load_lds16(r, t + (32 * wave + 8 * c) * 128, (c & 1) ? (vl ^ 64u) : vl,
-                     c * l_gstride + (uint32_t)l * 128u);
+      buf_load_lds16(r, t + (32 * wave + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
   };
 
   // Weight data of the wave's rows [32w, 32w+32) for step t: lane l loads 16
