@@ -329,12 +329,11 @@ hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const
   const int tm = (int)((M + TM - 1) / TM), tk = (int)((W.K + TK - 1) / TK);
   const unsigned grid = tile_grid(tm, tk);
   const int db = dx_bf16 ? 1 : 0;
-  TimedLaunch tl(kKernDxGemm, st);
   switch (2 * Rp / NSTEP) {
-#define QNF4_DX_CASE(LS) \
-  case LS:               \
-    dx_gemm_kernel<LS><<<grid, kThreads, 0, st>>>(W, dY, M, sU, AT2, Rp, dX, db, tm, tk, codebook()); \
-    break;
+#define QNF4_DX_CASE(LS)                                                                      \
+  case LS:                                                                                    \
+    return timed_launch(kKernDxGemm, dx_gemm_kernel<LS>, dim3(grid), dim3(kThreads), st, W, dY, M, \
+                        (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook());
     QNF4_DX_CASE(1)
     QNF4_DX_CASE(2)
     QNF4_DX_CASE(3)

@@ -331,12 +331,11 @@ hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const
   const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
   const unsigned grid = tile_grid(tm, tn);
   const int yb = y_bf16 ? 1 : 0;
-  TimedLaunch tl(kKernFwdGemm, st);
   switch (2 * Rp / KSTEP) {
-#define QNF4_FWD_CASE(LS) \
-  case LS:                \
-    fwd_gemm_kernel<LS><<<grid, kThreads, 0, st>>>(W, X, M, sT, B2, Rp, Y, yb, tm, tn, codebook()); \
-    break;
+#define QNF4_FWD_CASE(LS)                                                                   \
+  case LS:                                                                                  \
+    return timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS>, dim3(grid), dim3(kThreads), st, W, X, M, \
+                        (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook());
     QNF4_FWD_CASE(1)
     QNF4_FWD_CASE(2)
     QNF4_FWD_CASE(3)

@@ -3,135 +3,206 @@
 // P2 §六 and P5 (follow-up 1): at inference the 4-bit weight is dequantized to
 // 16 bit on the fly for every product; with few tokens the product is bound by
 // streaming the packed codes from HBM, so this path reads each code exactly
-// once and keeps everything else small.
+// once, keeps as many bytes in flight as possible and everything else small.
 //
-//   lora_down_small_kernel  T[m][j] = Σ_k X[m][k]·A[j][k] in fp32, one
-//                           workgroup per j, fixed-order reduction.
-//   gemv_kernel             one workgroup per 16 weight rows, 4 waves splitting
-//                           K round-robin by 64-blocks.  Each lane turns 16 codes
-//                           (8 bytes) of one row into bf16 in registers and feeds
-//                           them straight into v_mfma_f32_16x16x32_bf16 as the B
-//                           operand (X rows padded to 16 are the A operand).  The
-//                           four partial sums are combined in a fixed order and
-//                           the LoRA term s·Σ_j T[m][j]·B[n][j] is added in fp32.
+//   lora_down_small_kernel  T = X·Aᵀ (M x r, fp32) for one 16-wide slice of r
+//                           per workgroup: 8 waves split K, MFMA products,
+//                           fixed-order combination of the 8 partial tiles.
+//   gemv_kernel             one workgroup of 16 waves per 16 weight rows.  Lane
+//                           (row l % 16, q = l / 16) owns whole NF4 blocks (64
+//                           codes, one decoded constant c'); a "block group" is
+//                           4 consecutive blocks of the 16 rows, q taking one
+//                           each, and feeds 8 v_mfma_f32_16x16x32_bf16: MFMA t
+//                           takes codes 8t..8t+7 of every lane's block (the
+//                           A operand, X padded to 16 rows, uses the same
+//                           k slots).  Wave w takes block groups w, w+16, ...;
+//                           the codes, constants and X fragments of its next
+//                           group are loaded before the current one is
+//                           dequantized.  Each value is RNE_bf16(fl32(q_c * c'))
+//                           with q_c read from a 16-entry LDS codebook (one
+//                           address per code: no bank conflicts).  The 16
+//                           partial tiles are combined in a fixed order and
+//                           s·Σ_j T[m][j]·B[n][j] is added in fp32, one
+//                           thread per output.
 #include "host.h"
 
 namespace qnf4 {
 namespace {
 
-__global__ __launch_bounds__(256) void lora_down_small_kernel(const uint16_t* __restrict__ X,
-                                                              int M, int64_t K,
-                                                              const uint16_t* __restrict__ A,
-                                                              int r, float* __restrict__ T) {
-  __shared__ float s_part[4][16];
-  const int j = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float acc[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) acc[m] = 0.0f;
-  for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * 256) {
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(A + (int64_t)j * K + k);
-    float af[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[2 * i] = bf16lo(a[i]);
-      af[2 * i + 1] = bf16hi(a[i]);
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      if (m < M) {
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(X + (int64_t)m * K + k);
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s = __fadd_rn(s, __fmul_rn(bf16lo(x[i]), af[2 * i]));
-          s = __fadd_rn(s, __fmul_rn(bf16hi(x[i]), af[2 * i + 1]));
-        }
-        acc[m] = __fadd_rn(acc[m], s);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    float v = acc[m];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = __fadd_rn(v, __shfl_xor(v, o, 64));
-    if (lane == 0) s_part[wave][m] = v;
-  }
-  __syncthreads();
-  if (tid < M) {
-    const float v = __fadd_rn(__fadd_rn(s_part[0][tid], s_part[1][tid]),
-                              __fadd_rn(s_part[2][tid], s_part[3][tid]));
-    T[(int64_t)tid * r + j] = v;
-  }
-}
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
 
-constexpr int GEMV_ROWS = 16;
-
-__global__ __launch_bounds__(256) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X, int M,
-                                                   const float* __restrict__ T,
-                                                   const uint16_t* __restrict__ B, int r,
-                                                   float scale, void* __restrict__ Y, int y_bf16,
-                                                   Codebook cb) {
-  __shared__ float sq[16];
-  __shared__ f32x4_t s_acc[4][64];
-  if (threadIdx.x < 16) sq[threadIdx.x] = cb.q[threadIdx.x];
-  __syncthreads();
+__global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_t* __restrict__ X,
+                                                                   int M, int64_t K,
+                                                                   const uint16_t* __restrict__ A,
+                                                                   int r, float* __restrict__ T) {
+  __shared__ f32x4_t s_acc[kWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = lane & 15, kq = lane >> 4;
-  const int64_t K = W.K, N = W.N;
-  const int64_t n = (int64_t)blockIdx.x * GEMV_ROWS + row;
-  const bool row_ok = n < N;
-  const int64_t nsteps = K / kBlock;
-  const float mu = *W.mu;
-  const uint8_t* crow = W.codes + (row_ok ? n : 0) * (K / 2);
-  const uint16_t* xrow = X + (int64_t)(row < M ? row : 0) * K;
-  const bool x_ok = row < M;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int j0 = 16 * blockIdx.x;
+  // A operand: X rows (tokens), B operand: rows of A (rank index); rows past
+  // M or r read as zero
+  const rsrc_t rx = make_rsrc(X, (int64_t)M * K * 2);
+  const rsrc_t ra = make_rsrc(A + (int64_t)j0 * K, (int64_t)(r - j0) * K * 2);
+  const uint32_t vx = (uint32_t)((lr * K + 8 * kq) * 2);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t st = wave; st < nsteps; st += 4) {
-    u32x2_t cw = {0x77777777u, 0x77777777u};
-    float cp = 0.0f;
-    if (row_ok) {
-      cw = *reinterpret_cast<const u32x2_t*>(crow + st * 32 + kq * 8);
-      const int64_t b = n * nsteps + st;
-      cp = decode_constant(W.e[b], W.s[b / kDqBlock], mu);
+  // 32-wide steps st = wave, wave + 8, ...: lane slot kq holds k = 32st + 8kq..
+  const int64_t nst = K / 32;
+  for (int64_t st0 = wave; st0 < nst; st0 += 8 * 4) {
+    u32x4_t xa[4], ab[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t st = st0 + 8 * u;
+      const uint32_t off = st < nst ? (uint32_t)(st * 64) : 0x7fffffffu;  // past the end: zero
+      xa[u] = buf_load16(rx, vx, off);
+      ab[u] = buf_load16(ra, vx, off);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t w = cw[ks];
-      u32x4_t bfrag;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float a = __fmul_rn(sq[(w >> (8 * p)) & 15u], cp);
-        const float c = __fmul_rn(sq[(w >> (8 * p + 4)) & 15u], cp);
-        bfrag[p] = pack_bf16x2(a, c);
-      }
-      u32x4_t afrag = {0u, 0u, 0u, 0u};
-      if (x_ok) afrag = *reinterpret_cast<const u32x4_t*>(xrow + st * kBlock + kq * 16 + ks * 8);
-      acc = mfma_16x16x32(afrag, bfrag, acc);
-    }
+    for (int u = 0; u < 4; ++u) acc = mfma_16x16x32(xa[u], ab[u], acc);
   }
   s_acc[wave][lane] = acc;
   __syncthreads();
   if (wave == 0) {
-    const f32x4_t a0 = s_acc[0][lane], a1 = s_acc[1][lane], a2 = s_acc[2][lane],
-                  a3 = s_acc[3][lane];
-    // lane holds D rows (tokens) 4*(lane/16)+v of column (weight row) lane%16
-    const int64_t nn = (int64_t)blockIdx.x * GEMV_ROWS + (lane & 15);
+    // lane holds D rows (tokens) 4*(lane/16)+v of column (rank index) lane%16
+    f32x4_t t = s_acc[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4_t a = s_acc[w][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] = __fadd_rn(t[v], a[v]);
+    }
+    const int j = j0 + (lane & 15);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * (lane >> 4) + v;
-      if (m < M && nn < N) {
-        float y = __fadd_rn(__fadd_rn(a0[v], a1[v]), __fadd_rn(a2[v], a3[v]));
-        float l = 0.0f;
-        for (int j = 0; j < r; ++j)
-          l = __fadd_rn(l, __fmul_rn(T[(int64_t)m * r + j], bf16_to_f32(B[nn * r + j])));
-        y = __fadd_rn(y, __fmul_rn(scale, l));
-        if (y_bf16)
-          static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
-        else
-          static_cast<float*>(Y)[(int64_t)m * N + nn] = y;
-      }
+      if (m < M && j < r) T[(int64_t)m * r + j] = t[v];
+    }
+  }
+}
+
+constexpr int GEMV_ROWS = 16;
+constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
+
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
+                                                            int M, const float* __restrict__ T,
+                                                            const uint16_t* __restrict__ B, int r,
+                                                            float scale, void* __restrict__ Y,
+                                                            int y_bf16, Codebook cb) {
+  __shared__ float sq[16];
+  __shared__ f32x4_t s_acc[kGemvWaves][64];
+  // the LoRA epilogue's operands: T (M x r fp32) and the 16 rows of B (bf16)
+  __shared__ float sT[16 * 256];
+  __shared__ uint16_t sB[16 * 256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int64_t K = W.K, N = W.N;
+  const int64_t n0 = (int64_t)blockIdx.x * GEMV_ROWS;
+  const int64_t nb = K / kBlock;         // blocks per row
+  const int64_t ngroups = (nb + 3) / 4;  // block groups per row
+  const uint32_t kpr = (uint32_t)nb;
+  const float mu = *W.mu;
+  // rows past N and blocks past the row read as zero (code 0 with c' = 0
+  // would give 0; their products only reach unstored outputs or are zero)
+  const rsrc_t rc = make_rsrc(W.codes + n0 * (K / 2), (N - n0) * (K / 2));
+  const rsrc_t re = make_rsrc(W.e + n0 * kpr, (N - n0) * kpr);
+  const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
+  const rsrc_t rx = make_rsrc(X, (int64_t)M * K * 2);
+  const bool x_row = lr < M;
+
+  struct Group {
+    u32x4_t c[2];  // the lane's 64 codes
+    uint32_t e;    // e4m3 byte
+    float s;       // group scale
+    u32x4_t x[8];  // X fragments of the 8 MFMAs (zero if lr >= M)
+  };
+  auto load = [&](Group& g, int64_t grp) __attribute__((always_inline)) {
+    const int64_t b = 4 * grp + kq;  // this lane's block in its row
+    const bool ok = grp < ngroups && b < nb;
+    const uint32_t cb_off = ok ? (uint32_t)(lr * (K / 2) + b * 32) : 0x7fffffffu;
+    g.c[0] = buf_load16(rc, cb_off, 0u);
+    g.c[1] = buf_load16(rc, cb_off, 16u);
+    const uint32_t blk = (uint32_t)(lr * kpr + b);
+    g.e = buf_load1(re, ok ? blk : 0x7fffffffu, 0u);
+    g.s = __uint_as_float(buf_load4(rs, ok ? (((uint32_t)n0 * kpr + blk) / kDqBlock) * 4u : 0x7fffffffu, 0u));
+    // only the M token rows load X (the other lanes' A rows are zero)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) g.x[t] = u32x4_t{0u, 0u, 0u, 0u};
+    if (x_row) {
+      const uint32_t xo = ok ? (uint32_t)((lr * K + b * kBlock) * 2) : 0x7fffffffu;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) g.x[t] = buf_load16(rx, xo, 16u * t);
+    }
+  };
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](const Group& g) __attribute__((always_inline)) {
+    const float cp = decode_constant(g.e, g.s, mu);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t w = g.c[t >> 2][t & 3];  // codes 8t .. 8t+7
+      u32x4_t bfrag;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        bfrag[p] = pack_bf16x2(__fmul_rn(sq[(w >> (8 * p)) & 15u], cp),
+                               __fmul_rn(sq[(w >> (8 * p + 4)) & 15u], cp));
+      acc = mfma_16x16x32(g.x[t], bfrag, acc);
+    }
+  };
+
+  // Everything this workgroup reads from memory is requested up front: the
+  // first block group of every wave, then T and the B rows (used only by the
+  // epilogue, stored to LDS after the main loop).
+  Group ga, gb;
+  load(ga, wave);
+  const rsrc_t rt = make_rsrc(T, (int64_t)M * r * 4);
+  const rsrc_t rb = make_rsrc(B + n0 * r, (N - n0) * r * 2);
+  float tv[4];  // M*r and 16*r are at most 4096 = 4 per thread
+  uint32_t bv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + u * kGemvThreads;
+    tv[u] = __uint_as_float(buf_load4(rt, i < M * r ? 4u * i : 0x7fffffffu, 0u));
+    bv[u] = buf_load2(rb, i < GEMV_ROWS * r ? 2u * i : 0x7fffffffu, 0u);
+  }
+  if (tid < 16) sq[tid] = cb.q[tid];
+  __syncthreads();  // codebook
+
+  // two groups per iteration, alternating buffers: the loads of the next
+  // group are issued (and kept above the barrier to the scheduler) before
+  // the current group is consumed, and no loaded register is copied
+  for (int64_t grp = wave; grp < ngroups; grp += 2 * kGemvWaves) {
+    load(gb, grp + kGemvWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(ga);
+    if (grp + kGemvWaves >= ngroups) break;
+    load(ga, grp + 2 * kGemvWaves);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(gb);
+  }
+
+  s_acc[wave][lane] = acc;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = tid + u * kGemvThreads;
+    if (i < M * r) sT[i] = tv[u];
+    if (i < GEMV_ROWS * r) sB[i] = (uint16_t)bv[u];
+  }
+  __syncthreads();
+  // one thread per output (token m, weight row n0 + c): the 16 partial tiles
+  // in a fixed order, then s·Σ_j T[m][j]·B[n][j]
+  if (tid < 16 * GEMV_ROWS) {
+    const int m = tid >> 4, c = tid & 15;
+    const int64_t nn = n0 + c;
+    if (m < M && nn < N) {
+      // partial tile of wave w: lane 16(m/4) + c holds token m in component m%4
+      float y = s_acc[0][16 * (m >> 2) + c][m & 3];
+#pragma unroll
+      for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
+      float l = 0.0f;
+      for (int j = 0; j < r; ++j) l = __fadd_rn(l, __fmul_rn(sT[m * r + j], bf16_to_f32(sB[c * r + j])));
+      y = __fadd_rn(y, __fmul_rn(scale, l));
+      if (y_bf16)
+        static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+      else
+        static_cast<float*>(Y)[(int64_t)m * N + nn] = y;
     }
   }
 }
@@ -141,13 +212,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(Nf4View W, const uint16_t* __
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
                        const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
                        hipStream_t st) {
-  lora_down_small_kernel<<<(unsigned)r, 256, 0, st>>>(X, (int)M, W.K, A, r, T);
+  lora_down_small_kernel<<<(unsigned)((r + 15) / 16), kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
   const unsigned grid = (unsigned)((W.N + GEMV_ROWS - 1) / GEMV_ROWS);
-  {
-    TimedLaunch tl(kKernGemv, st);
-    gemv_kernel<<<grid, 256, 0, st>>>(W, X, (int)M, T, B, r, scale, Y, y_bf16 ? 1 : 0, codebook());
-  }
-  return hipGetLastError();
+  return timed_launch(kKernGemv, gemv_kernel, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
+                      (const float*)T, B, r, scale, Y, y_bf16 ? 1 : 0, codebook());
 }
 
 }  // namespace qnf4

@@ -3,6 +3,7 @@
 // return the status of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,24 +21,21 @@ struct TimingHook {
 };
 TimingHook& timing_hook();
 
-// Brackets one launch with the pending events if `kernel` was requested.
-struct TimedLaunch {
-  bool on;
-  hipEvent_t stop;
-  hipStream_t st;
-  TimedLaunch(int kernel, hipStream_t s) : on(false), stop(nullptr), st(s) {
-    TimingHook& h = timing_hook();
-    if (h.kernel == kernel) {
-      on = true;
-      stop = h.stop;
-      h.kernel = 0;
-      (void)hipEventRecord(h.start, st);
-    }
+// Launches kernel `k`.  If the calling thread asked to time the next launch
+// of `kernel_id`, the launch carries the caller's start/stop events, which
+// the runtime records around the dispatch itself (tighter than recording the
+// events on the stream before and after), and the request is cleared.
+template <typename F, typename... Args>
+hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  TimingHook& h = timing_hook();
+  if (h.kernel == kernel_id) {
+    h.kernel = 0;
+    hipExtLaunchKernelGGL(k, grid, block, 0, st, h.start, h.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(k, grid, block, 0, st, args...);
   }
-  ~TimedLaunch() {
-    if (on) (void)hipEventRecord(stop, st);
-  }
-};
+  return hipGetLastError();
+}
 enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4 };
 
 // Round `x` up to a multiple of `a`.

@@ -249,14 +249,13 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uin
                     reinterpret_cast<double*>(ws + L.off_lvl_b)};
   const Codebook& cb = codebook();
   {
-    TimedLaunch tl(kKernQuantize, st);
-    if (w_bf16) {
-      nf4_quantize_kernel<uint16_t><<<(unsigned)L.chunks, 256, 0, st>>>(
-          static_cast<const uint16_t*>(W), L.nb, codes, absmax, partial, cb);
-    } else {
-      nf4_quantize_kernel<float><<<(unsigned)L.chunks, 256, 0, st>>>(
-          static_cast<const float*>(W), L.nb, codes, absmax, partial, cb);
-    }
+    hipError_t e = w_bf16 ? timed_launch(kKernQuantize, nf4_quantize_kernel<uint16_t>, dim3((unsigned)L.chunks),
+                                         dim3(256), st, static_cast<const uint16_t*>(W), L.nb, codes,
+                                         absmax, partial, cb)
+                          : timed_launch(kKernQuantize, nf4_quantize_kernel<float>, dim3((unsigned)L.chunks),
+                                         dim3(256), st, static_cast<const float*>(W), L.nb, codes, absmax,
+                                         partial, cb);
+    if (e != hipSuccess) return e;
   }
   const double* in = partial;
   int64_t n_in = L.chunks;
