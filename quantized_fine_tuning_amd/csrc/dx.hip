@@ -25,10 +25,14 @@
 //   * dY and the weight data of the next steps are loaded into registers at
 //     the top of an iteration and stored to LDS at its end; the MFMAs of
 //     step s are interleaved in issue order with the dequantization of step
-//     s+1 into the other Ŵᵀ buffer.  Rows past N get an all-zero table.
+//     s+1 into the other Ŵᵀ buffer, in the first half of the step for one
+//     wave of each SIMD and in the second half for the other.  Rows past N
+//     get an all-zero table.
 //   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
 //     AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A), both
 //     copied straight into LDS.
+#include <type_traits>
+
 #include "host.h"
 #include "tiling.h"
 
@@ -214,13 +218,17 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 #pragma unroll
     for (int g = 0; g < 16; ++g) mfma_group(ya, wb, g);
   };
-  auto mfma_step_dequant = [&](const char* ya, const char* wb, int t, char* dst)
+  // The two waves of a SIMD (w and w + 4, i.e. wm = 0 and 1) dequantize in
+  // different halves of the step (phase P = wm): while one issues table
+  // arithmetic and lookups, the other issues MFMAs.
+  auto mfma_step_dequant = [&](auto P, const char* ya, const char* wb, int t, char* dst)
       __attribute__((always_inline)) {
+    constexpr int g0 = decltype(P)::value ? 8 : 0;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       mfma_group(ya, wb, g);
-      if (g == 0) build_table(t);
-      if (g == 4 || g == 10) dequant_cols(dst, (g - 4) / 6);
+      if (g == g0) build_table(t);
+      if (g == g0 + 1 || g == g0 + 3) dequant_cols(dst, (g - g0 - 1) / 2);
     }
   };
 
@@ -251,16 +259,23 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // loaded data (the weight buffers are wave-private and were last read
   // earlier in this iteration).  Weight data of step nsteps may be loaded:
   // its reads stay inside the buffers or return zeros, and it is not used.
-  for (int s = 0; s + 1 < nsteps; ++s) {
-    YRegs yr;
-    WRegs wr;
-    load_y(yr, s + 1);
-    load_w(wr, s + 2);
-    mfma_step_dequant(sa[s & 1], sw[s & 1], s + 1, sw[(s + 1) & 1]);
-    store_y(sa[(s + 1) & 1], yr);
-    store_w(wr);
-    __syncthreads();
-  }
+  // The loop is instantiated once per phase.
+  auto main_loop = [&](auto P) __attribute__((always_inline)) {
+    for (int s = 0; s + 1 < nsteps; ++s) {
+      YRegs yr;
+      WRegs wr;
+      load_y(yr, s + 1);
+      load_w(wr, s + 2);
+      mfma_step_dequant(P, sa[s & 1], sw[s & 1], s + 1, sw[(s + 1) & 1]);
+      store_y(sa[(s + 1) & 1], yr);
+      store_w(wr);
+      __syncthreads();
+    }
+  };
+  if (wm == 0)
+    main_loop(std::integral_constant<int, 0>());
+  else
+    main_loop(std::integral_constant<int, 1>());
   // last reduction step, copying LoRA step 0 (sU and AT2 tiles) into the
   // other buffers; then the LoRA steps, unrolled
   copy_su(sa[nsteps & 1], 0);

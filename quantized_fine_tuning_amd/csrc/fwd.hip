@@ -24,7 +24,9 @@
 //     next steps are loaded into registers at the top of an iteration and
 //     stored to LDS at its end, so no loaded register lives across
 //     iterations; the MFMAs of step s are interleaved in issue order with
-//     the dequantization of step s+1 into the other Ŵ buffer.
+//     the dequantization of step s+1 into the other Ŵ buffer, in the first
+//     half of the step for one wave of each SIMD and in the second half for
+//     the other.
 //   * All operand reads are buffer loads whose resources end at the tensor's
 //     last row, so ragged tiles read zeros without per-lane branches.
 //   * The LoRA up-projection is 2*Rp/64 extra reduction steps whose A operand
@@ -33,6 +35,8 @@
 //   * Workgroups are mapped to tiles so that each XCD (workgroup id mod 8)
 //     walks a contiguous run of a grouped tile order (4 M-tiles per group):
 //     the ~32 workgroups resident on one XCD share X and code rows in its L2.
+#include <type_traits>
+
 #include "host.h"
 #include "tiling.h"
 
@@ -208,13 +212,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // The MFMAs of one step interleaved with the dequantization of step t:
   // table build next to the first groups, one row group of lookups every
   // three MFMA groups.
-  auto mfma_step_dequant = [&](const char* xa, const char* wb, int t, int slot, char* dst)
+  // The two waves of a SIMD (w and w + 4, i.e. wm = 0 and 1) dequantize in
+  // different halves of the step (phase P = wm): while one issues table
+  // arithmetic and lookups, the other issues MFMAs.  Both instances keep the
+  // same barrier sequence.
+  auto mfma_step_dequant = [&](auto P, const char* xa, const char* wb, int t, int slot, char* dst)
       __attribute__((always_inline)) {
-    build_table(t, slot);
+    constexpr int g0 = decltype(P)::value ? 8 : 0;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       mfma_group(xa, wb, g);
-      if (g == 2 || g == 5 || g == 8 || g == 11) dequant_group(slot, dst, (g - 2) / 3);
+      if (g == g0) build_table(t, slot);
+      if (g > g0 && g <= g0 + 4) dequant_group(slot, dst, g - g0 - 1);
     }
   };
 
@@ -243,17 +252,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // in the previous iteration).  (Weight data of step ksteps may be loaded:
   // its reads stay inside the buffers or return zeros, and it is not used.)
   // One step per iteration and no other loop carrying the accumulators:
-  // anything else makes the register allocator shuffle or spill them.
-  for (int s = 0; s + 1 < ksteps; ++s) {
-    XRegs xr;
-    WRegs wr;
-    load_x(xr, s + 1);
-    load_w(wr, s + 2);
-    mfma_step_dequant(sx[s & 1], sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
-    store_x(sx[(s + 1) & 1], xr);
-    store_w(s & 1, wr);
-    __syncthreads();
-  }
+  // anything else makes the register allocator shuffle or spill them.  The
+  // loop is instantiated once per phase.
+  auto main_loop = [&](auto P) __attribute__((always_inline)) {
+    for (int s = 0; s + 1 < ksteps; ++s) {
+      XRegs xr;
+      WRegs wr;
+      load_x(xr, s + 1);
+      load_w(wr, s + 2);
+      mfma_step_dequant(P, sx[s & 1], sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
+      store_x(sx[(s + 1) & 1], xr);
+      store_w(s & 1, wr);
+      __syncthreads();
+    }
+  };
+  if (wm == 0)
+    main_loop(std::integral_constant<int, 0>());
+  else
+    main_loop(std::integral_constant<int, 1>());
   // Last weight step, copying LoRA step 0 (sT and B2 tiles) into the other
   // buffers; then the LoRA steps, unrolled.
   copy_lora(rt, sx[ksteps & 1], 0);
