@@ -154,6 +154,14 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ uint16_t lds_read_u16(uint32_t a) {
   return *(const lds_u16_t*)(uintptr_t)a;
 }
+// Returns x unchanged, but hides where it came from: values derived from it
+// are computed where they are used instead of being hoisted out of a loop,
+// where each would hold a register for the whole loop.
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // 2 * (4-bit code at bit `pos` of w), as a byte offset into a bf16 table.
 __device__ __forceinline__ uint32_t code_x2(uint32_t w, int pos) {
   return pos == 0 ? ((w << 1) & 0x1Eu) : ((w >> (pos - 1)) & 0x1Eu);

@@ -71,10 +71,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   __shared__ __attribute__((aligned(256))) char slut[kWaves][64 * 32];
   __shared__ __attribute__((aligned(16))) char scode[kWaves][64 * 16];
   __shared__ __attribute__((aligned(16))) uint32_t sconst[kWaves][2][64];
-  __shared__ float sq[16];
   int tmi, tki;
   if (!tile_of(blockIdx.x, tiles_m, tiles_k, tmi, tki)) return;
-  if (threadIdx.x < 16) sq[threadIdx.x] = cb.q[threadIdx.x];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
@@ -145,51 +143,82 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     r.e = buf_load1(re, blk, 0u);
     r.s = buf_load4(rs, (blk / kDqBlock) * 4u, 0u);
   };
+  // The code bytes go to LDS transposed for the lanes that dequantize them:
+  // the 2 bytes of column pair cg of row 8rg + i sit at byte 2i of 16-byte
+  // slot 8rg + (cg ^ rg), so that lane (rg, cg) later reads its 8 rows'
+  // codes with one 16-byte read.  Slot XOR: the writes of one pair index go
+  // to 8 distinct slots of each 128-byte line, the reads of 8 consecutive
+  // lanes to 8 distinct slots.
+  const uint32_t code_wbase = (uint32_t)((lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7));
   auto store_w = [&](const WRegs& r) __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4_t*>(scode[wave] + 16 * lane) = r.c;
+    const uint32_t wb = opaque(code_wbase);
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc)
+      *reinterpret_cast<uint16_t*>(scode[wave] + (wb ^ (uint32_t)(pc << 4))) =
+          (uint16_t)(r.c[pc >> 1] >> (16 * (pc & 1)));
     sconst[wave][0][lane] = r.e;
     sconst[wave][1][lane] = r.s;
   };
 
   // Dequantization of step t (weight data in the wave's buffers) into dst.
-  char* lut = slut[wave];
-  const uint32_t lut_addr = lds_offset(lut);
-  // table of row t (= lane) at slot 8(t & 7) + ((t ^ (t >> 3)) & 7): row 8rg + i
-  // sits at slot 8i + (i ^ rg), byte offset 256i + 32(i ^ rg)
-  const int my_slot = 8 * (lane & 7) + ((lane ^ (lane >> 3)) & 7);
+  // The table of weight row 8rg + i sits at byte 256i + 32rg of the wave's
+  // table area, so a lookup is (base of rg | 2*code) plus the constant 256i.
+  // Lane t builds the table of row 8rg + i with rg = t0 + 2t1 + 4t3 and
+  // i = t4 + 2t5 + 4t2 (t_b = bit b of t) and writes half t2 of it first:
+  // the 8 lanes of each 16-byte write then cover a 128-byte line.
+  const uint32_t lut_addr = lds_offset(slut[wave]);
+  const uint32_t lut_rg = lut_addr + 32u * (uint32_t)rg;
+  const int tb_rg = (lane & 3) | ((lane >> 1) & 4), tb_i = ((lane >> 4) & 3) | (lane & 4);
+  const int tb_row = 8 * tb_rg + tb_i;
+  const int tb_first = (lane >> 2) & 1;
+  char* const tb_dst = slut[wave] + 256 * tb_i + 32 * tb_rg + 16 * tb_first;
   auto build_table = [&](int t) __attribute__((always_inline)) {
-    const bool row_ok = wave_cols_ok && ((int64_t)t * NSTEP + lane < N);
-    const float cp = decode_constant(sconst[wave][0][lane], __uint_as_float(sconst[wave][1][lane]), mu);
+    const bool row_ok = wave_cols_ok && ((int64_t)t * NSTEP + tb_row < N);
+    const float cp = decode_constant(sconst[wave][0][tb_row], __uint_as_float(sconst[wave][1][tb_row]), mu);
     u32x4_t t0, t1;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      t0[p] = row_ok ? pack_bf16x2(__fmul_rn(sq[2 * p], cp), __fmul_rn(sq[2 * p + 1], cp)) : 0u;
-      t1[p] = row_ok ? pack_bf16x2(__fmul_rn(sq[8 + 2 * p], cp), __fmul_rn(sq[9 + 2 * p], cp)) : 0u;
+      t0[p] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[2 * p], cp), __fmul_rn(cb.q[2 * p + 1], cp)) : 0u;
+      t1[p] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[8 + 2 * p], cp), __fmul_rn(cb.q[9 + 2 * p], cp)) : 0u;
     }
-    *reinterpret_cast<u32x4_t*>(lut + my_slot * 32) = t0;
-    *reinterpret_cast<u32x4_t*>(lut + my_slot * 32 + 16) = t1;
+    char* const d = opaque(tb_dst);
+    *reinterpret_cast<u32x4_t*>(d) = tb_first ? t1 : t0;
+    *reinterpret_cast<u32x4_t*>((char*)((uintptr_t)d ^ 16u)) = tb_first ? t0 : t1;
+  };
+  // The codes of rows 8rg..8rg+7, columns 4cg..4cg+3: row 2p in the low
+  // half of dword p, row 2p + 1 in its high half.
+  const int code_rslot = 8 * rg + (cg ^ rg);
+  auto read_codes = [&]() __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4_t*>(scode[wave] + 16 * code_rslot);
   };
   // Column pair cp2 (columns 4cg + 2cp2, +1) of rows 8rg..8rg+7: 16
   // lookups, two 16-byte stores of 8 rows each.
-  auto dequant_cols = [&](char* dst, int cp2) __attribute__((always_inline)) {
-    uint32_t w2[8];
+  // Store address of column 4cg + c of the wave's slice, rows 8rg..8rg+7:
+  // wswz(32w + 4cg + c, rg) = (st0 ^ 16c) + 128c.
+  const uint32_t st0 = (uint32_t)((32 * wave + 4 * cg) * 128 + ((rg ^ cg ^ (4 * (cg & 1))) << 4));
+  auto dequant_cols = [&](char* dst, int cp2, const u32x4_t& cw) __attribute__((always_inline)) {
+    const uint32_t lb = opaque(lut_rg);
+    uint16_t v[2][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w2[i] = *reinterpret_cast<const uint16_t*>(scode[wave] + (8 * rg + i) * 16 + 2 * cg);
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int c = 2 * cp2 + cc;
+        v[cc][2 * p] = lds_read_u16((lb | code_x2(cw[p], 4 * c)) + 256u * (2 * p));
+        v[cc][2 * p + 1] = lds_read_u16((lb | code_x2(cw[p], 16 + 4 * c)) + 256u * (2 * p + 1));
+      }
+    // all 16 lookups are issued before the first result is used (one wait
+    // instead of a chain of them); MFMAs, scalar and global-memory
+    // instructions may still move across
+    __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+    const uint32_t sb = opaque(st0);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const int c = 2 * cp2 + cc;
       u32x4_t o;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        u16x2_t v;
-        v.x = lds_read_u16((lut_addr + 256u * (2 * p) + 32u * (uint32_t)((2 * p) ^ rg)) |
-                           code_x2(w2[2 * p], 4 * c));
-        v.y = lds_read_u16((lut_addr + 256u * (2 * p + 1) + 32u * (uint32_t)((2 * p + 1) ^ rg)) |
-                           code_x2(w2[2 * p + 1], 4 * c));
-        o[p] = __builtin_bit_cast(uint32_t, v);
-      }
-      *reinterpret_cast<u32x4_t*>(dst + wswz(32 * wave + 4 * cg + c, rg)) = o;
+      for (int p = 0; p < 4; ++p) o[p] = (uint32_t)v[cc][2 * p] | ((uint32_t)v[cc][2 * p + 1] << 16);
+      *reinterpret_cast<u32x4_t*>(dst + ((sb ^ (uint32_t)(16 * c)) + 128u * c)) = o;
     }
   };
 
@@ -201,16 +230,22 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 
   // MFMA group g (0..15): n-half ks = g / 8, token block i = g % 8; the B
   // fragments of the half are read at its first group.
-  const int arow = 128 * wm + lr, brow = 64 * wk + lr;
+  // Fragment addresses: xswz(128wm + lr + 16i, 2kq + ks) = (a0 ^ 16ks) + 2048i
+  // and wswz(64wk + lr + 16j, 2kq + ks) = (b0 ^ 16(ks + 4(j & 1))) + 2048j.
+  const uint32_t a0 = (uint32_t)((128 * wm + lr) * 128 + (((2 * kq) ^ (lr & 7)) << 4));
+  const uint32_t b0 = (uint32_t)((64 * wk + lr) * 128 + (((2 * kq) ^ ((lr ^ (lr >> 2)) & 7)) << 4));
   u32x4_t bfr[4];
+  uint32_t abase = 0;
   auto mfma_group = [&](const char* ya, const char* wb, int g) __attribute__((always_inline)) {
     const int ks = g >> 3, i = g & 7;
     if (i == 0) {
+      const uint32_t bb = opaque(b0);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + wswz(brow + 16 * j, 2 * kq + ks));
+        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + ((bb ^ (uint32_t)(16 * (ks + 4 * (j & 1)))) + 2048u * j));
+      abase = opaque(a0) ^ (uint32_t)(16 * ks);
     }
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ya + xswz(arow + 16 * i, 2 * kq + ks));
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ya + abase + 2048u * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
   };
@@ -224,11 +259,15 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   auto mfma_step_dequant = [&](auto P, const char* ya, const char* wb, int t, char* dst)
       __attribute__((always_inline)) {
     constexpr int g0 = decltype(P)::value ? 8 : 0;
+    u32x4_t cw;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       mfma_group(ya, wb, g);
-      if (g == g0) build_table(t);
-      if (g == g0 + 1 || g == g0 + 3) dequant_cols(dst, (g - g0 - 1) / 2);
+      if (g == g0) {
+        build_table(t);
+        cw = read_codes();
+      }
+      if (g == g0 + 1 || g == g0 + 3) dequant_cols(dst, (g - g0 - 1) / 2, cw);
     }
   };
 
@@ -242,10 +281,13 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     store_y(sa[0], yr);
     store_w(w0);
   }
-  __syncthreads();  // codebook, dY of step 0
+  __syncthreads();  // dY and weight data of step 0
   build_table(0);
+  {
+    const u32x4_t cw = read_codes();
 #pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2) dequant_cols(sw[0], c2);
+    for (int c2 = 0; c2 < 2; ++c2) dequant_cols(sw[0], c2, cw);
+  }
   {
     WRegs w1;
     load_w(w1, 1);
