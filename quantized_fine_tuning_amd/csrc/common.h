@@ -207,13 +207,12 @@ __device__ __forceinline__ void dma_lds4(i32x4_t r, const void* lds, uint32_t vo
 // (including copies into LDS, which the compiler does not track).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Waits until at most N vector-memory loads of this wave are outstanding
-// (loads complete in issue order, so the older ones are done).  N < 16.
-// Written as assembly with a memory clobber, so that no LDS read of copied
-// data is moved above it.
+// (loads complete in issue order, so the older ones are done).  N < 64.
+// Callers that read LDS filled by copies put a compiler barrier after it.
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

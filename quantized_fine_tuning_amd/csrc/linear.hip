@@ -1,0 +1,145 @@
+// Host orchestration of the QLoRA linear layer (forward and backward): the
+// order of the kernels, the workspace layout and the reduction slices.
+//
+// Forward (P1 §七 dataflow figure):  T = X·Aᵀ, Y = X·Ŵᵀ + s·T·Bᵀ.
+// Backward (P1 简化版, P2 §4.4): U = dY·B, dX = dY·Ŵ + s·U·A,
+// dA = s·Uᵀ·X, dB = s·dYᵀ·T; no gradient for the frozen weight.
+// The low-rank factors T and U enter the big products as bf16 hi/lo splits
+// of s·T and s·U (about 16 significant bits); dA and dB use the same splits.
+#include <algorithm>
+
+#include "host.h"
+
+namespace qnf4 {
+
+hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
+                          const uint16_t* A, int32_t r, int64_t Rp, uint16_t* AT2, void* dX,
+                          bool dx_bf16, hipStream_t st);
+hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
+                           const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
+                           bool y_bf16, hipStream_t st);
+hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
+                       const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
+                       hipStream_t st);
+
+namespace {
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  FwdLayout L{};
+  const int64_t Rp = lora_rp(r);
+  size_t off = 0;
+  L.off_T = off;
+  off += round_up(M * r * 4, 256);
+  L.off_sT = off;
+  off += round_up(M * 2 * Rp * 2, 256);
+  L.off_B2 = off;
+  off += M > 16 ? round_up(N * 2 * Rp * 2, 256) : 0;
+  L.off_P = off;
+  if (M > 16) {
+    L.slT = lora_slices(K, cdiv64(M, 64) * cdiv64(Rp, 64));
+    off += round_up(L.slT.count * M * Rp * 4, 256);
+  }
+  L.total = off;
+  return L;
+}
+
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdLayout L{};
+  const int64_t Rp = lora_rp(r), Mp = lora_mp(M);
+  const int64_t rowtiles = cdiv64(M, 64) * cdiv64(Rp, 64);
+  L.slT = lora_slices(K, rowtiles);
+  L.slU = lora_slices(N, rowtiles);
+  L.slA = lora_slices(M, cdiv64(K, 128) * cdiv64(Rp, 64));
+  L.slB = lora_slices(M, cdiv64(N, 128) * cdiv64(Rp, 64));
+  size_t off = 0;
+  L.off_sT = off;
+  off += round_up(M * 2 * Rp * 2, 256);
+  L.off_sTT = off;
+  off += round_up(2 * Rp * Mp * 2, 256);
+  L.off_sU = off;
+  off += round_up(M * 2 * Rp * 2, 256);
+  L.off_sUT = off;
+  off += round_up(2 * Rp * Mp * 2, 256);
+  L.off_BT = off;
+  off += round_up(Rp * round_up(N, 64) * 2, 256);
+  L.off_AT2 = off;
+  off += round_up(K * 2 * Rp * 2, 256);
+  // one partial-sum area reused by the successive reductions
+  L.off_P = off;
+  size_t p = 0;
+  p = std::max<size_t>(p, round_up(L.slT.count * M * Rp * 4, 256));
+  p = std::max<size_t>(p, round_up(L.slU.count * M * Rp * 4, 256));
+  p = std::max<size_t>(p, round_up(L.slA.count * K * Rp * 4, 256));
+  p = std::max<size_t>(p, round_up(L.slB.count * N * Rp * 4, 256));
+  off += p;
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
+                          const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16,
+                          float* T, char* ws, const FwdLayout& L, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  if (M <= 16) {
+    float* Tw = T ? T : reinterpret_cast<float*>(ws + L.off_T);
+    return launch_gemv(W, X, M, A, B, r, scale, Y, y_bf16, Tw, st);
+  }
+  const int64_t Rp = lora_rp(r);
+  uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
+  float* P = reinterpret_cast<float*>(ws + L.off_P);
+  hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, Rp, L.slT, P, st);
+  if (e != hipSuccess) return e;
+  e = launch_lora_reduce(P, (int)L.slT.count, M, r, Rp, scale, T, sT, nullptr, st);
+  if (e != hipSuccess) return e;
+  uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
+  return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y_bf16, st);
+}
+
+hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                           const float* T_saved, void* dX, bool dx_bf16, float* dA, float* dB,
+                           char* ws, const BwdLayout& L, hipStream_t st) {
+  const int64_t Rp = lora_rp(r), Mp = lora_mp(M);
+  const int64_t N = W.N, K = W.K;
+  float* P = reinterpret_cast<float*>(ws + L.off_P);
+  hipError_t e;
+  if (M == 0) {  // no tokens: the adapter gradients are zero
+    e = launch_reduce_slices(P, 0, 0, r, K, 1, 1, dA, st);
+    if (e != hipSuccess) return e;
+    return launch_reduce_slices(P, 0, 0, N, r, 1, 1, dB, st);
+  }
+  uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
+  uint16_t* sTT = reinterpret_cast<uint16_t*>(ws + L.off_sTT);
+  uint16_t* sU = reinterpret_cast<uint16_t*>(ws + L.off_sU);
+  uint16_t* sUT = reinterpret_cast<uint16_t*>(ws + L.off_sUT);
+  uint16_t* BT = reinterpret_cast<uint16_t*>(ws + L.off_BT);
+  uint16_t* AT2 = reinterpret_cast<uint16_t*>(ws + L.off_AT2);
+  // s·T (hi/lo and transposed): from the saved T, or recomputed
+  if (T_saved) {
+    e = launch_split_saved(T_saved, M, r, Rp, scale, sT, sTT, st);
+  } else {
+    e = launch_rowred(X, M, K, K, A, r, K, Rp, L.slT, P, st);
+    if (e == hipSuccess) e = launch_lora_reduce(P, (int)L.slT.count, M, r, Rp, scale, nullptr, sT, sTT, st);
+  }
+  if (e != hipSuccess) return e;
+  // s·U, U = dY·B
+  e = launch_transpose_lora_b(B, N, r, Rp, BT, st);
+  if (e == hipSuccess) e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), Rp, L.slU, P, st);
+  if (e == hipSuccess) e = launch_lora_reduce(P, (int)L.slU.count, M, r, Rp, scale, nullptr, sU, sUT, st);
+  if (e != hipSuccess) return e;
+  // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
+  e = launch_dx_gemm(W, dY, M, sU, A, r, Rp, AT2, dX, dx_bf16, st);
+  if (e != hipSuccess) return e;
+  // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
+  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.slA, P, st);
+  if (e == hipSuccess) e = launch_reduce_slices(P, (int)L.slA.count, K * Rp, r, K, 1, Rp, dA, st);
+  if (e != hipSuccess) return e;
+  // dB[n][j] = Σ_m dY[m][n] · (sT_hi + sT_lo)[m][j]
+  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.slB, P, st);
+  if (e == hipSuccess) e = launch_reduce_slices(P, (int)L.slB.count, N * Rp, N, r, Rp, 1, dB, st);
+  return e;
+}
+
+}  // namespace qnf4
