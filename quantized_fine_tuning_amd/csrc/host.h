@@ -70,31 +70,39 @@ struct Nf4View {
 };
 
 // LoRA side products -------------------------------------------------------
-// A reduction of `red` elements split into `count` slices of `chunk`
-// elements (a multiple of 64), summed afterwards in slice order.
-struct LoraSlices {
-  int64_t chunk, count;
+// Stream-K split of a product (see lora.hip): `tiles` output tiles, ut
+// units per tile, U units in all over G workgroups; a tile collects at most
+// cmax partial sums.
+constexpr uint32_t kSkWorkgroups = 256;  // one per compute unit of an MI355X
+struct SkPlan {
+  int64_t tiles;
+  uint32_t ut, U, G;
+  int cmax, jt;
 };
-LoraSlices lora_slices(int64_t red, int64_t tiles);
+// T = X·Aᵀ, U = dY·B: reduction over Kred for M rows, 64x64 tiles
+SkPlan rowred_plan(int64_t M, int64_t Kred, int64_t Rp);
+// dA, dB: reduction over Mred for Pn columns, 128x64 tiles
+SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp);
+size_t rowred_partial_bytes(const SkPlan& p);
+size_t colred_partial_bytes(const SkPlan& p);
 // Columns of the transposed bf16 splits [2Rp, Mp]: M rounded up to 64.
 int64_t lora_mp(int64_t M);
-// P[z][m][j] = Σ_{k in slice z} L[m][k]·R[j][k], j < Rp (rows of R past
-// rrows read as zero).
+// Partial tiles of Σ_k L[m][k]·R[j][k] (rows of R past rrows read as zero).
 hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl, const uint16_t* R,
-                         int64_t rrows, int64_t ldr, int64_t Rp, const LoraSlices& sl, float* P,
-                         hipStream_t st);
-// P[z][p][j] = Σ_{m in slice z} L[m][p]·(S[j][m] + S[Rp + j][m]).
+                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, hipStream_t st);
+// Sums them → optional fp32 T [M, r], the hi/lo split of scale·T [M, 2Rp]
+// and optionally its transpose [2Rp, Mp].
+hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
+                                float scale, float* T, uint16_t* out, uint16_t* outT, hipStream_t st);
+// Partial tiles of Σ_m L[m][p]·(S[j][m] + S[Rp + j][m]).
 hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const LoraSlices& sl, float* P, hipStream_t st);
-// Slice sums of P [S, M, Rp] → optional fp32 T [M, r], the hi/lo split of
-// scale·T [M, 2Rp] and optionally its transpose [2Rp, Mp].
-hipError_t launch_lora_reduce(const float* P, int S, int64_t M, int32_t r, int64_t Rp, float scale,
-                              float* T, uint16_t* out, uint16_t* outT, hipStream_t st);
+                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, hipStream_t st);
+// Sums them → out [Pn, r], or out [r, Pn] when transposed.
+hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
+                                float* out, hipStream_t st);
 hipError_t launch_split_saved(const float* T, int64_t M, int32_t r, int64_t Rp, float scale,
                               uint16_t* sT, uint16_t* sTT, hipStream_t st);
-// out[a][b] = Σ_z P[z·zs + a·sa + b·sb], a < An, b < Bn.
-hipError_t launch_reduce_slices(const float* P, int S, int64_t zs, int64_t An, int64_t Bn, int64_t sa,
-                                int64_t sb, float* out, hipStream_t st);
+hipError_t launch_zero(float* a, int64_t n, hipStream_t st);
 // BT [Rp, round_up(N, 64)] = Bᵀ, zero-padded.
 hipError_t launch_transpose_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp, uint16_t* BT,
                                    hipStream_t st);
@@ -104,7 +112,7 @@ struct FwdLayout {
   // fp32 T [M, r] (if not saved by the caller), bf16 sT [M, 2Rp], bf16 B2
   // [N, 2Rp], fp32 partial sums of T over the reduction slices
   size_t off_T, off_sT, off_B2, off_P, total;
-  LoraSlices slT;
+  SkPlan pT;
 };
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
@@ -118,7 +126,7 @@ struct BwdLayout {
   // [Rp, round_up(N, 64)]; bf16 AT2 [K, 2Rp]; one fp32 partial-sum area
   // reused by the T, U, dA and dB reductions
   size_t off_sT, off_sTT, off_sU, off_sUT, off_BT, off_AT2, off_P, total;
-  LoraSlices slT, slU, slA, slB;
+  SkPlan pT, pU, pA, pB;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 

@@ -22,10 +22,6 @@ hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uin
                        const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
                        hipStream_t st);
 
-namespace {
-int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-}  // namespace
-
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdLayout L{};
   const int64_t Rp = lora_rp(r);
@@ -38,8 +34,8 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   off += M > 16 ? round_up(N * 2 * Rp * 2, 256) : 0;
   L.off_P = off;
   if (M > 16) {
-    L.slT = lora_slices(K, cdiv64(M, 64) * cdiv64(Rp, 64));
-    off += round_up(L.slT.count * M * Rp * 4, 256);
+    L.pT = rowred_plan(M, K, Rp);
+    off += round_up(rowred_partial_bytes(L.pT), 256);
   }
   L.total = off;
   return L;
@@ -48,11 +44,12 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdLayout L{};
   const int64_t Rp = lora_rp(r), Mp = lora_mp(M);
-  const int64_t rowtiles = cdiv64(M, 64) * cdiv64(Rp, 64);
-  L.slT = lora_slices(K, rowtiles);
-  L.slU = lora_slices(N, rowtiles);
-  L.slA = lora_slices(M, cdiv64(K, 128) * cdiv64(Rp, 64));
-  L.slB = lora_slices(M, cdiv64(N, 128) * cdiv64(Rp, 64));
+  if (M > 0) {
+    L.pT = rowred_plan(M, K, Rp);
+    L.pU = rowred_plan(M, N, Rp);
+    L.pA = colred_plan(M, K, Rp);
+    L.pB = colred_plan(M, N, Rp);
+  }
   size_t off = 0;
   L.off_sT = off;
   off += round_up(M * 2 * Rp * 2, 256);
@@ -69,10 +66,12 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   // one partial-sum area reused by the successive reductions
   L.off_P = off;
   size_t p = 0;
-  p = std::max<size_t>(p, round_up(L.slT.count * M * Rp * 4, 256));
-  p = std::max<size_t>(p, round_up(L.slU.count * M * Rp * 4, 256));
-  p = std::max<size_t>(p, round_up(L.slA.count * K * Rp * 4, 256));
-  p = std::max<size_t>(p, round_up(L.slB.count * N * Rp * 4, 256));
+  if (M > 0) {
+    p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pT), 256));
+    p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pU), 256));
+    p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pA), 256));
+    p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pB), 256));
+  }
   off += p;
   L.total = off;
   return L;
@@ -89,9 +88,9 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
   const int64_t Rp = lora_rp(r);
   uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
   float* P = reinterpret_cast<float*>(ws + L.off_P);
-  hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, Rp, L.slT, P, st);
+  hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, L.pT, P, st);
   if (e != hipSuccess) return e;
-  e = launch_lora_reduce(P, (int)L.slT.count, M, r, Rp, scale, T, sT, nullptr, st);
+  e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, st);
   if (e != hipSuccess) return e;
   uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
   return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y_bf16, st);
@@ -106,9 +105,9 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   float* P = reinterpret_cast<float*>(ws + L.off_P);
   hipError_t e;
   if (M == 0) {  // no tokens: the adapter gradients are zero
-    e = launch_reduce_slices(P, 0, 0, r, K, 1, 1, dA, st);
+    e = launch_zero(dA, (int64_t)r * K, st);
     if (e != hipSuccess) return e;
-    return launch_reduce_slices(P, 0, 0, N, r, 1, 1, dB, st);
+    return launch_zero(dB, N * r, st);
   }
   uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
   uint16_t* sTT = reinterpret_cast<uint16_t*>(ws + L.off_sTT);
@@ -120,25 +119,25 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   if (T_saved) {
     e = launch_split_saved(T_saved, M, r, Rp, scale, sT, sTT, st);
   } else {
-    e = launch_rowred(X, M, K, K, A, r, K, Rp, L.slT, P, st);
-    if (e == hipSuccess) e = launch_lora_reduce(P, (int)L.slT.count, M, r, Rp, scale, nullptr, sT, sTT, st);
+    e = launch_rowred(X, M, K, K, A, r, K, L.pT, P, st);
+    if (e == hipSuccess) e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, st);
   }
   if (e != hipSuccess) return e;
   // s·U, U = dY·B
   e = launch_transpose_lora_b(B, N, r, Rp, BT, st);
-  if (e == hipSuccess) e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), Rp, L.slU, P, st);
-  if (e == hipSuccess) e = launch_lora_reduce(P, (int)L.slU.count, M, r, Rp, scale, nullptr, sU, sUT, st);
+  if (e == hipSuccess) e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, st);
+  if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, st);
   if (e != hipSuccess) return e;
   // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
   e = launch_dx_gemm(W, dY, M, sU, A, r, Rp, AT2, dX, dx_bf16, st);
   if (e != hipSuccess) return e;
   // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
-  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.slA, P, st);
-  if (e == hipSuccess) e = launch_reduce_slices(P, (int)L.slA.count, K * Rp, r, K, 1, Rp, dA, st);
+  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, st);
+  if (e == hipSuccess) e = launch_colred_finish(P, L.pA, K, r, true, dA, st);
   if (e != hipSuccess) return e;
   // dB[n][j] = Σ_m dY[m][n] · (sT_hi + sT_lo)[m][j]
-  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.slB, P, st);
-  if (e == hipSuccess) e = launch_reduce_slices(P, (int)L.slB.count, N * Rp, N, r, Rp, 1, dB, st);
+  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.pB, P, st);
+  if (e == hipSuccess) e = launch_colred_finish(P, L.pB, N, r, false, dB, st);
   return e;
 }
 

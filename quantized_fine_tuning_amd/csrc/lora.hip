@@ -21,8 +21,9 @@
 // unrolled over them, so that the compiler can tell the copy into one stage
 // from the reads of another and needs no full wait before each read; each
 // wave waits for its own copies of a stage before the barrier that opens it.
-// Partial sums over the reduction slices are added in a fixed order by the
-// reduction kernels below, which also produce the bf16 hi/lo splits.
+// The work is split evenly over the workgroups (stream-K, below); partial
+// sums are added in a fixed order by the finishing kernels, which also
+// produce the bf16 hi/lo splits.
 #include <algorithm>
 
 #include "host.h"
@@ -61,59 +62,80 @@ __device__ __forceinline__ void split_hilo(float v, uint16_t& hi, uint16_t& lo) 
 }
 
 // ---------------------------------------------------------------------------
-// rowred: P[z][m][j0 + j] = Σ_{k in slice z} L[m][k] · R[j0 + j][k],  j < 64.
+// Work split (stream-K).  A product has `tiles` output tiles, each a
+// reduction of ns stages, cut into units of NSTAGE stages (ut per tile; the
+// stages of a last, partial unit past ns read zeros).  Workgroup g of G
+// takes units [gU/G, (g+1)U/G) of the U = tiles·ut units in tile order, so
+// every workgroup has the same amount of work whatever the number of tiles;
+// the copy ring runs on across tile boundaries.  At the end of each tile
+// it holds, a workgroup writes its partial sum into slot g - first(t) of
+// that tile; the reduction kernels add the slots of a tile in slot order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t sk_begin(uint32_t g, uint32_t U, uint32_t G) {
+  return (uint32_t)(((uint64_t)g * U) / G);
+}
+// the workgroup whose range holds unit u
+__device__ __host__ inline uint32_t sk_owner(uint32_t u, uint32_t U, uint32_t G) {
+  uint32_t g = (uint32_t)(((uint64_t)u * G) / U);
+  while (g + 1 < G && (uint32_t)(((uint64_t)(g + 1) * U) / G) <= u) ++g;
+  while (g > 0 && (uint32_t)(((uint64_t)g * U) / G) > u) --g;
+  return g;
+}
+
+// ---------------------------------------------------------------------------
+// rowred: tile (mb, jb) = Σ_k L[64mb + i][k] · R[64jb + j][k], i, j < 64.
 // L [M, Kred] (leading dimension ldl), R [rrows, Kred] (leading dimension
-// ldr); rows past M or rrows read as zero, and so do reduction columns past
-// Kred.  Workgroup: 64 rows of L by 64 rows of R, 4 waves of 32 x 32.
-// Grid (ceil(M/64), ceil(Rp/64), slices of `chunk`).  Output [S, M, Rp].
+// ldr); rows past M or rrows and columns past Kred read as zero.  Tile t =
+// mb·jt + jb; 4 waves of 32 x 32.  Partial tiles [tiles, cmax, 64, 64].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict__ L, int64_t M,
                                                      int64_t Kred, int64_t ldl,
                                                      const uint16_t* __restrict__ R, int64_t rrows,
-                                                     int64_t ldr, int64_t chunk, int64_t Rp,
-                                                     float* __restrict__ P) {
+                                                     int64_t ldr, int jt, uint32_t ut, uint32_t U,
+                                                     int cmax, float* __restrict__ P) {
   __shared__ __attribute__((aligned(1024))) char l0[64 * 128], l1[64 * 128], l2[64 * 128], l3[64 * 128];
   __shared__ __attribute__((aligned(1024))) char r0[64 * 128], r1[64 * 128], r2[64 * 128], r3[64 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
-  const int64_t kb = (int64_t)blockIdx.z * chunk;
-  const int64_t kext = std::min(chunk, Kred - kb);
-  const int nsteps = (int)((kext + ST - 1) / ST);
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  const uint32_t u0 = sk_begin(g, U, G), u1 = sk_begin(g + 1, U, G);
 
-  // Resources start at (first row, kb); rows past the tensor are outside.
-  const int64_t lbytes = ((M - m0) * ldl - kb) * 2, rbytes = ((rrows - j0) * ldr - kb) * 2;
-  const rsrc_t rl = make_rsrc(L + m0 * ldl + kb, lbytes);
-  const rsrc_t rr = make_rsrc(R + j0 * ldr + kb, rrows > j0 ? rbytes : 0);
   // Wave w copies rows 16w + 8c + (lane >> 3), c = 0, 1, of both tiles; lane
   // i fills physical chunk i & 7, i.e. logical chunk (i & 7) ^ (i >> 3).
   const int lch = (lane & 7) ^ (lane >> 3);
   const int crow = 16 * wave + (lane >> 3);
   const uint32_t vl = (uint32_t)((crow * ldl + 8 * lch) * 2), vr = (uint32_t)((crow * ldr + 8 * lch) * 2);
-  const uint32_t l_oob = (uint32_t)std::min<int64_t>(std::max<int64_t>(lbytes, 0), 0x7fffffff);
-  const uint32_t r_oob = (uint32_t)std::min<int64_t>(std::max<int64_t>(rbytes, 0), 0x7fffffff);
-
-  // Steps past the slice are issued too, with every lane outside the
-  // resource: they fill their stage with zeros, so that the pipeline has no
-  // branches (a branch would make the compiler wait for all copies before
-  // each LDS read) and the extra steps add nothing.
-  auto issue = [&](char* lt, char* rt, int s) __attribute__((always_inline)) {
-    const bool in = (int64_t)s * ST + 8 * lch < kext;  // also false past the slice
+  // Source of a unit: the resources of its tile and its first stage (past
+  // the workgroup's range: a stage beyond every tile, so all lanes read
+  // zeros).
+  struct Src {
+    rsrc_t rl, rr;
+    int k0;
+  };
+  auto src = [&](uint32_t u) __attribute__((always_inline)) {
+    const uint32_t uu = u < u1 ? u : u1 - 1;
+    const uint32_t t = uu / ut;
+    const int64_t mb = t / jt, jb = t % jt;
+    Src o;
+    o.rl = make_rsrc(L + 64 * mb * ldl, (M - 64 * mb) * ldl * 2);
+    o.rr = make_rsrc(R + 64 * jb * ldr, rrows > 64 * jb ? (rrows - 64 * jb) * ldr * 2 : 0);
+    o.k0 = u < u1 ? (int)(uu - t * ut) * NSTAGE : (1 << 24);
+    return o;
+  };
+  auto issue = [&](char* lt, char* rt, const Src& sr, int i) __attribute__((always_inline)) {
+    const int kc = (sr.k0 + i) * ST;
+    const bool in = (int64_t)kc + 8 * lch < Kred;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint32_t ol = in ? vl + (uint32_t)(c * 8 * ldl * 2) + (uint32_t)s * (ST * 2) : l_oob;
-      const uint32_t orr = in ? vr + (uint32_t)(c * 8 * ldr * 2) + (uint32_t)s * (ST * 2) : r_oob;
-      buf_load_lds16(rl, lt + (16 * wave + 8 * c) * 128, ol, 0u);
-      buf_load_lds16(rr, rt + (16 * wave + 8 * c) * 128, orr, 0u);
+      const uint32_t ol = in ? vl + (uint32_t)(c * 8 * ldl * 2) + (uint32_t)kc * 2u : 0x7fffffffu;
+      const uint32_t orr = in ? vr + (uint32_t)(c * 8 * ldr * 2) + (uint32_t)kc * 2u : 0x7fffffffu;
+      buf_load_lds16(sr.rl, lt + (16 * wave + 8 * c) * 128, ol, 0u);
+      buf_load_lds16(sr.rr, rt + (16 * wave + 8 * c) * 128, orr, 0u);
     }
   };
 
   const int wm = wave >> 1, wj = wave & 1;
   f32x4_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const char* lt, const char* rt) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -130,43 +152,52 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
     }
   };
-  // one step on the ring stage (lt, rt); the stage refilled after the
-  // barrier is the one read in the previous step
-  auto step = [&](int s, char* lt, char* rt, char* lnext, char* rnext) __attribute__((always_inline)) {
+  // one stage: wait for it, open it, refill the stage read before it, multiply
+  auto step = [&](const char* lt, const char* rt, char* ln, char* rn, const Src& sr, int i)
+      __attribute__((always_inline)) {
     wait_stage<4>();
     stage_barrier();
-    issue(lnext, rnext, s + NSTAGE - 1);
+    issue(ln, rn, sr, i);
     compute(lt, rt);
   };
-  issue(l0, r0, 0);
-  issue(l1, r1, 1);
-  issue(l2, r2, 2);
-  for (int s = 0; s < nsteps; s += NSTAGE) {
-    step(s, l0, r0, l3, r3);
-    step(s + 1, l1, r1, l0, r0);
-    step(s + 2, l2, r2, l1, r1);
-    step(s + 3, l3, r3, l2, r2);
+
+  Src cur = src(u0);
+  issue(l0, r0, cur, 0);
+  issue(l1, r1, cur, 1);
+  issue(l2, r2, cur, 2);
+  uint32_t u = u0;
+  while (u < u1) {
+    const uint32_t t = u / ut, ue = std::min(u1, (t + 1) * ut);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (; u < ue; ++u) {
+      const Src nxt = src(u + 1);
+      step(l0, r0, l3, r3, cur, 3);
+      step(l1, r1, l0, r0, nxt, 0);
+      step(l2, r2, l1, r1, nxt, 1);
+      step(l3, r3, l2, r2, nxt, 2);
+      cur = nxt;
+    }
+    float* o = P + ((int64_t)t * cmax + (g - sk_owner(t * ut, U, G))) * (64 * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          o[(32 * wm + 16 * i + 4 * kq + v) * 64 + 32 * wj + 16 * j + lr] = acc[i][j][v];
   }
   wait_vmem();  // no copy may land in LDS after the workgroup ends
-
-  float* o = P + (int64_t)blockIdx.z * M * Rp;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + 32 * wm + 16 * i + 4 * kq + v, jj = j0 + 32 * wj + 16 * j + lr;
-        if (m < M && jj < Rp) o[m * Rp + jj] = acc[i][j][v];
-      }
 }
 
 // ---------------------------------------------------------------------------
-// colred: P[z][p0 + p][j0 + j] = Σ_{m in slice z} L[m][p] · (S[j][m] + S[Rp + j][m])
+// colred: tile (pb, jb) = Σ_m L[m][128pb + p] · (S[64jb + j][m] + S[Rp + 64jb + j][m])
 // for p < 128, j < 64.  L [Mred, Pn] (leading dimension ldl); S [2Rp, lds]
 // (the transposed hi/lo split, columns m >= Mred zero).  Rows m past Mred
-// read as zero.  Workgroup: 128 columns of L by 64 rows of S, 4 waves of
-// 32 x 64.  Grid (ceil(Pn/128), ceil(Rp/64), slices).  Output [S, Pn, Rp].
+// read as zero.  Tile t = pb·jt + jb; 4 waves of 32 x 64.  Partial tiles
+// [tiles, cmax, 128, 64].
 //
 // The L tile keeps the natural layout (rows m of 256 bytes, 16-byte chunk c
 // of row m at physical chunk c ^ 2((m >> 3) & 7)); an MFMA operand needs 8
@@ -180,54 +211,59 @@ __device__ __forceinline__ int lswz(int row, int chunk) {
 __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict__ L, int64_t Mred,
                                                      int64_t Pn, int64_t ldl,
                                                      const uint16_t* __restrict__ S, int64_t lds,
-                                                     int64_t Rp, int64_t chunk, float* __restrict__ P) {
+                                                     int64_t Rp, int jt, uint32_t ut, uint32_t U, int cmax,
+                                                     float* __restrict__ P) {
   __shared__ __attribute__((aligned(1024))) char l0[64 * 256], l1[64 * 256], l2[64 * 256], l3[64 * 256];
   __shared__ __attribute__((aligned(1024))) char s0[128 * 128], s1[128 * 128], s2[128 * 128], s3[128 * 128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
-  const int64_t p0 = (int64_t)blockIdx.x * 128, j0 = (int64_t)blockIdx.y * 64;
-  const int64_t mb = (int64_t)blockIdx.z * chunk;
-  const int64_t mext = std::min(chunk, Mred - mb);
-  const int nsteps = (int)((mext + ST - 1) / ST);
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  const uint32_t u0 = sk_begin(g, U, G), u1 = sk_begin(g + 1, U, G);
+  (void)Pn;
 
-  const rsrc_t rl = make_rsrc(L + mb * ldl + p0, ((Mred - mb) * ldl - p0) * 2);
-  const rsrc_t rs = make_rsrc(S + mb, (2 * Rp * lds - mb) * 2);
   // L tile: wave w copies rows 16w + 4c + (lane >> 4), c = 0..3; lane i fills
   // physical chunk i & 15.  S tile: wave w copies rows 32w + 8c + (lane >> 3)
-  // (tile rows 0..63: hi rows j0 + t, 64..127: lo rows Rp + j0 + t - 64).
+  // (tile rows 0..63: hi rows 64jb + t, 64..127: lo rows Rp + 64jb + t - 64).
   const int lpc = lane & 15;
-  uint32_t vl[4];
+  uint32_t vl[4], vs[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int row = 16 * wave + 4 * c + (lane >> 4);
     vl[c] = (uint32_t)((row * ldl + 8 * (lpc ^ (((row >> 3) & 7) << 1))) * 2);
-  }
-  uint32_t vs[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
     const int t = 32 * wave + 8 * c + (lane >> 3);
-    const int64_t srow = t < 64 ? j0 + t : Rp + j0 + (t - 64);
-    const int sch = (lane & 7) ^ (t & 7);
-    vs[c] = (uint32_t)((srow * lds + 8 * sch) * 2);
+    const int64_t srow = t < 64 ? t : Rp + (t - 64);
+    vs[c] = (uint32_t)((srow * lds + 8 * ((lane & 7) ^ (t & 7))) * 2);
   }
-  // steps past the slice read zeros (all lanes outside the resources)
-  // (the test is made on a vector register: a uniform one would become a
-  // branch)
-  auto issue = [&](char* lt, char* st, int s) __attribute__((always_inline)) {
-    const bool in = opaque(s) < nsteps;
-    const uint32_t sl = (uint32_t)((int64_t)s * ST * ldl * 2), ss = (uint32_t)s * (ST * 2);
+  const rsrc_t rs = make_rsrc(S, 2 * Rp * lds * 2);
+  struct Src {
+    rsrc_t rl;
+    uint32_t sbase;  // byte offset of the tile's first S row
+    int k0;
+  };
+  auto src = [&](uint32_t u) __attribute__((always_inline)) {
+    const uint32_t uu = u < u1 ? u : u1 - 1;
+    const uint32_t t = uu / ut;
+    const int64_t pb = t / jt, jb = t % jt;
+    Src o;
+    o.rl = make_rsrc(L + 128 * pb, (Mred * ldl - 128 * pb) * 2);
+    o.sbase = (uint32_t)(64 * jb * lds * 2);
+    o.k0 = u < u1 ? (int)(uu - t * ut) * NSTAGE : (1 << 20);
+    return o;
+  };
+  // (the row test is made on a vector register: on a scalar one it would
+  // become a branch, and a branch makes the compiler wait for every copy)
+  auto issue = [&](char* lt, char* st, const Src& sr, int i) __attribute__((always_inline)) {
+    const int ks = sr.k0 + i;
+    const bool in = (int64_t)opaque(ks) * ST < Mred;
+    const uint32_t ol = (uint32_t)((int64_t)ks * ST * ldl * 2), os = sr.sbase + (uint32_t)ks * (ST * 2);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      buf_load_lds16(rl, lt + (16 * wave + 4 * c) * 256, in ? vl[c] : 0x7fffffffu, sl);
-      buf_load_lds16(rs, st + (32 * wave + 8 * c) * 128, in ? vs[c] : 0x7fffffffu, ss);
+      buf_load_lds16(sr.rl, lt + (16 * wave + 4 * c) * 256, in ? vl[c] + ol : 0x7fffffffu, 0u);
+      buf_load_lds16(rs, st + (32 * wave + 8 * c) * 128, in ? vs[c] + os : 0x7fffffffu, 0u);
     }
   };
 
   f32x4_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const char* lt, const char* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int mh = 0; mh < 2; ++mh) {
@@ -256,69 +292,150 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
       }
     }
   };
-  auto step = [&](int s, char* lt, char* st, char* lnext, char* snext) __attribute__((always_inline)) {
+  auto step = [&](const char* lt, const char* st, char* ln, char* sn, const Src& sr, int i)
+      __attribute__((always_inline)) {
     wait_stage<8>();
     stage_barrier();
-    issue(lnext, snext, s + NSTAGE - 1);
+    issue(ln, sn, sr, i);
     compute(lt, st);
   };
-  issue(l0, s0, 0);
-  issue(l1, s1, 1);
-  issue(l2, s2, 2);
-  for (int s = 0; s < nsteps; s += NSTAGE) {
-    step(s, l0, s0, l3, s3);
-    step(s + 1, l1, s1, l0, s0);
-    step(s + 2, l2, s2, l1, s1);
-    step(s + 3, l3, s3, l2, s2);
+
+  Src cur = src(u0);
+  issue(l0, s0, cur, 0);
+  issue(l1, s1, cur, 1);
+  issue(l2, s2, cur, 2);
+  uint32_t u = u0;
+  while (u < u1) {
+    const uint32_t t = u / ut, ue = std::min(u1, (t + 1) * ut);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (; u < ue; ++u) {
+      const Src nxt = src(u + 1);
+      step(l0, s0, l3, s3, cur, 3);
+      step(l1, s1, l0, s0, nxt, 0);
+      step(l2, s2, l1, s1, nxt, 1);
+      step(l3, s3, l2, s2, nxt, 2);
+      cur = nxt;
+    }
+    float* o = P + ((int64_t)t * cmax + (g - sk_owner(t * ut, U, G))) * (128 * 64);
+#pragma unroll
+    for (int pf = 0; pf < 2; ++pf)
+#pragma unroll
+      for (int jf = 0; jf < 4; ++jf)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          o[(32 * wave + 16 * pf + 4 * kq + v) * 64 + 16 * jf + lr] = acc[pf][jf][v];
   }
   wait_vmem();
-
-  float* o = P + (int64_t)blockIdx.z * Pn * Rp;
-#pragma unroll
-  for (int pf = 0; pf < 2; ++pf)
-#pragma unroll
-    for (int jf = 0; jf < 4; ++jf)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t p = p0 + 32 * wave + 16 * pf + 4 * kq + v, j = j0 + 16 * jf + lr;
-        if (p < Pn && j < Rp) o[p * Rp + j] = acc[pf][jf][v];
-      }
 }
 
 // ---------------------------------------------------------------------------
-// Reductions of the slices (fixed order z = 0..S-1) and operand preparation
+// Reductions of the partial tiles (slot order) and operand preparation
 // ---------------------------------------------------------------------------
 
-// From P [S, M, Rp]: optional fp32 T [M, r]; hi/lo split of scale·T into
-// out [M, 2Rp] (hi in columns < Rp, lo from Rp; zeros for j >= r) and, if
-// outT is non-null, its transpose outT [2Rp, Mp] (zeros for m >= M).
-// One thread per (m, j), m < Mp.
-__global__ void lora_reduce_kernel(const float* __restrict__ P, int S, int64_t M, int64_t Mp, int r,
-                                   int64_t Rp, float scale, float* __restrict__ T,
-                                   uint16_t* __restrict__ out, uint16_t* __restrict__ outT) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Mp * Rp) return;
-  // m runs fastest inside a block of 64 so that the transposed stores coalesce
-  const int64_t mblk = idx / (64 * Rp), rem = idx % (64 * Rp);
-  const int64_t j = rem / 64, m = mblk * 64 + rem % 64;
-  uint16_t hi = 0, lo = 0;
-  if (m < M) {
-    float acc = 0.0f;
-    for (int z = 0; z < S; ++z) acc = __fadd_rn(acc, P[((int64_t)z * M + m) * Rp + j]);
-    if (j < r) {
-      if (T) T[m * r + j] = acc;
-      split_hilo(__fmul_rn(scale, acc), hi, lo);
+// Slot range of tile t: partial tiles P[t][0 .. count).
+__device__ __forceinline__ int sk_count(uint32_t t, uint32_t ut, uint32_t U, uint32_t G) {
+  return (int)(sk_owner((t + 1) * ut - 1, U, G) - sk_owner(t * ut, U, G)) + 1;
+}
+
+// rowred tiles (64 m x 64 j) → optional fp32 T [M, r]; hi/lo split of
+// scale·T into out [M, 2Rp] (hi in columns < Rp, lo from Rp; zeros for
+// j >= r) and, if outT is non-null, its transpose outT [2Rp, Mp] (zeros for
+// m >= M).  One workgroup of 256 per 32 rows of a tile (8 values a thread,
+// each slot's 8 loads issued together).
+__global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restrict__ P, int jt, uint32_t ut,
+                                                            uint32_t U, uint32_t G, int cmax, int64_t M,
+                                                            int64_t Mp, int r, int64_t Rp, float scale,
+                                                            float* __restrict__ T, uint16_t* __restrict__ out,
+                                                            uint16_t* __restrict__ outT) {
+  __shared__ uint32_t sh[64][33];  // hi | lo << 16 of (j, m), padded
+  const uint32_t t = blockIdx.x >> 1, half = blockIdx.x & 1;
+  const int64_t m0 = (int64_t)(t / jt) * 64 + 32 * half, j0 = (int64_t)(t % jt) * 64;
+  const int cnt = sk_count(t, ut, U, G);
+  const float* pt = P + (int64_t)t * cmax * 4096 + 32 * half * 64;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < cnt; ++c) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = pt[(int64_t)c * 4096 + threadIdx.x + 256 * e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = threadIdx.x + 256 * e, i = idx >> 6, jj = idx & 63;
+    const int64_t m = m0 + i, j = j0 + jj;
+    uint16_t hi = 0, lo = 0;
+    if (m < M && j < r) {
+      if (T) T[m * r + j] = acc[e];
+      split_hilo(__fmul_rn(scale, acc[e]), hi, lo);
     }
-    out[m * 2 * Rp + j] = hi;
-    out[m * 2 * Rp + Rp + j] = lo;
+    if (m < M && j < Rp) {
+      out[m * 2 * Rp + j] = hi;
+      out[m * 2 * Rp + Rp + j] = lo;
+    }
+    sh[jj][i] = (uint32_t)hi | ((uint32_t)lo << 16);
   }
-  if (outT) {
-    outT[j * Mp + m] = hi;
-    outT[(Rp + j) * Mp + m] = lo;
+  if (!outT) return;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = threadIdx.x + 256 * e, jj = idx >> 5, i = idx & 31;
+    const int64_t m = m0 + i, j = j0 + jj;
+    if (j < Rp && m < Mp) {
+      const uint32_t v = sh[jj][i];
+      outT[j * Mp + m] = (uint16_t)(v & 0xffffu);
+      outT[(Rp + j) * Mp + m] = (uint16_t)(v >> 16);
+    }
   }
 }
 
-// sT and its transpose from a saved fp32 T [M, r].
+// colred tiles (128 p x 64 j) → out [Pn, r] (out[p][j], transpose == 0) or
+// out [r, Pn] (out[j][p], transpose == 1).  One workgroup of 256 per 32
+// rows p of a tile.
+__global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restrict__ P, int jt, uint32_t ut,
+                                                            uint32_t U, uint32_t G, int cmax, int64_t Pn,
+                                                            int r, int transpose, float* __restrict__ out) {
+  __shared__ float sh[64][33];
+  const uint32_t t = blockIdx.x >> 2, q = blockIdx.x & 3;
+  const int64_t p0 = (int64_t)(t / jt) * 128 + 32 * q, j0 = (int64_t)(t % jt) * 64;
+  const int cnt = sk_count(t, ut, U, G);
+  const float* pt = P + (int64_t)t * cmax * 8192 + 32 * q * 64;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < cnt; ++c) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = pt[(int64_t)c * 8192 + threadIdx.x + 256 * e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], v[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = threadIdx.x + 256 * e, i = idx >> 6, jj = idx & 63;
+    const int64_t p = p0 + i, j = j0 + jj;
+    if (!transpose) {
+      if (p < Pn && j < r) out[p * r + j] = acc[e];
+    } else {
+      sh[jj][i] = acc[e];
+    }
+  }
+  if (!transpose) return;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int idx = threadIdx.x + 256 * e, jj = idx >> 5, i = idx & 31;
+    const int64_t p = p0 + i, j = j0 + jj;
+    if (p < Pn && j < r) out[j * Pn + p] = sh[jj][i];
+  }
+}
+
+// sT [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r].
 __global__ void split_saved_kernel(const float* __restrict__ T, int64_t M, int64_t Mp, int r, int64_t Rp,
                                    float scale, uint16_t* __restrict__ sT, uint16_t* __restrict__ sTT) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -335,16 +452,10 @@ __global__ void split_saved_kernel(const float* __restrict__ T, int64_t M, int64
   sTT[(Rp + j) * Mp + m] = lo;
 }
 
-// out[a][b] = Σ_z P[z·zs + a·sa + b·sb] for a < An, b < Bn (fixed order);
-// with S == 0, zeros.
-__global__ void reduce_slices_kernel(const float* __restrict__ P, int S, int64_t zs, int64_t An,
-                                     int64_t Bn, int64_t sa, int64_t sb, float* __restrict__ out) {
+// Zeros of the adapter gradients when there are no tokens.
+__global__ void zero_kernel(float* __restrict__ a, int64_t n) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= An * Bn) return;
-  const int64_t a = idx / Bn, b = idx % Bn;
-  float acc = 0.0f;
-  for (int z = 0; z < S; ++z) acc = __fadd_rn(acc, P[(int64_t)z * zs + a * sa + b * sb]);
-  out[idx] = acc;
+  if (idx < n) a[idx] = 0.0f;
 }
 
 // BT [Rp, Np] = Bᵀ for j < r, n < N; zeros elsewhere.  B is [N, r].
@@ -360,41 +471,59 @@ unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
-// Reduction slices for `tiles` output tiles over `red` reduction elements:
-// about 256 workgroups in all, but at least 8 stages per slice where the
-// reduction allows it.
-LoraSlices lora_slices(int64_t red, int64_t tiles) {
-  const int64_t steps = std::max<int64_t>(1, (red + ST - 1) / ST);
-  int64_t s = std::max<int64_t>(1, (256 + tiles - 1) / std::max<int64_t>(tiles, 1));
-  s = std::min(s, std::max<int64_t>(1, steps / 8));
-  const int64_t per = (steps + s - 1) / s;
-  LoraSlices out;
-  out.chunk = per * ST;
-  out.count = (steps + per - 1) / per;
-  return out;
+// Stream-K plan of a product with `tiles` output tiles of `ns` stages each.
+SkPlan sk_plan(int64_t tiles, int64_t ns, int jt) {
+  SkPlan p{};
+  p.jt = jt;
+  p.tiles = tiles;
+  p.ut = (uint32_t)std::max<int64_t>(1, (ns + NSTAGE - 1) / NSTAGE);
+  p.U = (uint32_t)(tiles * p.ut);
+  p.G = std::min<uint32_t>(p.U, kSkWorkgroups);
+  p.cmax = 1;
+  for (int64_t t = 0; t < tiles; ++t) {
+    const int c = (int)(sk_owner((uint32_t)((t + 1) * p.ut - 1), p.U, p.G) -
+                        sk_owner((uint32_t)(t * p.ut), p.U, p.G)) + 1;
+    p.cmax = std::max(p.cmax, c);
+  }
+  return p;
 }
+
+SkPlan rowred_plan(int64_t M, int64_t Kred, int64_t Rp) {
+  const int jt = (int)cdiv(Rp, 64);
+  return sk_plan((int64_t)cdiv(M, 64) * jt, cdiv(Kred, ST), jt);
+}
+SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp) {
+  const int jt = (int)cdiv(Rp, 64);
+  return sk_plan((int64_t)cdiv(Pn, 128) * jt, cdiv(Mred, ST), jt);
+}
+size_t rowred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 64 * 64 * 4; }
+size_t colred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 128 * 64 * 4; }
 
 int64_t lora_mp(int64_t M) { return round_up(std::max<int64_t>(M, 1), 64); }
 
 hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl, const uint16_t* R,
-                         int64_t rrows, int64_t ldr, int64_t Rp, const LoraSlices& sl, float* P,
-                         hipStream_t st) {
-  rowred_kernel<<<dim3(cdiv(M, 64), cdiv(Rp, 64), (unsigned)sl.count), 256, 0, st>>>(
-      L, M, Kred, ldl, R, rrows, ldr, sl.chunk, Rp, P);
+                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, hipStream_t st) {
+  rowred_kernel<<<p.G, 256, 0, st>>>(L, M, Kred, ldl, R, rrows, ldr, p.jt, p.ut, p.U, p.cmax, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
+                                float scale, float* T, uint16_t* out, uint16_t* outT, hipStream_t st) {
+  rowred_finish_kernel<<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M), r, Rp,
+                                                          scale, T, out, outT);
   return hipGetLastError();
 }
 
 hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const LoraSlices& sl, float* P, hipStream_t st) {
-  colred_kernel<<<dim3(cdiv(Pn, 128), cdiv(Rp, 64), (unsigned)sl.count), 256, 0, st>>>(
-      L, Mred, Pn, ldl, S, lds, Rp, sl.chunk, P);
+                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, hipStream_t st) {
+  colred_kernel<<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
   return hipGetLastError();
 }
 
-hipError_t launch_lora_reduce(const float* P, int S, int64_t M, int32_t r, int64_t Rp, float scale,
-                              float* T, uint16_t* out, uint16_t* outT, hipStream_t st) {
-  const int64_t Mp = lora_mp(M);
-  lora_reduce_kernel<<<cdiv(Mp * Rp, 256), 256, 0, st>>>(P, S, M, Mp, r, Rp, scale, T, out, outT);
+hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
+                                float* out, hipStream_t st) {
+  colred_finish_kernel<<<(unsigned)(4 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, Pn, r,
+                                                          transpose ? 1 : 0, out);
   return hipGetLastError();
 }
 
@@ -405,10 +534,9 @@ hipError_t launch_split_saved(const float* T, int64_t M, int32_t r, int64_t Rp, 
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_slices(const float* P, int S, int64_t zs, int64_t An, int64_t Bn, int64_t sa,
-                                int64_t sb, float* out, hipStream_t st) {
-  if (An * Bn == 0) return hipSuccess;
-  reduce_slices_kernel<<<cdiv(An * Bn, 256), 256, 0, st>>>(P, S, zs, An, Bn, sa, sb, out);
+hipError_t launch_zero(float* a, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  zero_kernel<<<cdiv(n, 256), 256, 0, st>>>(a, n);
   return hipGetLastError();
 }
 
