@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
                                                               int64_t Rp, void* __restrict__ dX,
                                                               int dx_bf16, int tiles_m, int tiles_k,
                                                               Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char sa[2][TM * 128];  // A tiles: dY, then sU
+  __shared__ __attribute__((aligned(16))) char sa0[TM * 128], sa1[TM * 128];  // A tiles: dY, then sU
   __shared__ __attribute__((aligned(16))) char sw[2][TK * 128];  // B tiles: Ŵᵀ, then AT2
   // per wave (all wave-private, so one buffer each): 64 row tables of 32
   // bytes, the 16 code bytes of each weight row for the wave's 32 columns,
@@ -94,22 +94,22 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rat = make_rsrc(AT2 + k0 * 2 * Rp, (K - k0) * 2 * Rp * 2);
 
-  // dY tile: thread τ moves 16 bytes of rows 64c + (τ >> 3), c = 0..3, into
-  // physical chunk τ & 7: logical chunk (τ & 7) ^ ((τ >> 3) & 7).
+  // dY tile, copied straight into LDS: thread τ moves 16 bytes of rows
+  // 64c + (τ >> 3), c = 0..3, into physical chunk τ & 7: logical chunk
+  // (τ & 7) ^ ((τ >> 3) & 7); each wave's copy is 1 KB contiguous.  (Written
+  // as assembly: the compiler then inserts no wait for these copies in front
+  // of the LDS reads of the step; the wait before the step's closing
+  // barrier is explicit.)
   const int ylch = (tid & 7) ^ ((tid >> 3) & 7);
   const uint32_t vy = (uint32_t)(((tid >> 3) * N + 8 * ylch) * 2);
   const uint32_t y_gstride = (uint32_t)(64 * N * 2);
-  struct YRegs {
-    u32x4_t v[4];
-  };
-  auto load_y = [&](YRegs& r, int s) __attribute__((always_inline)) {
+  const i32x4_t ryw = rsrc_words(dY + m0 * N, (M - m0) * N * 2);
+  auto copy_y = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.v[c] = buf_load16(rdy, vy, c * y_gstride + (uint32_t)s * 128u);
+    for (int c = 0; c < 4; ++c)
+      dma_lds16(ryw, t + 64 * c * 128 + 1024 * wave, vy + c * y_gstride, (uint32_t)s * 128u);
   };
-  auto store_y = [&](char* t, const YRegs& r) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(t + 64 * c * 128 + 16 * tid) = r.v[c];
-  };
+  auto sab = [&](int i) { return i ? sa1 : sa0; };
   // LoRA tiles copied straight into LDS: wave w copies rows 32w + 8c + (i >> 3),
   // lane i into physical chunk i & 7.  sU rows use xswz, AT2 rows wswz.
   const uint32_t vsu = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
@@ -274,13 +274,12 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // prologue: dY and weight data of step 0; dequantize step 0; weight data
   // of step 1
   {
-    YRegs yr;
     WRegs w0;
-    load_y(yr, 0);
+    copy_y(sa0, 0);
     load_w(w0, 0);
-    store_y(sa[0], yr);
     store_w(w0);
   }
+  wait_vmem();
   __syncthreads();  // dY and weight data of step 0
   build_table(0);
   {
@@ -295,22 +294,23 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   }
   __syncthreads();
 
-  // Reduction steps 0 .. nsteps-2: load dY of step s+1 and the weight data
-  // of step s+2, issue the MFMAs of step s interleaved with the
-  // dequantization of step s+1 into the other Ŵᵀ buffer, then store the
-  // loaded data (the weight buffers are wave-private and were last read
-  // earlier in this iteration).  Weight data of step nsteps may be loaded:
-  // its reads stay inside the buffers or return zeros, and it is not used.
-  // The loop is instantiated once per phase.
+  // Reduction steps 0 .. nsteps-2: copy dY of step s+1 into the other dY
+  // buffer and load the weight data of step s+2, issue the MFMAs of step s
+  // interleaved with the dequantization of step s+1 into the other Ŵᵀ
+  // buffer, then store the loaded weight data (the weight buffers are
+  // wave-private and were last read earlier in this iteration).  Weight data
+  // of step nsteps may be loaded: its reads stay inside the buffers or
+  // return zeros, and it is not used.  The loop is instantiated once per
+  // phase.
   auto main_loop = [&](auto P) __attribute__((always_inline)) {
+#pragma unroll 1
     for (int s = 0; s + 1 < nsteps; ++s) {
-      YRegs yr;
       WRegs wr;
-      load_y(yr, s + 1);
+      copy_y(sab((s + 1) & 1), s + 1);
       load_w(wr, s + 2);
-      mfma_step_dequant(P, sa[s & 1], sw[s & 1], s + 1, sw[(s + 1) & 1]);
-      store_y(sa[(s + 1) & 1], yr);
+      mfma_step_dequant(P, sab(s & 1), sw[s & 1], s + 1, sw[(s + 1) & 1]);
       store_w(wr);
+      wait_vmem();
       __syncthreads();
     }
   };
@@ -320,19 +320,19 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     main_loop(std::integral_constant<int, 1>());
   // last reduction step, copying LoRA step 0 (sU and AT2 tiles) into the
   // other buffers; then the LoRA steps, unrolled
-  copy_su(sa[nsteps & 1], 0);
+  copy_su(sab(nsteps & 1), 0);
   copy_at(sw[nsteps & 1], 0);
-  mfma_step(sa[(nsteps - 1) & 1], sw[(nsteps - 1) & 1]);
+  mfma_step(sab((nsteps - 1) & 1), sw[(nsteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int l = 0; l < LSTEPS; ++l) {
     const int s = nsteps + l;
     if (l + 1 < LSTEPS) {
-      copy_su(sa[(s + 1) & 1], l + 1);
+      copy_su(sab((s + 1) & 1), l + 1);
       copy_at(sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sa[s & 1], sw[s & 1]);
+    mfma_step(sab(s & 1), sw[s & 1]);
     wait_vmem();
     __syncthreads();
   }
@@ -367,22 +367,10 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   }
 }
 
-// AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r, else 0;  [K, 2Rp] bf16.
-__global__ void transpose_lora_a_kernel(const uint16_t* __restrict__ A, int64_t K, int r, int64_t Rp,
-                                        uint16_t* __restrict__ AT2) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= K * 2 * Rp) return;
-  const int64_t k = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
-  AT2[idx] = j < r ? A[j * K + k] : (uint16_t)0;
-}
-
 }  // namespace
 
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* A, int32_t r, int64_t Rp, uint16_t* AT2, void* dX,
-                          bool dx_bf16, hipStream_t st) {
-  const int64_t n2 = W.K * 2 * Rp;
-  transpose_lora_a_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, st>>>(A, W.K, r, Rp, AT2);
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx_bf16, hipStream_t st) {
   const int tm = (int)((M + TM - 1) / TM), tk = (int)((W.K + TK - 1) / TK);
   const unsigned grid = tile_grid(tm, tk);
   const int db = dx_bf16 ? 1 : 0;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                int64_t Rp, void* __restrict__ Y,
                                                                int y_bf16, int tiles_m, int tiles_n,
                                                                Codebook cb) {
-  __shared__ __attribute__((aligned(16))) char sx[2][TM * 128];  // A tiles: X, then sT
+  __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
   // per wave: tables of its 32 rows (row t at 32(t % 8) + 256(t / 8)), the
   // packed codes of its rows (32 bytes each) and, per row, the dword holding
@@ -95,23 +95,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
 
-  // X tile: thread τ moves 16 bytes of rows 64c + (τ >> 3), c = 0..3, into
-  // physical chunk τ & 7, so it fetches logical chunk (τ & 7) ^ ((τ >> 3) & 7)
-  // (row & 7 does not depend on c).  LDS offset 64c*128 + 16τ.
+  // X tile, copied straight into LDS: thread τ moves 16 bytes of rows
+  // 64c + (τ >> 3), c = 0..3, into physical chunk τ & 7, so it fetches
+  // logical chunk (τ & 7) ^ ((τ >> 3) & 7) (row & 7 does not depend on c).
+  // LDS offset 64c*128 + 16τ: each wave's copy is 1 KB contiguous.
   const int xlch = (tid & 7) ^ ((tid >> 3) & 7);
   const uint32_t vx = (uint32_t)(((tid >> 3) * K + 8 * xlch) * 2);
   const uint32_t x_gstride = (uint32_t)(64 * K * 2);
-  struct XRegs {
-    u32x4_t v[4];
-  };
-  auto load_x = [&](XRegs& r, int s) __attribute__((always_inline)) {
+  // (written as assembly: the compiler then inserts no wait for these copies
+  // in front of the LDS reads of the step; the wait before the step's
+  // closing barrier is explicit)
+  const i32x4_t rxw = rsrc_words(X + m0 * K, (M - m0) * K * 2);
+  auto copy_x = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.v[c] = buf_load16(rx, vx, c * x_gstride + (uint32_t)s * 128u);
+    for (int c = 0; c < 4; ++c)
+      dma_lds16(rxw, t + 64 * c * 128 + 1024 * wave, vx + c * x_gstride, (uint32_t)s * 128u);
   };
-  auto store_x = [&](char* t, const XRegs& r) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(t + 64 * c * 128 + 16 * tid) = r.v[c];
-  };
+  auto sxb = [&](int i) { return i ? sx1 : sx0; };
   // LoRA tiles (sT rows, B2 rows) copied straight into LDS: wave w copies rows
   // 32w + 8c + (i >> 3), c = 0..3, lane i into physical chunk i & 7, so it
   // fetches logical chunk (i & 7) ^ (i >> 3).
@@ -230,41 +230,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // prologue: X and weight data of step 0, weight data of step 1 (K >= 64,
   // so step 0 is a weight step); dequantize step 0
   {
-    XRegs xr;
     WRegs w0, w1;
-    load_x(xr, 0);
+    copy_x(sx0, 0);
     load_w(w0, 0);
     load_w(w1, 1);
-    store_x(sx[0], xr);
     store_w(0, w0);
     store_w(1, w1);
   }
+  wait_vmem();
   __syncthreads();
   build_table(0, 0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) dequant_group(0, sw[0], q);
   __syncthreads();
 
-  // Weight steps 0 .. ksteps-2: load X of step s+1 and the weight data of
-  // step s+2 into registers, issue the MFMAs of step s interleaved with the
-  // dequantization of step s+1 into the other Ŵ buffer, then store the
-  // loaded data into the other X buffer and weight slot s % 2 (both last read
-  // in the previous iteration).  (Weight data of step ksteps may be loaded:
-  // its reads stay inside the buffers or return zeros, and it is not used.)
-  // One step per iteration and no other loop carrying the accumulators:
-  // anything else makes the register allocator shuffle or spill them.  The
-  // loop is instantiated once per phase.
+  // Weight steps 0 .. ksteps-2: copy X of step s+1 into the other X buffer
+  // and load the weight data of step s+2 into registers, issue the MFMAs of
+  // step s interleaved with the dequantization of step s+1 into the other Ŵ
+  // buffer, then store the weight data into slot s % 2 (both buffers last
+  // read in the previous iteration).  (Weight data of step ksteps may be
+  // loaded: its reads stay inside the buffers or return zeros, and it is not
+  // used.)  One step per iteration and no other loop carrying the
+  // accumulators: anything else makes the register allocator shuffle or
+  // spill them.  The loop is instantiated once per phase.
+  auto iter = [&](auto P, int s, const char* xa, char* xn) __attribute__((always_inline)) {
+    WRegs wr;
+    copy_x(xn, s + 1);
+    load_w(wr, s + 2);
+    mfma_step_dequant(P, xa, sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
+    store_w(s & 1, wr);
+    wait_vmem();
+    __syncthreads();
+  };
   auto main_loop = [&](auto P) __attribute__((always_inline)) {
-    for (int s = 0; s + 1 < ksteps; ++s) {
-      XRegs xr;
-      WRegs wr;
-      load_x(xr, s + 1);
-      load_w(wr, s + 2);
-      mfma_step_dequant(P, sx[s & 1], sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
-      store_x(sx[(s + 1) & 1], xr);
-      store_w(s & 1, wr);
-      __syncthreads();
-    }
+#pragma unroll 1
+    for (int s = 0; s + 1 < ksteps; ++s) iter(P, s, sxb(s & 1), sxb((s + 1) & 1));
   };
   if (wm == 0)
     main_loop(std::integral_constant<int, 0>());
@@ -272,19 +272,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     main_loop(std::integral_constant<int, 1>());
   // Last weight step, copying LoRA step 0 (sT and B2 tiles) into the other
   // buffers; then the LoRA steps, unrolled.
-  copy_lora(rt, sx[ksteps & 1], 0);
+  copy_lora(rt, sxb(ksteps & 1), 0);
   copy_lora(rb, sw[ksteps & 1], 0);
-  mfma_step(sx[(ksteps - 1) & 1], sw[(ksteps - 1) & 1]);
+  mfma_step(sxb((ksteps - 1) & 1), sw[(ksteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int l = 0; l < LSTEPS; ++l) {
     const int s = ksteps + l;
     if (l + 1 < LSTEPS) {
-      copy_lora(rt, sx[(s + 1) & 1], l + 1);
+      copy_lora(rt, sxb((s + 1) & 1), l + 1);
       copy_lora(rb, sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sx[s & 1], sw[s & 1]);
+    mfma_step(sxb(s & 1), sw[s & 1]);
     wait_vmem();
     __syncthreads();
   }

@@ -100,12 +100,13 @@ hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ld
 // Sums them → out [Pn, r], or out [r, Pn] when transposed.
 hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
                                 float* out, hipStream_t st);
-hipError_t launch_split_saved(const float* T, int64_t M, int32_t r, int64_t Rp, float scale,
-                              uint16_t* sT, uint16_t* sTT, hipStream_t st);
+// The backward pass's operand copies, one launch: if T is non-null, sT
+// [M, 2Rp] and sTT [2Rp, Mp] from the saved T; BT [Rp, round_up(N, 64)] =
+// Bᵀ zero-padded; AT2 [K, 2Rp] = [Aᵀ | Aᵀ] zero-padded.
+hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, float scale, uint16_t* sT,
+                           uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
+                           int64_t K, uint16_t* AT2, hipStream_t st);
 hipError_t launch_zero(float* a, int64_t n, hipStream_t st);
-// BT [Rp, round_up(N, 64)] = Bᵀ, zero-padded.
-hipError_t launch_transpose_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp, uint16_t* BT,
-                                   hipStream_t st);
 
 // Forward ------------------------------------------------------------------
 struct FwdLayout {

@@ -13,8 +13,7 @@
 namespace qnf4 {
 
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* A, int32_t r, int64_t Rp, uint16_t* AT2, void* dX,
-                          bool dx_bf16, hipStream_t st);
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx_bf16, hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
                            bool y_bf16, hipStream_t st);
@@ -115,21 +114,20 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   uint16_t* sUT = reinterpret_cast<uint16_t*>(ws + L.off_sUT);
   uint16_t* BT = reinterpret_cast<uint16_t*>(ws + L.off_BT);
   uint16_t* AT2 = reinterpret_cast<uint16_t*>(ws + L.off_AT2);
-  // s·T (hi/lo and transposed): from the saved T, or recomputed
-  if (T_saved) {
-    e = launch_split_saved(T_saved, M, r, Rp, scale, sT, sTT, st);
-  } else {
+  // operand copies: s·T (hi/lo and transposed) from the saved T, Bᵀ, [Aᵀ | Aᵀ]
+  e = launch_bwd_prep(T_saved, M, r, Rp, scale, sT, sTT, B, N, BT, A, K, AT2, st);
+  if (e != hipSuccess) return e;
+  if (!T_saved) {  // s·T recomputed
     e = launch_rowred(X, M, K, K, A, r, K, L.pT, P, st);
     if (e == hipSuccess) e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, st);
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
   // s·U, U = dY·B
-  e = launch_transpose_lora_b(B, N, r, Rp, BT, st);
-  if (e == hipSuccess) e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, st);
+  e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, st);
   if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, st);
   if (e != hipSuccess) return e;
   // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
-  e = launch_dx_gemm(W, dY, M, sU, A, r, Rp, AT2, dX, dx_bf16, st);
+  e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx_bf16, st);
   if (e != hipSuccess) return e;
   // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
   e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, st);

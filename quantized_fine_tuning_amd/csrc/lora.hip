@@ -16,8 +16,8 @@
 //   * colred: P[z][p][j] = Σ_m L[m][p]·S[j][m] over slice z of m (dA, dB),
 //     with S = hi + lo rows of the transposed bf16 split of s·U or s·T.
 // Both copy their operand tiles straight from global memory into a ring of
-// four LDS stages (buffer loads with the LDS destination), three stages in
-// flight per workgroup.  The stages are separate LDS arrays and the loop is
+// LDS stages (buffer loads with the LDS destination; 8 stages of 16 KB for
+// rowred, 5 of 32 KB for colred), all but one in flight per workgroup.  The stages are separate LDS arrays and the loop is
 // unrolled over them, so that the compiler can tell the copy into one stage
 // from the reads of another and needs no full wait before each read; each
 // wave waits for its own copies of a stage before the barrier that opens it.
@@ -31,8 +31,9 @@
 namespace qnf4 {
 namespace {
 
-constexpr int ST = 64;     // reduction elements per stage
-constexpr int NSTAGE = 4;  // ring depth
+constexpr int ST = 64;      // reduction elements per stage
+constexpr int kRowRing = 8;  // rowred ring depth (8 x 16 KB)
+constexpr int kColRing = 5;  // colred ring depth (5 x 32 KB)
 
 __device__ __forceinline__ int xswz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
@@ -46,11 +47,12 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Waits until the copies of the current stage are done: two more stages'
-// copies (PER load instructions per stage and wave) may stay in flight.
-template <int PER>
+// Waits until the copies of the current stage are done: the NS - 2 stages
+// issued after it (PER load instructions per stage and wave) may stay in
+// flight.
+template <int NS, int PER>
 __device__ __forceinline__ void wait_stage() {
-  wait_vmem_le<2 * PER>();
+  wait_vmem_le<(NS - 2) * PER>();
   asm volatile("" ::: "memory");
 }
 
@@ -63,7 +65,8 @@ __device__ __forceinline__ void split_hilo(float v, uint16_t& hi, uint16_t& lo) 
 
 // ---------------------------------------------------------------------------
 // Work split (stream-K).  A product has `tiles` output tiles, each a
-// reduction of ns stages, cut into units of NSTAGE stages (ut per tile; the
+// reduction of ns stages, cut into units of NS stages, NS the depth of the
+// copy ring (ut units per tile; the
 // stages of a last, partial unit past ns read zeros).  Workgroup g of G
 // takes units [gU/G, (g+1)U/G) of the U = tiles·ut units in tile order, so
 // every workgroup has the same amount of work whatever the number of tiles;
@@ -93,8 +96,14 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ R, int64_t rrows,
                                                      int64_t ldr, int jt, uint32_t ut, uint32_t U,
                                                      int cmax, float* __restrict__ P) {
-  __shared__ __attribute__((aligned(1024))) char l0[64 * 128], l1[64 * 128], l2[64 * 128], l3[64 * 128];
-  __shared__ __attribute__((aligned(1024))) char r0[64 * 128], r1[64 * 128], r2[64 * 128], r3[64 * 128];
+  constexpr int NS = kRowRing;
+  // the ring: separate arrays per stage (see the file comment)
+  __shared__ __attribute__((aligned(1024))) char l0[8192], l1[8192], l2[8192], l3[8192], l4[8192], l5[8192],
+      l6[8192], l7[8192];
+  __shared__ __attribute__((aligned(1024))) char r0[8192], r1[8192], r2[8192], r3[8192], r4[8192], r5[8192],
+      r6[8192], r7[8192];
+  char* const ls[NS] = {l0, l1, l2, l3, l4, l5, l6, l7};
+  char* const rs[NS] = {r0, r1, r2, r3, r4, r5, r6, r7};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const uint32_t G = gridDim.x, g = blockIdx.x;
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
     Src o;
     o.rl = make_rsrc(L + 64 * mb * ldl, (M - 64 * mb) * ldl * 2);
     o.rr = make_rsrc(R + 64 * jb * ldr, rrows > 64 * jb ? (rrows - 64 * jb) * ldr * 2 : 0);
-    o.k0 = u < u1 ? (int)(uu - t * ut) * NSTAGE : (1 << 24);
+    o.k0 = u < u1 ? (int)(uu - t * ut) * NS : (1 << 24);
     return o;
   };
   auto issue = [&](char* lt, char* rt, const Src& sr, int i) __attribute__((always_inline)) {
@@ -155,16 +164,15 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
   // one stage: wait for it, open it, refill the stage read before it, multiply
   auto step = [&](const char* lt, const char* rt, char* ln, char* rn, const Src& sr, int i)
       __attribute__((always_inline)) {
-    wait_stage<4>();
+    wait_stage<NS, 4>();
     stage_barrier();
     issue(ln, rn, sr, i);
     compute(lt, rt);
   };
 
   Src cur = src(u0);
-  issue(l0, r0, cur, 0);
-  issue(l1, r1, cur, 1);
-  issue(l2, r2, cur, 2);
+#pragma unroll
+  for (int i = 0; i + 1 < NS; ++i) issue(ls[i], rs[i], cur, i);
   uint32_t u = u0;
   while (u < u1) {
     const uint32_t t = u / ut, ue = std::min(u1, (t + 1) * ut);
@@ -173,11 +181,12 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (; u < ue; ++u) {
+      // stage i holds stage i of unit u; the stage refilled at position i
+      // takes stage NS - 1 of unit u (i = 0) or stage i - 1 of unit u + 1
       const Src nxt = src(u + 1);
-      step(l0, r0, l3, r3, cur, 3);
-      step(l1, r1, l0, r0, nxt, 0);
-      step(l2, r2, l1, r1, nxt, 1);
-      step(l3, r3, l2, r2, nxt, 2);
+      step(ls[0], rs[0], ls[NS - 1], rs[NS - 1], cur, NS - 1);
+#pragma unroll
+      for (int i = 1; i < NS; ++i) step(ls[i], rs[i], ls[i - 1], rs[i - 1], nxt, i - 1);
       cur = nxt;
     }
     float* o = P + ((int64_t)t * cmax + (g - sk_owner(t * ut, U, G))) * (64 * 64);
@@ -213,8 +222,11 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ S, int64_t lds,
                                                      int64_t Rp, int jt, uint32_t ut, uint32_t U, int cmax,
                                                      float* __restrict__ P) {
-  __shared__ __attribute__((aligned(1024))) char l0[64 * 256], l1[64 * 256], l2[64 * 256], l3[64 * 256];
-  __shared__ __attribute__((aligned(1024))) char s0[128 * 128], s1[128 * 128], s2[128 * 128], s3[128 * 128];
+  constexpr int NS = kColRing;
+  __shared__ __attribute__((aligned(1024))) char l0[16384], l1[16384], l2[16384], l3[16384], l4[16384];
+  __shared__ __attribute__((aligned(1024))) char s0[16384], s1[16384], s2[16384], s3[16384], s4[16384];
+  char* const ls[NS] = {l0, l1, l2, l3, l4};
+  char* const ss[NS] = {s0, s1, s2, s3, s4};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const uint32_t G = gridDim.x, g = blockIdx.x;
@@ -247,7 +259,7 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
     Src o;
     o.rl = make_rsrc(L + 128 * pb, (Mred * ldl - 128 * pb) * 2);
     o.sbase = (uint32_t)(64 * jb * lds * 2);
-    o.k0 = u < u1 ? (int)(uu - t * ut) * NSTAGE : (1 << 20);
+    o.k0 = u < u1 ? (int)(uu - t * ut) * NS : (1 << 20);
     return o;
   };
   // (the row test is made on a vector register: on a scalar one it would
@@ -294,16 +306,15 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
   };
   auto step = [&](const char* lt, const char* st, char* ln, char* sn, const Src& sr, int i)
       __attribute__((always_inline)) {
-    wait_stage<8>();
+    wait_stage<NS, 8>();
     stage_barrier();
     issue(ln, sn, sr, i);
     compute(lt, st);
   };
 
   Src cur = src(u0);
-  issue(l0, s0, cur, 0);
-  issue(l1, s1, cur, 1);
-  issue(l2, s2, cur, 2);
+#pragma unroll
+  for (int i = 0; i + 1 < NS; ++i) issue(ls[i], ss[i], cur, i);
   uint32_t u = u0;
   while (u < u1) {
     const uint32_t t = u / ut, ue = std::min(u1, (t + 1) * ut);
@@ -313,10 +324,9 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (; u < ue; ++u) {
       const Src nxt = src(u + 1);
-      step(l0, s0, l3, s3, cur, 3);
-      step(l1, s1, l0, s0, nxt, 0);
-      step(l2, s2, l1, s1, nxt, 1);
-      step(l3, s3, l2, s2, nxt, 2);
+      step(ls[0], ss[0], ls[NS - 1], ss[NS - 1], cur, NS - 1);
+#pragma unroll
+      for (int i = 1; i < NS; ++i) step(ls[i], ss[i], ls[i - 1], ss[i - 1], nxt, i - 1);
       cur = nxt;
     }
     float* o = P + ((int64_t)t * cmax + (g - sk_owner(t * ut, U, G))) * (128 * 64);
@@ -435,21 +445,42 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
   }
 }
 
-// sT [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r].
-__global__ void split_saved_kernel(const float* __restrict__ T, int64_t M, int64_t Mp, int r, int64_t Rp,
-                                   float scale, uint16_t* __restrict__ sT, uint16_t* __restrict__ sTT) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Mp * Rp) return;
-  const int64_t mblk = idx / (64 * Rp), rem = idx % (64 * Rp);
-  const int64_t j = rem / 64, m = mblk * 64 + rem % 64;
-  uint16_t hi = 0, lo = 0;
-  if (m < M) {
-    if (j < r) split_hilo(__fmul_rn(scale, T[m * r + j]), hi, lo);
-    sT[m * 2 * Rp + j] = hi;
-    sT[m * 2 * Rp + Rp + j] = lo;
+// The backward pass's operand copies in one launch.  Blocks [0, b1): sT
+// [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r] (no
+// blocks when T is null); [b1, b2): BT [Rp, Np] = Bᵀ zero-padded; [b2, ...):
+// AT2 [K, 2Rp], AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r, else 0.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ T, int64_t M, int64_t Mp,
+                                                       int r, int64_t Rp, float scale, uint16_t* __restrict__ sT,
+                                                       uint16_t* __restrict__ sTT, const uint16_t* __restrict__ B,
+                                                       int64_t N, int64_t Np, uint16_t* __restrict__ BT,
+                                                       const uint16_t* __restrict__ A, int64_t K,
+                                                       uint16_t* __restrict__ AT2, unsigned b1, unsigned b2) {
+  const unsigned b = blockIdx.x;
+  if (b < b1) {
+    const int64_t idx = (int64_t)b * 256 + threadIdx.x;
+    if (idx >= Mp * Rp) return;
+    // m runs fastest inside blocks of 64 so that the transposed stores coalesce
+    const int64_t mblk = idx / (64 * Rp), rem = idx % (64 * Rp);
+    const int64_t j = rem / 64, m = mblk * 64 + rem % 64;
+    uint16_t hi = 0, lo = 0;
+    if (m < M) {
+      if (j < r) split_hilo(__fmul_rn(scale, T[m * r + j]), hi, lo);
+      sT[m * 2 * Rp + j] = hi;
+      sT[m * 2 * Rp + Rp + j] = lo;
+    }
+    sTT[j * Mp + m] = hi;
+    sTT[(Rp + j) * Mp + m] = lo;
+  } else if (b < b2) {
+    const int64_t idx = (int64_t)(b - b1) * 256 + threadIdx.x;
+    if (idx >= Rp * Np) return;
+    const int64_t j = idx / Np, n = idx % Np;
+    BT[idx] = (j < r && n < N) ? B[n * r + j] : (uint16_t)0;
+  } else {
+    const int64_t idx = (int64_t)(b - b2) * 256 + threadIdx.x;
+    if (idx >= K * 2 * Rp) return;
+    const int64_t k = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
+    AT2[idx] = j < r ? A[j * K + k] : (uint16_t)0;
   }
-  sTT[j * Mp + m] = hi;
-  sTT[(Rp + j) * Mp + m] = lo;
 }
 
 // Zeros of the adapter gradients when there are no tokens.
@@ -458,25 +489,16 @@ __global__ void zero_kernel(float* __restrict__ a, int64_t n) {
   if (idx < n) a[idx] = 0.0f;
 }
 
-// BT [Rp, Np] = Bᵀ for j < r, n < N; zeros elsewhere.  B is [N, r].
-__global__ void transpose_lora_b_kernel(const uint16_t* __restrict__ B, int64_t N, int64_t Np, int r,
-                                        int64_t Rp, uint16_t* __restrict__ BT) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= Rp * Np) return;
-  const int64_t j = idx / Np, n = idx % Np;
-  BT[idx] = (j < r && n < N) ? B[n * r + j] : (uint16_t)0;
-}
-
 unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
 // Stream-K plan of a product with `tiles` output tiles of `ns` stages each.
-SkPlan sk_plan(int64_t tiles, int64_t ns, int jt) {
+SkPlan sk_plan(int64_t tiles, int64_t ns, int jt, int ring) {
   SkPlan p{};
   p.jt = jt;
   p.tiles = tiles;
-  p.ut = (uint32_t)std::max<int64_t>(1, (ns + NSTAGE - 1) / NSTAGE);
+  p.ut = (uint32_t)std::max<int64_t>(1, (ns + ring - 1) / ring);
   p.U = (uint32_t)(tiles * p.ut);
   p.G = std::min<uint32_t>(p.U, kSkWorkgroups);
   p.cmax = 1;
@@ -490,11 +512,11 @@ SkPlan sk_plan(int64_t tiles, int64_t ns, int jt) {
 
 SkPlan rowred_plan(int64_t M, int64_t Kred, int64_t Rp) {
   const int jt = (int)cdiv(Rp, 64);
-  return sk_plan((int64_t)cdiv(M, 64) * jt, cdiv(Kred, ST), jt);
+  return sk_plan((int64_t)cdiv(M, 64) * jt, cdiv(Kred, ST), jt, kRowRing);
 }
 SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp) {
   const int jt = (int)cdiv(Rp, 64);
-  return sk_plan((int64_t)cdiv(Pn, 128) * jt, cdiv(Mred, ST), jt);
+  return sk_plan((int64_t)cdiv(Pn, 128) * jt, cdiv(Mred, ST), jt, kColRing);
 }
 size_t rowred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 64 * 64 * 4; }
 size_t colred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 128 * 64 * 4; }
@@ -527,23 +549,20 @@ hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int
   return hipGetLastError();
 }
 
-hipError_t launch_split_saved(const float* T, int64_t M, int32_t r, int64_t Rp, float scale,
-                              uint16_t* sT, uint16_t* sTT, hipStream_t st) {
-  const int64_t Mp = lora_mp(M);
-  split_saved_kernel<<<cdiv(Mp * Rp, 256), 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT);
+hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, float scale, uint16_t* sT,
+                           uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
+                           int64_t K, uint16_t* AT2, hipStream_t st) {
+  const int64_t Mp = lora_mp(M), Np = round_up(N, 64);
+  const unsigned b1 = T ? cdiv(Mp * Rp, 256) : 0u;
+  const unsigned b2 = b1 + cdiv(Rp * Np, 256);
+  const unsigned b3 = b2 + cdiv(K * 2 * Rp, 256);
+  bwd_prep_kernel<<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
   return hipGetLastError();
 }
 
 hipError_t launch_zero(float* a, int64_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   zero_kernel<<<cdiv(n, 256), 256, 0, st>>>(a, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp, uint16_t* BT,
-                                   hipStream_t st) {
-  const int64_t Np = round_up(N, 64);
-  transpose_lora_b_kernel<<<cdiv(Rp * Np, 256), 256, 0, st>>>(B, N, Np, r, Rp, BT);
   return hipGetLastError();
 }
 
