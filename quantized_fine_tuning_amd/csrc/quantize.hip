@@ -20,6 +20,8 @@
 //                         s = max / 448, e = E4M3(d / s).
 //   nf4_dequant_kernel    32 elements per thread, 16-byte loads of codes,
 //                         64-byte contiguous stores of bf16.
+#include <type_traits>
+
 #include "host.h"
 
 namespace qnf4 {
@@ -41,6 +43,59 @@ struct QTraits<uint16_t> {
   __device__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
 };
 
+// Codes through a table.  code(x) = #{j : x > t_j} for the sorted fp32
+// thresholds t_0 < ... < t_14; every |t_j| > 2^-5, so |x| < 2^-5 has the zero
+// code 7.  For 2^-5 <= |x| <= 1, cut each binade [2^e, 2^(e+1)) of |x| into
+// 8 cells by the top 3 mantissa bits (bits 20..30 of |x| index the cell):
+// 41 cells per sign, and no cell holds more than one threshold (checked
+// where the codebook is built).  Cell c of a sign stores base = the count of
+// thresholds below the whole cell and t* = the threshold inside it (or +inf):
+// code(x) = base + (x > t*).  Cell 0 of each sign covers |x| < 2^-5 (base
+// 7, t* = +inf).  Table: 42 cells for x >= 0, then 42 for x < 0.
+constexpr int kCodeCells = 42;
+constexpr int kCellBias = (122 << 3) - 1;  // bits 20..30 of 2^-5, minus one
+__device__ __forceinline__ uint2 code_cell(int c, const Codebook& cb) {
+  const int neg = c / kCodeCells, i = c % kCodeCells;
+  if (i == 0) return make_uint2(0x7f800000u, 7u);
+  const float lo = __uint_as_float((uint32_t)(kCellBias + i) << 20);
+  const float hi = __uint_as_float((uint32_t)(kCellBias + i + 1) << 20);
+  uint32_t base = 0;
+  float tstar = __int_as_float(0x7f800000);  // +inf
+  for (int j = 0; j < 15; ++j) {
+    const float t = cb.t[j];
+    if (!neg) {  // cell [lo, hi)
+      if (t < lo) ++base;
+      else if (t < hi) tstar = t;
+    } else {  // cell (-hi, -lo]
+      if (t <= -hi) ++base;
+      else if (t <= -lo) tstar = t;
+    }
+  }
+  return make_uint2(__float_as_uint(tstar), base);
+}
+// table index of x (no branch: |x| < 2^-5 clamps to cell 0)
+__device__ __forceinline__ int code_cell_index(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const int mag = max((int)((u & 0x7fffffffu) >> 20) - kCellBias, 0);
+  return mag + (int)(u >> 31) * kCodeCells;
+}
+
+// max over the aligned group of LPB lanes (LPB = 8 or 16) of non-negative
+// floats, as integers (same order), with DPP lane moves: xor 1 and 2 within
+// quads, then mirrors within half rows and rows
+template <int LPB>
+__device__ __forceinline__ float group_max(float m) {
+  uint32_t v = __float_as_uint(m);
+  auto mv = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, decltype(ctrl)::value, 0xf, 0xf, false);
+  };
+  v = max(v, mv(v, std::integral_constant<int, 0xB1>()));   // quad_perm [1,0,3,2]
+  v = max(v, mv(v, std::integral_constant<int, 0x4E>()));   // quad_perm [2,3,0,1]
+  v = max(v, mv(v, std::integral_constant<int, 0x141>()));  // row_half_mirror
+  if constexpr (LPB == 16) v = max(v, mv(v, std::integral_constant<int, 0x140>()));  // row_mirror
+  return __uint_as_float(v);
+}
+
 template <typename WT>
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict__ W, int64_t nb,
                                                            uint8_t* __restrict__ codes,
@@ -52,27 +107,26 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
   constexpr int BPW = 64 / LPB;          // blocks per wave per iteration
   constexpr int BPI = 4 * BPW;           // blocks per workgroup per iteration
   constexpr int ITERS = kChunkBlocks / BPI;
-  typedef uint32_t load_t __attribute__((ext_vector_type(4)));
+  static_assert(LPB == 8 || LPB == 16, "lanes per block");
 
   __shared__ float s_c[kChunkBlocks];
   __shared__ double s_w[4];
+  __shared__ uint2 s_tab[2 * kCodeCells];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int sub = lane % LPB, bl = lane / LPB;
   const int64_t chunk0 = (int64_t)blockIdx.x * kChunkBlocks;
 
-  // issue every load of the chunk first
-  load_t raw[ITERS];
+  // issue every load of the chunk first (buffer loads: blocks past the
+  // tensor read as zeros)
+  const rsrc_t rw = make_rsrc(W + chunk0 * kBlock, (nb - chunk0) * kBlock * (int64_t)sizeof(WT));
+  const uint32_t voff = (uint32_t)(((wave * BPW + bl) * kBlock + sub * EPL) * sizeof(WT));
+  u32x4_t raw[ITERS];
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int64_t b = chunk0 + it * BPI + wave * BPW + bl;
-    if (b < nb) {
-      raw[it] = *reinterpret_cast<const load_t*>(W + b * kBlock + sub * EPL);
-    } else {
-      raw[it] = load_t{0u, 0u, 0u, 0u};
-    }
-  }
+  for (int it = 0; it < ITERS; ++it) raw[it] = buf_load16(rw, voff, (uint32_t)(it * BPI * kBlock * sizeof(WT)));
+  if (tid < 2 * kCodeCells) s_tab[tid] = code_cell(tid, cb);
+  __syncthreads();
 
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -87,21 +141,32 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
       w[i] = QTraits<WT>::to_f32(v[i]);
       m = fmaxf(m, fabsf(w[i]));
     }
-#pragma unroll
-    for (int o = LPB / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    m = group_max<LPB>(m);
 
-    uint32_t packed = 0;
+    // x = fl32(w / m), the correctly rounded quotient, from one correctly
+    // rounded reciprocal per block: q = w·y, then two residual corrections
+    // r = w - q·m (exact with an FMA), q = q + r·y.  After the first, q is
+    // within an ulp of w/m; with y = fl32(1/m) the second then gives the
+    // correctly rounded quotient (Markstein's theorem).  A block with a tiny
+    // absmax is scaled by 2^64 first (exact) so that y stays finite, and an
+    // all-zero block divides by 1 (every x is 0: the zero code).
+    const float sc = m < 0x1p-100f ? 0x1p64f : 1.0f;
+    const float den = m != 0.0f ? m * sc : 1.0f;
+    const float y = 1.0f / den;
+    float x[EPL];
+    uint2 cell[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      uint32_t code = 7u;
-      if (m != 0.0f) {
-        const float x = w[i] / m;  // one correctly rounded fp32 division
-        code = 0u;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) code += (x > cb.t[j]) ? 1u : 0u;
-      }
-      packed |= code << (4 * i);
+      const float ws = w[i] * sc;
+      float q = ws * y;
+      q = __builtin_fmaf(__builtin_fmaf(-q, den, ws), y, q);
+      x[i] = __builtin_fmaf(__builtin_fmaf(-q, den, ws), y, q);
+      cell[i] = s_tab[code_cell_index(x[i])];
     }
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      packed |= (cell[i].y + (x[i] > __uint_as_float(cell[i].x) ? 1u : 0u)) << (4 * i);
     if (b < nb) {
       uint8_t* dst = codes + b * (kBlock / 2) + sub * (EPL / 2);
       if constexpr (EPL == 4) {
@@ -111,7 +176,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
       }
       if (sub == 0) absmax[b] = m;
     }
-    if (sub == 0) s_c[local] = (b < nb) ? m : 0.0f;
+  if (sub == 0) s_c[local] = (b < nb) ? m : 0.0f;
   }
   __syncthreads();
 

@@ -71,6 +71,37 @@ def test_edge_values():
     check_full(W, G.dev_f32(W))
 
 
+def test_quotients_at_thresholds():
+    # x = fl32(w / m) lands on or next to every decision threshold, for block
+    # maxima spread over binades (including just below powers of two and
+    # tiny ones): the codes depend on the quotient being correctly rounded
+    q = nf4.codebook()
+    t = nf4.thresholds(q).astype(np.float32)
+    rng = np.random.default_rng(123)
+    maxima = [np.float32(1.0), np.float32(np.nextafter(np.float32(2.0), np.float32(0))),
+              np.float32(0.75), np.float32(3.0e-3), np.float32(np.nextafter(np.float32(0.5), np.float32(0))),
+              np.float32(1e-30), np.float32(2.0 ** -120), np.float32(12345.678)]
+    maxima += [np.float32(v) for v in rng.uniform(1e-3, 10.0, 24)]
+    rows = []
+    for m in maxima:
+        for j in range(15):
+            target = np.float32(t[j] * np.float64(m))
+            blk = []
+            for d in range(-2, 3):  # w = fl32(t_j * m) moved by -2..2 ulps
+                v = target
+                for _ in range(abs(d)):
+                    v = np.nextafter(v, np.float32(np.inf if d > 0 else -np.inf))
+                blk.append(v)
+            blk = np.array(blk, dtype=np.float32)
+            row = np.zeros(64, dtype=np.float32)
+            row[0] = m  # the block maximum
+            row[1:1 + len(blk)] = np.clip(blk, -m, m)
+            rows.append(row)
+    W = np.stack(rows).reshape(-1, 256)
+    print(f"quotients at thresholds: {W.size // 64} blocks", flush=True)
+    check_full(W, G.dev_f32(W))
+
+
 def test_mlp_weight_sampled():
     # full-size 11008x4096 fp32 weight: mean, all constants and scales exact;
     # codes and dequantized values exact on 64 sampled weight rows
