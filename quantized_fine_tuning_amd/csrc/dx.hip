@@ -14,14 +14,14 @@
 //     transposed bf16 tile Ŵᵀ[k][n] in LDS; then wave (wm, wk) multiplies
 //     token rows [128wm, +128) by columns [64wk, +64): 64
 //     v_mfma_f32_16x16x32_bf16 per wave and step, operands read from LDS.
-//   * Dequantization goes through a per-row table: lane t writes the 16
-//     values RNE_bf16(fl32(q_j * c')) of weight row t (its block's scaled
-//     codebook) to LDS; lane (rg, cg) then owns rows 8rg..8rg+7 by columns
-//     4cg..4cg+3 of the wave's slice, each code one 2-byte table read, and
-//     packs 8 consecutive rows of one column into one 16-byte store: the
-//     values come out already transposed.  Table slots, tile swizzles and
-//     lane maps are chosen so that lookups, stores and fragment reads are
-//     free of LDS bank conflicts (32 banks of 4 bytes).
+//   * Dequantization goes through a per-row table: for each weight row of
+//     the step one lane writes the 16 values RNE_bf16(fl32(q_j * c')) (its
+//     block's scaled codebook) to LDS; lane (rg, cg) then owns rows
+//     8rg..8rg+7 by columns 4cg..4cg+3 of the wave's slice, each code one
+//     2-byte table read, and packs 8 consecutive rows of one column into one
+//     16-byte store: the values come out already transposed.  Table slots,
+//     tile swizzles and lane maps are chosen so that lookups, stores and
+//     fragment reads are free of LDS bank conflicts (32 banks of 4 bytes).
 //   * dY and the weight data of the next steps are loaded into registers at
 //     the top of an iteration and stored to LDS at its end; the MFMAs of
 //     step s are interleaved in issue order with the dequantization of step
