@@ -22,12 +22,13 @@
 //     16-byte store: the values come out already transposed.  Table slots,
 //     tile swizzles and lane maps are chosen so that lookups, stores and
 //     fragment reads are free of LDS bank conflicts (32 banks of 4 bytes).
-//   * dY and the weight data of the next steps are loaded into registers at
-//     the top of an iteration and stored to LDS at its end; the MFMAs of
-//     step s are interleaved in issue order with the dequantization of step
-//     s+1 into the other Ŵᵀ buffer, in the first half of the step for one
-//     wave of each SIMD and in the second half for the other.  Rows past N
-//     get an all-zero table.
+//   * The dY tile of the next step is copied straight into LDS; the weight
+//     data of the step after is loaded into registers at the top of an
+//     iteration and stored to LDS at its end.  The MFMAs of step s are
+//     interleaved in issue order with the dequantization of step s+1 into the
+//     other Ŵᵀ buffer, in the first half of the step for one wave of each
+//     SIMD and in the second half for the other.  Rows past N get an all-zero
+//     table.
 //   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
 //     AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A), both
 //     copied straight into LDS.

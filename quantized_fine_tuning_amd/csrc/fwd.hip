@@ -20,13 +20,13 @@
 //     groups of 8 of the 32 banks, so lookups never conflict.
 //   * Tiles are stored with 16-byte chunks XOR-swizzled by row (xswz) so that
 //     MFMA operand reads of 8 rows cover the 32 LDS banks once.
-//   * X and the weight data (packed codes, e4m3 bytes, group scales) of the
-//     next steps are loaded into registers at the top of an iteration and
-//     stored to LDS at its end, so no loaded register lives across
-//     iterations; the MFMAs of step s are interleaved in issue order with
-//     the dequantization of step s+1 into the other Ŵ buffer, in the first
-//     half of the step for one wave of each SIMD and in the second half for
-//     the other.
+//   * The X tile of the next step is copied straight into LDS; the weight
+//     data (packed codes, e4m3 bytes, group scales) of the step after is
+//     loaded into registers at the top of an iteration and stored to LDS at
+//     its end, so no loaded register lives across iterations.  The MFMAs of
+//     step s are interleaved in issue order with the dequantization of step
+//     s+1 into the other Ŵ buffer, in the first half of the step for one wave
+//     of each SIMD and in the second half for the other.
 //   * All operand reads are buffer loads whose resources end at the tensor's
 //     last row, so ragged tiles read zeros without per-lane branches.
 //   * The LoRA up-projection is 2*Rp/64 extra reduction steps whose A operand
