@@ -33,6 +33,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -60,11 +61,19 @@ KERNEL_SOURCES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_mlp7b.txt")
 
 
+def _code_only(text):
+    """The source without comments and blank space, so that edits of comments
+    do not count as changes of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(kernel):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "quantized_fine_tuning_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_fine_tuning_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
