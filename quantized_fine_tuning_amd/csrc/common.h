@@ -154,6 +154,15 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ uint16_t lds_read_u16(uint32_t a) {
   return *(const lds_u16_t*)(uintptr_t)a;
 }
+// v = hi + lo with hi = RNE_bf16(v) and lo = RNE_bf16(v - hi): the pair
+// carries about 16 significant bits of an fp32 value into bf16 products.
+__device__ __forceinline__ void split_hilo(float v, uint16_t& hi, uint16_t& lo) {
+  const uint32_t h = pack_bf16x2(v, 0.0f) & 0xffffu;
+  const float rem = __fsub_rn(v, __uint_as_float(h << 16));
+  hi = (uint16_t)h;
+  lo = (uint16_t)(pack_bf16x2(rem, 0.0f) & 0xffffu);
+}
+
 // Returns x unchanged, but hides where it came from: values derived from it
 // are computed where they are used instead of being hoisted out of a loop,
 // where each would hold a register for the whole loop.

@@ -6,8 +6,9 @@
 // once, keeps as many bytes in flight as possible and everything else small.
 //
 //   lora_down_small_kernel  T = X·Aᵀ (M x r, fp32) for one 16-wide slice of r
-//                           per workgroup: 8 waves split K, MFMA products,
-//                           fixed-order combination of the 8 partial tiles.
+//                           per workgroup: 16 waves split K, all loads issued
+//                           first, MFMA products, fixed-order combination of
+//                           the 16 partial tiles.
 //   gemv_kernel             one workgroup of 16 waves per 16 weight rows.  Lane
 //                           (row l % 16, q = l / 16) owns whole NF4 blocks (64
 //                           codes, one decoded constant c'); a "block group" is
@@ -20,17 +21,24 @@
 //                           group are loaded before the current one is
 //                           dequantized.  Each value is RNE_bf16(fl32(q_c * c'))
 //                           with q_c read from a 16-entry LDS codebook (one
-//                           address per code: no bank conflicts).  The 16
-//                           partial tiles are combined in a fixed order and
-//                           s·Σ_j T[m][j]·B[n][j] is added in fp32, one
+//                           address per code: no bank conflicts).  The LoRA
+//                           term s·T·Bᵀ is 2 MFMAs per 32 ranks in wave 0 (A
+//                           operand the bf16 hi/lo split of s·T), and the 16
+//                           partial tiles are combined in a fixed order, one
 //                           thread per output.
 #include "host.h"
 
 namespace qnf4 {
 namespace {
 
-constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kWaves = 16, kThreads = 64 * kWaves;
+constexpr int kDownSteps = 8;  // 32-wide K steps per wave and pass
 
+// T = X·Aᵀ (M x r, fp32) for one 16-wide slice of r per workgroup of 16
+// waves.  Wave w takes the 32-wide K steps w, w + 16, ...; each pass issues
+// the loads of 8 steps before their MFMAs (for K = 4096 one pass: every load
+// of the kernel is in flight at once).  The 16 partial tiles are combined in
+// a fixed order.
 __global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_t* __restrict__ X,
                                                                    int M, int64_t K,
                                                                    const uint16_t* __restrict__ A,
@@ -45,19 +53,19 @@ __global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_
   const rsrc_t ra = make_rsrc(A + (int64_t)j0 * K, (int64_t)(r - j0) * K * 2);
   const uint32_t vx = (uint32_t)((lr * K + 8 * kq) * 2);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // 32-wide steps st = wave, wave + 8, ...: lane slot kq holds k = 32st + 8kq..
+  // lane slot kq of step st holds k = 32st + 8kq .. +7
   const int64_t nst = K / 32;
-  for (int64_t st0 = wave; st0 < nst; st0 += 8 * 4) {
-    u32x4_t xa[4], ab[4];
+  for (int64_t st0 = wave; st0 < nst; st0 += (int64_t)kWaves * kDownSteps) {
+    u32x4_t xa[kDownSteps], ab[kDownSteps];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t st = st0 + 8 * u;
+    for (int u = 0; u < kDownSteps; ++u) {
+      const int64_t st = st0 + (int64_t)kWaves * u;
       const uint32_t off = st < nst ? (uint32_t)(st * 64) : 0x7fffffffu;  // past the end: zero
       xa[u] = buf_load16(rx, vx, off);
       ab[u] = buf_load16(ra, vx, off);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma_16x16x32(xa[u], ab[u], acc);
+    for (int u = 0; u < kDownSteps; ++u) acc = mfma_16x16x32(xa[u], ab[u], acc);
   }
   s_acc[wave][lane] = acc;
   __syncthreads();
@@ -89,9 +97,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
                                                             int y_bf16, Codebook cb) {
   __shared__ float sq[16];
   __shared__ f32x4_t s_acc[kGemvWaves][64];
-  // the LoRA epilogue's operands: T (M x r fp32) and the 16 rows of B (bf16)
-  __shared__ float sT[16 * 256];
-  __shared__ uint16_t sB[16 * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t K = W.K, N = W.N;
@@ -147,20 +152,54 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     }
   };
 
-  // Everything this workgroup reads from memory is requested up front: the
-  // first block group of every wave, then T and the B rows (used only by the
-  // epilogue, stored to LDS after the main loop).
-  Group ga, gb;
-  load(ga, wave);
+  // The LoRA term s·T·Bᵀ enters wave 0's accumulator as extra MFMAs over
+  // the rank in steps of 32: A operand the bf16 hi/lo split of s·T (token
+  // row lr), B operand the workgroup's B rows (weight row lr); ranks past r
+  // and tokens past M read as zero.
   const rsrc_t rt = make_rsrc(T, (int64_t)M * r * 4);
   const rsrc_t rb = make_rsrc(B + n0 * r, (N - n0) * r * 2);
-  float tv[4];  // M*r and 16*r are at most 4096 = 4 per thread
-  uint32_t bv[4];
+  struct Lora {
+    float t[8];
+    uint32_t b[8];
+  };
+  auto lora_load = [&](Lora& l, int js) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = tid + u * kGemvThreads;
-    tv[u] = __uint_as_float(buf_load4(rt, i < M * r ? 4u * i : 0x7fffffffu, 0u));
-    bv[u] = buf_load2(rb, i < GEMV_ROWS * r ? 2u * i : 0x7fffffffu, 0u);
+    for (int e = 0; e < 8; ++e) {
+      const int j = 32 * js + 8 * kq + e;
+      l.t[e] = __uint_as_float(buf_load4(rt, (x_row && j < r) ? (uint32_t)((lr * r + j) * 4) : 0x7fffffffu, 0u));
+      l.b[e] = buf_load2(rb, j < r ? (uint32_t)((lr * r + j) * 2) : 0x7fffffffu, 0u);
+    }
+  };
+  auto lora_mfma = [&](const Lora& l) __attribute__((always_inline)) {
+    u32x4_t hi, lo, bf;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint16_t h0, l0, h1, l1;
+      split_hilo(__fmul_rn(scale, l.t[2 * p]), h0, l0);
+      split_hilo(__fmul_rn(scale, l.t[2 * p + 1]), h1, l1);
+      hi[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      bf[p] = (l.b[2 * p] & 0xffffu) | (l.b[2 * p + 1] << 16);
+    }
+    acc = mfma_16x16x32(hi, bf, acc);
+    acc = mfma_16x16x32(lo, bf, acc);
+  };
+  const int rsteps = (r + 31) / 32;
+
+  // Everything this workgroup reads from memory is requested up front: the
+  // first block group of every wave and, in wave 0, the LoRA operands, whose
+  // MFMAs wave 0 issues before its main loop (their registers are free again
+  // by then).
+  Group ga, gb;
+  load(ga, wave);
+  if (wave == 0) {
+    for (int js = 0; js < rsteps; js += 2) {
+      Lora la[2];
+      lora_load(la[0], js);
+      if (js + 1 < rsteps) lora_load(la[1], js + 1);
+      lora_mfma(la[0]);
+      if (js + 1 < rsteps) lora_mfma(la[1]);
+    }
   }
   if (tid < 16) sq[tid] = cb.q[tid];
   __syncthreads();  // codebook
@@ -177,17 +216,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     __builtin_amdgcn_sched_barrier(0);
     consume(gb);
   }
-
   s_acc[wave][lane] = acc;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = tid + u * kGemvThreads;
-    if (i < M * r) sT[i] = tv[u];
-    if (i < GEMV_ROWS * r) sB[i] = (uint16_t)bv[u];
-  }
   __syncthreads();
   // one thread per output (token m, weight row n0 + c): the 16 partial tiles
-  // in a fixed order, then s·Σ_j T[m][j]·B[n][j]
+  // in a fixed order
   if (tid < 16 * GEMV_ROWS) {
     const int m = tid >> 4, c = tid & 15;
     const int64_t nn = n0 + c;
@@ -196,9 +228,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
       float y = s_acc[0][16 * (m >> 2) + c][m & 3];
 #pragma unroll
       for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
-      float l = 0.0f;
-      for (int j = 0; j < r; ++j) l = __fadd_rn(l, __fmul_rn(sT[m * r + j], bf16_to_f32(sB[c * r + j])));
-      y = __fadd_rn(y, __fmul_rn(scale, l));
       if (y_bf16)
         static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
       else

@@ -56,13 +56,6 @@ __device__ __forceinline__ void wait_stage() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void split_hilo(float v, uint16_t& hi, uint16_t& lo) {
-  const uint32_t h = pack_bf16x2(v, 0.0f) & 0xffffu;
-  const float rem = __fsub_rn(v, __uint_as_float(h << 16));
-  hi = (uint16_t)h;
-  lo = (uint16_t)(pack_bf16x2(rem, 0.0f) & 0xffffu);
-}
-
 // ---------------------------------------------------------------------------
 // Work split (stream-K).  A product has `tiles` output tiles, each a
 // reduction of ns stages, cut into units of NS stages, NS the depth of the
