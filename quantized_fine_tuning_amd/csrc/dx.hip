@@ -105,10 +105,12 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   const uint32_t vy = (uint32_t)(((tid >> 3) * N + 8 * ylch) * 2);
   const uint32_t y_gstride = (uint32_t)(64 * N * 2);
   const i32x4_t ryw = rsrc_words(dY + m0 * N, (M - m0) * N * 2);
+  auto copy_y_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
+    dma_lds16(ryw, t + 64 * c * 128 + 1024 * wave, vy + c * y_gstride, (uint32_t)s * 128u);
+  };
   auto copy_y = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      dma_lds16(ryw, t + 64 * c * 128 + 1024 * wave, vy + c * y_gstride, (uint32_t)s * 128u);
+    for (int c = 0; c < 4; ++c) copy_y_part(t, s, c);
   };
   auto sab = [&](int i) { return i ? sa1 : sa0; };
   // LoRA tiles copied straight into LDS: wave w copies rows 32w + 8c + (i >> 3),
@@ -257,13 +259,14 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // The two waves of a SIMD (w and w + 4, i.e. wm = 0 and 1) dequantize in
   // different halves of the step (phase P = wm): while one issues table
   // arithmetic and lookups, the other issues MFMAs.
-  auto mfma_step_dequant = [&](auto P, const char* ya, const char* wb, int t, char* dst)
-      __attribute__((always_inline)) {
+  auto mfma_step_dequant = [&](auto P, const char* ya, const char* wb, int t, char* dst,
+                               auto&& after_group) __attribute__((always_inline)) {
     constexpr int g0 = decltype(P)::value ? 8 : 0;
     u32x4_t cw;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       mfma_group(ya, wb, g);
+      after_group(g);
       if (g == g0) {
         build_table(t);
         cw = read_codes();
@@ -303,13 +306,25 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // of step nsteps may be loaded: its reads stay inside the buffers or
   // return zeros, and it is not used.  The loop is instantiated once per
   // phase.
+  // Global reads queue behind one another in the compute unit's memory
+  // pipeline, and a wave cannot issue past a read that does not fit: the
+  // waves that dequantize first issue theirs at the top, the others one
+  // after each of their first MFMA groups.
   auto main_loop = [&](auto P) __attribute__((always_inline)) {
+    constexpr bool early = decltype(P)::value == 0;
 #pragma unroll 1
     for (int s = 0; s + 1 < nsteps; ++s) {
       WRegs wr;
-      copy_y(sab((s + 1) & 1), s + 1);
-      load_w(wr, s + 2);
-      mfma_step_dequant(P, sab(s & 1), sw[s & 1], s + 1, sw[(s + 1) & 1]);
+      if constexpr (early) {
+        copy_y(sab((s + 1) & 1), s + 1);
+        load_w(wr, s + 2);
+      }
+      mfma_step_dequant(P, sab(s & 1), sw[s & 1], s + 1, sw[(s + 1) & 1], [&](int g) {
+        if constexpr (!early) {
+          if (g < 4) copy_y_part(sab((s + 1) & 1), s + 1, g);
+          if (g == 4) load_w(wr, s + 2);
+        }
+      });
       store_w(wr);
       wait_vmem();
       __syncthreads();

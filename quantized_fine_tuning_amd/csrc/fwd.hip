@@ -4,29 +4,31 @@
 // matmul and the LoRA path is added to the output.)
 //
 // Design
-//   * 256x256 output tile per workgroup of 8 waves, two per SIMD: while one
-//     wave of a SIMD issues MFMAs the other can issue its dequantization
-//     arithmetic (within one wave the two largely serialize).
-//   * Per 64-wide reduction step every wave dequantizes 32 of the tile's 256
-//     weight rows into a shared bf16 tile Ŵ[n][k] in LDS; then wave (wm, wn)
-//     multiplies token rows [128wm, +128) by weight rows [64wn, +64): 64
-//     v_mfma_f32_16x16x32_bf16 per wave and step, operands read from LDS.
-//   * Dequantization goes through a per-row table: lane t < 32 writes the 16
-//     values RNE_bf16(fl32(q_j * c')) of row t to LDS, and every code is one
-//     2-byte table read (bit-identical to multiplying per element, since the
-//     value depends only on code and row).  Lane l reads rows 8q + (l >> 3),
-//     k = 8(l & 7) + 0..7: the 8 lanes of one row hit its table, and the 4
-//     rows of each half-wave (served in one LDS cycle) hit 4 different
-//     groups of 8 of the 32 banks, so lookups never conflict.
+//   * 256x256 output tile per workgroup of 12 waves, three per SIMD, in two
+//     roles.  Waves 0..7 only multiply: wave (wm, wn) owns token rows
+//     [128wm, +128) and weight rows [64wn, +64) of the tile, 64
+//     v_mfma_f32_16x16x32_bf16 per 64-wide reduction step, operands read
+//     from LDS one MFMA group ahead.  Waves 8..11 (one per SIMD) produce the
+//     operands: each copies a quarter of the next step's X tile straight
+//     into LDS and dequantizes 64 of the tile's 256 weight rows of the next
+//     step into the shared bf16 tile Ŵ[n][k].  The producers' table
+//     arithmetic, lookups and copies overlap the MFMAs of the other two
+//     waves of their SIMD instead of interrupting a wave's own MFMA stream.
+//   * Dequantization goes through a per-row table: lane t writes the 16
+//     values RNE_bf16(fl32(q_j * c')) of its row t to LDS, and every code is
+//     one 2-byte table read (bit-identical to multiplying per element, since
+//     the value depends only on code and row).  For row group q lane l reads
+//     rows 8q + (l >> 3), k = 8(l & 7) + 0..7: the 8 lanes of one row hit its
+//     table, and the 4 rows of each half-wave (served in one LDS cycle) hit 4
+//     different groups of 8 of the 32 banks.  The lookups of one row group
+//     are in flight while the previous group's values are packed and stored.
 //   * Tiles are stored with 16-byte chunks XOR-swizzled by row (xswz) so that
 //     MFMA operand reads of 8 rows cover the 32 LDS banks once.
-//   * The X tile of the next step is copied straight into LDS; the weight
-//     data (packed codes, e4m3 bytes, group scales) of the step after is
-//     loaded into registers at the top of an iteration and stored to LDS at
-//     its end, so no loaded register lives across iterations.  The MFMAs of
-//     step s are interleaved in issue order with the dequantization of step
-//     s+1 into the other Ŵ buffer, in the first half of the step for one wave
-//     of each SIMD and in the second half for the other.
+//   * The packed codes, e4m3 bytes and group scales of step s+2 are loaded
+//     while step s+1 is dequantized; codes go through LDS (each producer
+//     reads back only its own rows), constants stay in registers.
+//   * One barrier per step: after it the MFMA waves use X(s) and Ŵ(s) while
+//     the producers fill the other buffers with X(s+1) and Ŵ(s+1).
 //   * All operand reads are buffer loads whose resources end at the tensor's
 //     last row, so ragged tiles read zeros without per-lane branches.
 //   * The LoRA up-projection is 2*Rp/64 extra reduction steps whose A operand
@@ -44,9 +46,9 @@ namespace qnf4 {
 namespace {
 
 constexpr int TM = 256, TN = 256, KSTEP = 64;
-constexpr int kWaves = 8, kThreads = 64 * kWaves;
-
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+constexpr int kMfmaWaves = 8, kProdWaves = 4, kWaves = kMfmaWaves + kProdWaves;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kProdRows = TN / kProdWaves;  // weight rows per producer wave
 
 // A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
 // physical chunk c ^ (r & 7).  LDS has 32 banks of 4 bytes and serves a
@@ -65,259 +67,294 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
-  // per wave: tables of its 32 rows (row t at 32(t % 8) + 256(t / 8)), the
-  // packed codes of its rows (32 bytes each) and, per row, the dword holding
-  // its e4m3 byte and its group scale; code data double-buffered by step
-  __shared__ __attribute__((aligned(256))) char slut[kWaves][32 * 32];
-  __shared__ __attribute__((aligned(16))) char scode[2][kWaves][32 * 32];
-  __shared__ __attribute__((aligned(16))) uint32_t sconst[2][kWaves][2][32];
-  __shared__ float sq[16];
+  // per producer wave: tables of its 64 rows (row t at 32(t % 8) + 256(t / 8));
+  // packed codes of the tile's rows (32 bytes each), double-buffered by step
+  __shared__ __attribute__((aligned(256))) char slut[kProdWaves][kProdRows * 32];
+  __shared__ __attribute__((aligned(16))) char scode[2][TN * 32];
   int tmi, tni;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni)) return;
-  if (threadIdx.x < 16) sq[threadIdx.x] = cb.q[threadIdx.x];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, kq = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, n0 = (int64_t)tni * TN;
   const int ksteps = (int)(K / KSTEP);
+  auto sxb = [&](int i) { return i ? sx1 : sx0; };
+
+  if (wave < kMfmaWaves) {
+    // ---------------------------------------------------------------- MFMA
+    const int lr = lane & 15, kq = lane >> 4;
+    const int wm = wave >> 2, wn = wave & 3;
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA group g (0..15) of a step: k-half ks = g / 8, token block i = g % 8.
+    // A fragments are read one group ahead: group g first reads the A
+    // fragment of group g + 1, so the read's latency overlaps this group's
+    // MFMAs.  The B fragments of the second k-half are read right after the
+    // MFMAs of group 7.
+    const int arow = 128 * wm + lr, brow = 64 * wn + lr;
+    u32x4_t bfr[4], anext;
+    auto read_b = [&](const char* wb, int ks, u32x4_t* b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const u32x4_t*>(wb + xswz(brow + 16 * j, 2 * kq + ks));
+    };
+    auto read_a = [&](const char* xa, int g) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4_t*>(xa + xswz(arow + 16 * (g & 7), 2 * kq + (g >> 3)));
+    };
+    auto mfma_step = [&](const char* xa, const char* wb) __attribute__((always_inline)) {
+      read_b(wb, 0, bfr);
+      anext = read_a(xa, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const int i = g & 7;
+        const u32x4_t a = anext;
+        if (g < 15) anext = read_a(xa, g + 1);
+        // keep the reads ahead of the MFMAs (the scheduler would sink them
+        // below to reuse the fragment's registers)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+        if (g == 7) read_b(wb, 1, bfr);
+      }
+    };
+
+    __syncthreads();  // step 0 in place
+#pragma unroll 1
+    for (int s = 0; s < ksteps + LSTEPS; ++s) {
+      mfma_step(sxb(s & 1), sw[s & 1]);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds rows 128wm + 16i + 4kq + v of column 64wn + 16j + lr.
+    // The row/column bases go through an empty asm so that their address
+    // arithmetic is not hoisted above the main loop (it would stay live there).
+    int row0 = 128 * wm + 4 * kq, col0 = 64 * wn + lr;
+    asm volatile("" : "+v"(row0), "+v"(col0));
+    const bool full = (m0 + TM <= M) && (n0 + TN <= N);
+    if (y_bf16) {
+      uint16_t* Yb = static_cast<uint16_t*>(Y) + (m0 + row0) * N + n0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
+            if (full || (m < M && n < N))
+              Yb[(16 * i + v) * N + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
+          }
+    } else {
+      float* Yf = static_cast<float*>(Y) + (m0 + row0) * N + n0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
+            if (full || (m < M && n < N)) Yf[(16 * i + v) * N + 16 * j] = acc[i][j][v];
+          }
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------ producers
+  const int p = wave - kMfmaWaves;  // weight rows [64p, 64p + 64) of the tile
   const uint32_t kpr = (uint32_t)(K / kBlock);  // blocks per weight row
   const float mu = *W.mu;
 
   // Resources start at this tile's first row and end at the tensor's last
   // row: rows past M or N read as zero.  (Rows past M only feed output rows
   // past M, rows past N only output columns past N; neither is stored.)
-  const rsrc_t rx = make_rsrc(X + m0 * K, (M - m0) * K * 2);
   const rsrc_t rt = make_rsrc(sT + m0 * 2 * Rp, (M - m0) * 2 * Rp * 2);
   const rsrc_t rc = make_rsrc(W.codes + n0 * (K / 2), (N - n0) * (K / 2));
   const rsrc_t re = make_rsrc(W.e + n0 * kpr, (N - n0) * kpr);
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
 
-  // X tile, copied straight into LDS: thread τ moves 16 bytes of rows
-  // 64c + (τ >> 3), c = 0..3, into physical chunk τ & 7, so it fetches
-  // logical chunk (τ & 7) ^ ((τ >> 3) & 7) (row & 7 does not depend on c).
-  // LDS offset 64c*128 + 16τ: each wave's copy is 1 KB contiguous.
-  const int xlch = (tid & 7) ^ ((tid >> 3) & 7);
-  const uint32_t vx = (uint32_t)(((tid >> 3) * K + 8 * xlch) * 2);
-  const uint32_t x_gstride = (uint32_t)(64 * K * 2);
-  // (written as assembly: the compiler then inserts no wait for these copies
-  // in front of the LDS reads of the step; the wait before the step's
-  // closing barrier is explicit)
+  // X rows [64p, +64) of a step, copied straight into LDS: part c
+  // moves rows 64p + 8c + (l >> 3), lane l into physical chunk l & 7, so it
+  // fetches logical chunk (l & 7) ^ (l >> 3) (row & 7 = l >> 3).  Each
+  // instruction fills 1 KB of LDS contiguously.  (Written as assembly: the
+  // compiler then inserts no wait for these copies in front of the
+  // producer's own LDS reads; the wait before the step's closing barrier is
+  // explicit.)
+  const int xlch = (lane & 7) ^ (lane >> 3);
+  const uint32_t vx = (uint32_t)(((64 * p + (lane >> 3)) * K + 8 * xlch) * 2);
+  const uint32_t x_gstride = (uint32_t)(8 * K * 2);
   const i32x4_t rxw = rsrc_words(X + m0 * K, (M - m0) * K * 2);
+  auto copy_x_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
+    dma_lds16(rxw, t + (64 * p + 8 * c) * 128, vx + c * x_gstride, (uint32_t)s * 128u);
+  };
   auto copy_x = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      dma_lds16(rxw, t + 64 * c * 128 + 1024 * wave, vx + c * x_gstride, (uint32_t)s * 128u);
+    for (int c = 0; c < 8; ++c) copy_x_part(t, s, c);
   };
-  auto sxb = [&](int i) { return i ? sx1 : sx0; };
-  // LoRA tiles (sT rows, B2 rows) copied straight into LDS: wave w copies rows
-  // 32w + 8c + (i >> 3), c = 0..3, lane i into physical chunk i & 7, so it
-  // fetches logical chunk (i & 7) ^ (i >> 3).
-  const int llch = (lane & 7) ^ (lane >> 3);
-  const uint32_t vl = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * llch) * 2);
+  // LoRA tiles (sT rows, B2 rows), the same pattern over rows of 2Rp bf16.
+  const uint32_t vl = (uint32_t)(((64 * p + (lane >> 3)) * 2 * Rp + 8 * xlch) * 2);
   const uint32_t l_gstride = (uint32_t)(8 * 2 * Rp * 2);
   auto copy_lora = [&](rsrc_t r, char* t, int l) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      buf_load_lds16(r, t + (32 * wave + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
+    for (int c = 0; c < 8; ++c)
+      buf_load_lds16(r, t + (64 * p + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
   };
 
-  // Weight data of the wave's rows [32w, 32w+32) for step t: lane l loads 16
-  // code bytes of row l/2 (half l%2); lane l < 32 the dword holding the e4m3
-  // byte of row l and that row's group scale (lanes >= 32 repeat them).
-  const uint32_t vcd = (uint32_t)((32 * wave + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
-  const int crow = 32 * wave + (lane & 31);
-  const uint32_t ve_me = (uint32_t)crow * kpr;
-  const uint32_t blk_me = (uint32_t)(n0 + crow) * kpr;
+  // Weight data of row 64p + l for step t: its 32 code bytes, the dword
+  // holding its e4m3 byte and its group scale.
+  const int prow = kProdRows * p + lane;
+  const uint32_t vcd = (uint32_t)prow * (uint32_t)(K / 2);
+  const uint32_t ve_me = (uint32_t)prow * kpr;
+  const uint32_t blk_me = (uint32_t)(n0 + prow) * kpr;
   struct WRegs {
-    u32x4_t c;
+    u32x4_t c0, c1;
     uint32_t e, s;
   };
-  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
-    r.c = buf_load16(rc, vcd, (uint32_t)t * 32u);
+  auto load_codes = [&](WRegs& r, int t) __attribute__((always_inline)) {
+    r.c0 = buf_load16(rc, vcd, (uint32_t)t * 32u);
+    r.c1 = buf_load16(rc, vcd + 16u, (uint32_t)t * 32u);
+  };
+  auto load_consts = [&](WRegs& r, int t) __attribute__((always_inline)) {
     r.e = buf_load4(re, (ve_me + (uint32_t)t) & ~3u, 0u);
     r.s = buf_load4(rs, ((blk_me + (uint32_t)t) / kDqBlock) * 4u, 0u);
   };
-  auto store_w = [&](int slot, const WRegs& r) __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4_t*>(scode[slot][wave] + 16 * lane) = r.c;
-    if (lane < 32) {
-      sconst[slot][wave][0][lane] = r.e;
-      sconst[slot][wave][1][lane] = r.s;
-    }
+  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
+    load_codes(r, t);
+    load_consts(r, t);
+  };
+  auto store_codes = [&](int slot, const WRegs& r) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4_t*>(scode[slot] + 32 * prow) = r.c0;
+    *reinterpret_cast<u32x4_t*>(scode[slot] + 32 * prow + 16) = r.c1;
   };
 
-  // Dequantization of step t (weight data in slot) into the tile `dst`.
-  char* lut = slut[wave];
+  // Table of row 64p + lane for step t (constants in r).
+  char* lut = slut[p];
   const int dr = lane >> 3, dc = lane & 7;  // row 8q + dr of the wave, k-chunk dc
   const uint32_t lut_lane = lds_offset(lut) + (uint32_t)dr * 32u;
-  auto build_table = [&](int t, int slot) __attribute__((always_inline)) {
-    if (lane < 32) {
-      const uint32_t e = (sconst[slot][wave][0][lane] >> (8 * ((ve_me + (uint32_t)t) & 3u))) & 0xffu;
-      const float cp = decode_constant(e, __uint_as_float(sconst[slot][wave][1][lane]), mu);
-      u32x4_t t0, t1;
+  char* const tb_row = lut + 32 * (lane & 7) + 256 * (lane >> 3);
+  auto build_table = [&](int t, const WRegs& r) __attribute__((always_inline)) {
+    const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)t) & 3u))) & 0xffu;
+    const float cp = decode_constant(e, __uint_as_float(r.s), mu);
+    u32x4_t t0, t1;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        t0[p] = pack_bf16x2(__fmul_rn(sq[2 * p], cp), __fmul_rn(sq[2 * p + 1], cp));
-        t1[p] = pack_bf16x2(__fmul_rn(sq[8 + 2 * p], cp), __fmul_rn(sq[9 + 2 * p], cp));
-      }
-      char* row = lut + 32 * (lane & 7) + 256 * (lane >> 3);
-      *reinterpret_cast<u32x4_t*>(row) = t0;
-      *reinterpret_cast<u32x4_t*>(row + 16) = t1;
+    for (int j = 0; j < 4; ++j) {
+      t0[j] = pack_bf16x2(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
+      t1[j] = pack_bf16x2(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp));
+    }
+    *reinterpret_cast<u32x4_t*>(tb_row) = t0;
+    *reinterpret_cast<u32x4_t*>(tb_row + 16) = t1;
+  };
+  // the code dwords of k-chunk dc of rows 8q + dr, q = 0..7 (32 consecutive
+  // dwords per q: no bank conflicts)
+  auto read_codes = [&](int slot, uint32_t* cw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      cw[q] = *reinterpret_cast<const uint32_t*>(scode[slot] + (kProdRows * p + 8 * q + dr) * 32 +
+                                                  dc * 4);
+  };
+  // rows 8q + dr: the 8 table lookups of code dword w, then one 16-byte
+  // store of the 8 consecutive bf16.  The table of row 8q + dr starts at
+  // lut_lane + 256q, whose low byte is 32dr (the tables are 256-byte
+  // aligned); a lookup address is that base with its low byte replaced by
+  // 32dr | 2*code.  The low bytes of the 4 even (odd) codes of w are formed
+  // together, then each address is one byte permute.
+  const uint32_t dr32x4 = (uint32_t)dr * 0x20202020u;
+  auto lookup_group = [&](uint32_t w, int q, uint32_t* v) __attribute__((always_inline)) {
+    const uint32_t tab = lut_lane + 256u * (uint32_t)q;
+    const uint32_t we = ((w << 1) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j
+    const uint32_t wo = ((w >> 3) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j+1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = lds_read_u16(__builtin_amdgcn_perm(tab, we, 0x07060500u | (uint32_t)j));
+      v[2 * j + 1] = lds_read_u16(__builtin_amdgcn_perm(tab, wo, 0x07060500u | (uint32_t)j));
     }
   };
-  // rows 8q + dr: the code dword of k-chunk dc, its 8 table lookups, one
-  // 16-byte store of 8 consecutive bf16
-  auto dequant_group = [&](int slot, char* dst, int q) __attribute__((always_inline)) {
-    const uint32_t w =
-        *reinterpret_cast<const uint32_t*>(scode[slot][wave] + (8 * q + dr) * 32 + dc * 4);
-    const uint32_t tab = lut_lane + 256u * (uint32_t)q;  // 32-byte aligned
+  // (the empty asm pins the wait for the lookups here: otherwise the values
+  // are packed, and so waited for, right after the lookups are issued)
+  auto store_group = [&](uint32_t* v, char* dst, int q) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7]));
     u32x4_t o;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      u16x2_t v;
-      v.x = lds_read_u16(tab | code_x2(w, 8 * p));
-      v.y = lds_read_u16(tab | code_x2(w, 8 * p + 4));
-      o[p] = __builtin_bit_cast(uint32_t, v);
-    }
-    *reinterpret_cast<u32x4_t*>(dst + xswz(32 * wave + 8 * q + dr, dc)) = o;
+    for (int j = 0; j < 4; ++j) o[j] = v[2 * j] | (v[2 * j + 1] << 16);
+    *reinterpret_cast<u32x4_t*>(dst + xswz(kProdRows * p + 8 * q + dr, dc)) = o;
   };
-
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // MFMA group g (0..15) of a step: k-half ks = g / 8, token block i = g % 8;
-  // B fragments of the k-half are read at its first group.
-  const int arow = 128 * wm + lr, brow = 64 * wn + lr;
-  u32x4_t bfr[4];
-  auto mfma_group = [&](const char* xa, const char* wb, int g) __attribute__((always_inline)) {
-    const int ks = g >> 3, i = g & 7;
-    if (i == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + xswz(brow + 16 * j, 2 * kq + ks));
-    }
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(xa + xswz(arow + 16 * i, 2 * kq + ks));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
-  };
-  auto mfma_step = [&](const char* xa, const char* wb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < 16; ++g) mfma_group(xa, wb, g);
-  };
-  // The MFMAs of one step interleaved with the dequantization of step t:
-  // table build next to the first groups, one row group of lookups every
-  // three MFMA groups.
-  // The two waves of a SIMD (w and w + 4, i.e. wm = 0 and 1) dequantize in
-  // different halves of the step (phase P = wm): while one issues table
-  // arithmetic and lookups, the other issues MFMAs.  Both instances keep the
-  // same barrier sequence.
-  auto mfma_step_dequant = [&](auto P, const char* xa, const char* wb, int t, int slot, char* dst)
+  // issue(q) runs after the lookups of row group q are issued: global reads
+  // queue behind one another in the compute unit's memory pipeline and a
+  // wave cannot issue past one that does not fit, so they are spread over
+  // the dequantization instead of issued all at once.
+  auto dequant = [&](int t, int slot, const WRegs& r, char* dst, auto&& issue)
       __attribute__((always_inline)) {
-    constexpr int g0 = decltype(P)::value ? 8 : 0;
+    uint32_t cw[8], lv[2][8];
+    build_table(t, r);
+    read_codes(slot, cw);
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      mfma_group(xa, wb, g);
-      if (g == g0) build_table(t, slot);
-      if (g > g0 && g <= g0 + 4) dequant_group(slot, dst, g - g0 - 1);
+    for (int q = 0; q <= 8; ++q) {
+      if (q < 8) {
+        lookup_group(cw[q], q, lv[q & 1]);
+        issue(q);
+        __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+      }
+      if (q > 0) store_group(lv[(q - 1) & 1], dst, q - 1);
     }
   };
 
   // prologue: X and weight data of step 0, weight data of step 1 (K >= 64,
   // so step 0 is a weight step); dequantize step 0
+  WRegs wcur, wnext;
   {
-    WRegs w0, w1;
+    WRegs w0;
     copy_x(sx0, 0);
     load_w(w0, 0);
-    load_w(w1, 1);
-    store_w(0, w0);
-    store_w(1, w1);
+    load_w(wcur, 1);
+    wait_vmem();
+    store_codes(0, w0);
+    store_codes(1, wcur);
+    dequant(0, 0, w0, sw[0], [](int) {});
   }
   wait_vmem();
-  __syncthreads();
-  build_table(0, 0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dequant_group(0, sw[0], q);
-  __syncthreads();
+  __syncthreads();  // step 0 in place
 
-  // Weight steps 0 .. ksteps-2: copy X of step s+1 into the other X buffer
-  // and load the weight data of step s+2 into registers, issue the MFMAs of
-  // step s interleaved with the dequantization of step s+1 into the other Ŵ
-  // buffer, then store the weight data into slot s % 2 (both buffers last
-  // read in the previous iteration).  (Weight data of step ksteps may be
-  // loaded: its reads stay inside the buffers or return zeros, and it is not
-  // used.)  One step per iteration and no other loop carrying the
-  // accumulators: anything else makes the register allocator shuffle or
-  // spill them.  The loop is instantiated once per phase.
-  auto iter = [&](auto P, int s, const char* xa, char* xn) __attribute__((always_inline)) {
-    WRegs wr;
-    copy_x(xn, s + 1);
-    load_w(wr, s + 2);
-    mfma_step_dequant(P, xa, sw[s & 1], s + 1, (s + 1) & 1, sw[(s + 1) & 1]);
-    store_w(s & 1, wr);
+  // Weight steps 0 .. ksteps-2: dequantize step s+1 (constants loaded in the
+  // previous iteration, codes in slot (s+1) % 2) into the other Ŵ buffer,
+  // meanwhile copying X of step s+1 into the other X buffer and loading the
+  // weight data of step s+2; then store the codes of step s+2 into slot
+  // s % 2 (last read in the previous iteration).  (Weight data of step ksteps may be loaded:
+  // its reads stay inside the buffers or return zeros, and it is not used.)
+#pragma unroll 1
+  for (int s = 0; s + 1 < ksteps; ++s) {
+    char* const xn = sxb((s + 1) & 1);
+    dequant(s + 1, (s + 1) & 1, wcur, sw[(s + 1) & 1], [&](int q) {
+      if (q < 4) {
+        copy_x_part(xn, s + 1, 2 * q);
+        copy_x_part(xn, s + 1, 2 * q + 1);
+      }
+      if (q == 4) load_codes(wnext, s + 2);
+      if (q == 5) load_consts(wnext, s + 2);
+    });
+    store_codes(s & 1, wnext);
+    wcur = wnext;
     wait_vmem();
     __syncthreads();
-  };
-  auto main_loop = [&](auto P) __attribute__((always_inline)) {
-#pragma unroll 1
-    for (int s = 0; s + 1 < ksteps; ++s) iter(P, s, sxb(s & 1), sxb((s + 1) & 1));
-  };
-  if (wm == 0)
-    main_loop(std::integral_constant<int, 0>());
-  else
-    main_loop(std::integral_constant<int, 1>());
-  // Last weight step, copying LoRA step 0 (sT and B2 tiles) into the other
-  // buffers; then the LoRA steps, unrolled.
+  }
+  // last weight step: copy LoRA step 0 (sT and B2 tiles) into the other
+  // buffers; then the LoRA steps
   copy_lora(rt, sxb(ksteps & 1), 0);
   copy_lora(rb, sw[ksteps & 1], 0);
-  mfma_step(sxb((ksteps - 1) & 1), sw[(ksteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
-#pragma unroll
+#pragma unroll 1
   for (int l = 0; l < LSTEPS; ++l) {
     const int s = ksteps + l;
     if (l + 1 < LSTEPS) {
       copy_lora(rt, sxb((s + 1) & 1), l + 1);
       copy_lora(rb, sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sxb(s & 1), sw[s & 1]);
     wait_vmem();
     __syncthreads();
-  }
-
-  // epilogue: lane holds rows 128wm + 16i + 4kq + v of column 64wn + 16j + lr.
-  // The row/column bases go through an empty asm so that their address
-  // arithmetic is not hoisted above the main loop (it would stay live there).
-  int row0 = 128 * wm + 4 * kq, col0 = 64 * wn + lr;
-  asm volatile("" : "+v"(row0), "+v"(col0));
-  const bool full = (m0 + TM <= M) && (n0 + TN <= N);
-  if (y_bf16) {
-    uint16_t* Yb = static_cast<uint16_t*>(Y) + (m0 + row0) * N + n0 + col0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
-          if (full || (m < M && n < N))
-            Yb[(16 * i + v) * N + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
-        }
-  } else {
-    float* Yf = static_cast<float*>(Y) + (m0 + row0) * N + n0 + col0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
-          if (full || (m < M && n < N)) Yf[(16 * i + v) * N + 16 * j] = acc[i][j][v];
-        }
   }
 }
 
