@@ -67,10 +67,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
-  // per producer wave: tables of its 64 rows (row t at 32(t % 8) + 256(t / 8));
-  // packed codes of the tile's rows (32 bytes each), double-buffered by step
-  __shared__ __attribute__((aligned(256))) char slut[kProdWaves][kProdRows * 32];
-  __shared__ __attribute__((aligned(16))) char scode[2][TN * 32];
+  // tables of the tile's weight rows (row r at 32(r % 8) + 256(r / 8)),
+  // double-buffered by step
+  __shared__ __attribute__((aligned(256))) char stab[2][TN * 32];
   int tmi, tni;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni)) return;
 
@@ -79,6 +78,66 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const int64_t m0 = (int64_t)tmi * TM, n0 = (int64_t)tni * TN;
   const int ksteps = (int)(K / KSTEP);
   auto sxb = [&](int i) { return i ? sx1 : sx0; };
+
+  // Resources start at this tile's first row and end at the tensor's last
+  // row: rows past M or N read as zero.  (Rows past M only feed output rows
+  // past M, rows past N only output columns past N; neither is stored.)
+  // Reads of weight data one or two steps past the last step stay inside
+  // these buffers or return zeros; their results are never used.
+  const rsrc_t rc = make_rsrc(W.codes + n0 * (K / 2), (N - n0) * (K / 2));
+
+  // Lookups of a row group (8 weight rows from tile row R, a multiple of 8):
+  // lane l = (dr, dc) = (l >> 3, l & 7) takes code dword dc of row R + dr
+  // (k = 8dc .. 8dc + 7 of the step) and looks each code up in its row's
+  // table, then stores the 8 bf16 as one 16-byte chunk.  The 8 lanes of a
+  // row hit its table, and the 4 rows of each half-wave (served in one LDS
+  // cycle) hit 4 different groups of 8 of the 32 banks.  The table of row
+  // R + dr starts at a 256-byte-aligned base + 256(R / 8) + 32dr, so a
+  // lookup address is that address with its low byte replaced by
+  // 32dr | 2*code; the low bytes of the 4 even (odd) codes of a dword are
+  // formed together, then each address is one byte permute.
+  const int dr = lane >> 3, dc = lane & 7;
+  const uint32_t dr32x4 = (uint32_t)dr * 0x20202020u;
+  auto load_code = [&](int R, int t) __attribute__((always_inline)) {
+    return buf_load4(rc, (uint32_t)(R + dr) * (uint32_t)(K / 2) + 4u * (uint32_t)dc, (uint32_t)t * 32u);
+  };
+  auto lookup_group = [&](uint32_t w, const char* tabs, int R, uint32_t* v) __attribute__((always_inline)) {
+    const uint32_t tab = lds_offset(tabs) + 256u * (uint32_t)(R >> 3) + 32u * (uint32_t)dr;
+    const uint32_t we = ((w << 1) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j
+    const uint32_t wo = ((w >> 3) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j+1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = lds_read_u16(__builtin_amdgcn_perm(tab, we, 0x07060500u | (uint32_t)j));
+      v[2 * j + 1] = lds_read_u16(__builtin_amdgcn_perm(tab, wo, 0x07060500u | (uint32_t)j));
+    }
+  };
+  // (the empty asm pins the wait for the lookups here: otherwise the values
+  // are packed, and so waited for, right after the lookups are issued)
+  auto store_group = [&](uint32_t* v, char* dst, int R) __attribute__((always_inline)) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                 "+v"(v[7]));
+    u32x4_t o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = v[2 * j] | (v[2 * j + 1] << 16);
+    *reinterpret_cast<u32x4_t*>(dst + xswz(R + dr, dc)) = o;
+  };
+  // NG row groups from R0 (8 rows apart), lookups of group q in flight while
+  // group q - 1 is packed and stored; issue(q) runs after group q's lookups.
+  auto dequant_rows = [&](auto NGc, int R0, const uint32_t* cw, int t, auto&& issue)
+      __attribute__((always_inline)) {
+    constexpr int NG = decltype(NGc)::value;
+    uint32_t lv[2][8];
+#pragma unroll
+    for (int q = 0; q <= NG; ++q) {
+      if (q < NG) {
+        lookup_group(cw[q], stab[t & 1], R0 + 8 * q, lv[q & 1]);
+        issue(q);
+        __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+      }
+      if (q > 0) store_group(lv[(q - 1) & 1], sw[t & 1], R0 + 8 * (q - 1));
+    }
+  };
+  auto no_issue = [](int) {};
 
   if (wave < kMfmaWaves) {
     // ---------------------------------------------------------------- MFMA
@@ -122,9 +181,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       }
     };
 
+    // This wave also dequantizes weight rows [16w, 16w + 16) of every step,
+    // after its MFMAs of the step before.
+    const int R0 = 16 * wave;
+    uint32_t cw[2];
+    cw[0] = load_code(R0, 0);
+    cw[1] = load_code(R0 + 8, 0);
+    __syncthreads();  // tables of steps 0 and 1 in place
+    dequant_rows(std::integral_constant<int, 2>(), R0, cw, 0, no_issue);
     __syncthreads();  // step 0 in place
 #pragma unroll 1
-    for (int s = 0; s < ksteps + LSTEPS; ++s) {
+    for (int s = 0; s + 1 < ksteps; ++s) {
+      cw[0] = load_code(R0, s + 1);
+      cw[1] = load_code(R0 + 8, s + 1);
+      mfma_step(sxb(s & 1), sw[s & 1]);
+      dequant_rows(std::integral_constant<int, 2>(), R0, cw, s + 1, no_issue);
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int s = ksteps - 1; s < ksteps + LSTEPS; ++s) {
       mfma_step(sxb(s & 1), sw[s & 1]);
       __syncthreads();
     }
@@ -163,15 +238,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   }
 
   // ------------------------------------------------------------ producers
-  const int p = wave - kMfmaWaves;  // weight rows [64p, 64p + 64) of the tile
+  // Producer p builds the tables of weight rows [64p, 64p + 64), dequantizes
+  // rows [128 + 32p, +32) and copies X rows [64p, +64) of every step.
+  const int p = wave - kMfmaWaves;
   const uint32_t kpr = (uint32_t)(K / kBlock);  // blocks per weight row
   const float mu = *W.mu;
-
-  // Resources start at this tile's first row and end at the tensor's last
-  // row: rows past M or N read as zero.  (Rows past M only feed output rows
-  // past M, rows past N only output columns past N; neither is stored.)
   const rsrc_t rt = make_rsrc(sT + m0 * 2 * Rp, (M - m0) * 2 * Rp * 2);
-  const rsrc_t rc = make_rsrc(W.codes + n0 * (K / 2), (N - n0) * (K / 2));
   const rsrc_t re = make_rsrc(W.e + n0 * kpr, (N - n0) * kpr);
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
@@ -203,39 +275,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       buf_load_lds16(r, t + (64 * p + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
   };
 
-  // Weight data of row 64p + l for step t: its 32 code bytes, the dword
-  // holding its e4m3 byte and its group scale.
-  const int prow = kProdRows * p + lane;
-  const uint32_t vcd = (uint32_t)prow * (uint32_t)(K / 2);
-  const uint32_t ve_me = (uint32_t)prow * kpr;
-  const uint32_t blk_me = (uint32_t)(n0 + prow) * kpr;
-  struct WRegs {
-    u32x4_t c0, c1;
+  // Table of row 64p + lane for step t: the dword holding its e4m3 byte and
+  // its group scale, loaded a step ahead; lane writes the 16 values
+  // RNE_bf16(fl32(q_j * c')) (bit-identical to multiplying per element,
+  // since the value depends only on code and row).
+  const int trow = 64 * p + lane;
+  const uint32_t ve_me = (uint32_t)trow * kpr;
+  const uint32_t blk_me = (uint32_t)(n0 + trow) * kpr;
+  struct Consts {
     uint32_t e, s;
   };
-  auto load_codes = [&](WRegs& r, int t) __attribute__((always_inline)) {
-    r.c0 = buf_load16(rc, vcd, (uint32_t)t * 32u);
-    r.c1 = buf_load16(rc, vcd + 16u, (uint32_t)t * 32u);
-  };
-  auto load_consts = [&](WRegs& r, int t) __attribute__((always_inline)) {
+  auto load_consts = [&](Consts& r, int t) __attribute__((always_inline)) {
     r.e = buf_load4(re, (ve_me + (uint32_t)t) & ~3u, 0u);
     r.s = buf_load4(rs, ((blk_me + (uint32_t)t) / kDqBlock) * 4u, 0u);
   };
-  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
-    load_codes(r, t);
-    load_consts(r, t);
-  };
-  auto store_codes = [&](int slot, const WRegs& r) __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4_t*>(scode[slot] + 32 * prow) = r.c0;
-    *reinterpret_cast<u32x4_t*>(scode[slot] + 32 * prow + 16) = r.c1;
-  };
-
-  // Table of row 64p + lane for step t (constants in r).
-  char* lut = slut[p];
-  const int dr = lane >> 3, dc = lane & 7;  // row 8q + dr of the wave, k-chunk dc
-  const uint32_t lut_lane = lds_offset(lut) + (uint32_t)dr * 32u;
-  char* const tb_row = lut + 32 * (lane & 7) + 256 * (lane >> 3);
-  auto build_table = [&](int t, const WRegs& r) __attribute__((always_inline)) {
+  const int tb_off = 32 * (lane & 7) + 256 * (8 * p + (lane >> 3));
+  auto build_table = [&](int t, const Consts& r) __attribute__((always_inline)) {
     const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)t) & 3u))) & 0xffu;
     const float cp = decode_constant(e, __uint_as_float(r.s), mu);
     u32x4_t t0, t1;
@@ -244,99 +299,54 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       t0[j] = pack_bf16x2(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
       t1[j] = pack_bf16x2(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp));
     }
-    *reinterpret_cast<u32x4_t*>(tb_row) = t0;
-    *reinterpret_cast<u32x4_t*>(tb_row + 16) = t1;
-  };
-  // the code dwords of k-chunk dc of rows 8q + dr, q = 0..7 (32 consecutive
-  // dwords per q: no bank conflicts)
-  auto read_codes = [&](int slot, uint32_t* cw) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      cw[q] = *reinterpret_cast<const uint32_t*>(scode[slot] + (kProdRows * p + 8 * q + dr) * 32 +
-                                                  dc * 4);
-  };
-  // rows 8q + dr: the 8 table lookups of code dword w, then one 16-byte
-  // store of the 8 consecutive bf16.  The table of row 8q + dr starts at
-  // lut_lane + 256q, whose low byte is 32dr (the tables are 256-byte
-  // aligned); a lookup address is that base with its low byte replaced by
-  // 32dr | 2*code.  The low bytes of the 4 even (odd) codes of w are formed
-  // together, then each address is one byte permute.
-  const uint32_t dr32x4 = (uint32_t)dr * 0x20202020u;
-  auto lookup_group = [&](uint32_t w, int q, uint32_t* v) __attribute__((always_inline)) {
-    const uint32_t tab = lut_lane + 256u * (uint32_t)q;
-    const uint32_t we = ((w << 1) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j
-    const uint32_t wo = ((w >> 3) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j+1
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = lds_read_u16(__builtin_amdgcn_perm(tab, we, 0x07060500u | (uint32_t)j));
-      v[2 * j + 1] = lds_read_u16(__builtin_amdgcn_perm(tab, wo, 0x07060500u | (uint32_t)j));
-    }
-  };
-  // (the empty asm pins the wait for the lookups here: otherwise the values
-  // are packed, and so waited for, right after the lookups are issued)
-  auto store_group = [&](uint32_t* v, char* dst, int q) __attribute__((always_inline)) {
-    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
-                 "+v"(v[7]));
-    u32x4_t o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = v[2 * j] | (v[2 * j + 1] << 16);
-    *reinterpret_cast<u32x4_t*>(dst + xswz(kProdRows * p + 8 * q + dr, dc)) = o;
-  };
-  // issue(q) runs after the lookups of row group q are issued: global reads
-  // queue behind one another in the compute unit's memory pipeline and a
-  // wave cannot issue past one that does not fit, so they are spread over
-  // the dequantization instead of issued all at once.
-  auto dequant = [&](int t, int slot, const WRegs& r, char* dst, auto&& issue)
-      __attribute__((always_inline)) {
-    uint32_t cw[8], lv[2][8];
-    build_table(t, r);
-    read_codes(slot, cw);
-#pragma unroll
-    for (int q = 0; q <= 8; ++q) {
-      if (q < 8) {
-        lookup_group(cw[q], q, lv[q & 1]);
-        issue(q);
-        __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
-      }
-      if (q > 0) store_group(lv[(q - 1) & 1], dst, q - 1);
-    }
+    char* const d = stab[t & 1] + tb_off;
+    *reinterpret_cast<u32x4_t*>(d) = t0;
+    *reinterpret_cast<u32x4_t*>(d + 16) = t1;
   };
 
-  // prologue: X and weight data of step 0, weight data of step 1 (K >= 64,
-  // so step 0 is a weight step); dequantize step 0
-  WRegs wcur, wnext;
+  const int PR0 = 128 + 32 * p;
+  uint32_t cw[4], cwn[4];
+  Consts cc, cn;
+  // prologue: X of step 0, tables of steps 0 and 1, lookups of step 0
   {
-    WRegs w0;
+    Consts c0;
     copy_x(sx0, 0);
-    load_w(w0, 0);
-    load_w(wcur, 1);
-    wait_vmem();
-    store_codes(0, w0);
-    store_codes(1, wcur);
-    dequant(0, 0, w0, sw[0], [](int) {});
+    load_consts(c0, 0);
+    load_consts(cn, 1);
+    load_consts(cc, 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cw[q] = load_code(PR0 + 8 * q, 0);
+      cwn[q] = load_code(PR0 + 8 * q, 1);
+    }
+    build_table(0, c0);
+    build_table(1, cn);
   }
+  __syncthreads();  // tables of steps 0 and 1 in place
+  dequant_rows(std::integral_constant<int, 4>(), PR0, cw, 0, no_issue);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cw[q] = cwn[q];
   wait_vmem();
   __syncthreads();  // step 0 in place
 
-  // Weight steps 0 .. ksteps-2: dequantize step s+1 (constants loaded in the
-  // previous iteration, codes in slot (s+1) % 2) into the other Ŵ buffer,
-  // meanwhile copying X of step s+1 into the other X buffer and loading the
-  // weight data of step s+2; then store the codes of step s+2 into slot
-  // s % 2 (last read in the previous iteration).  (Weight data of step ksteps may be loaded:
-  // its reads stay inside the buffers or return zeros, and it is not used.)
+  // Weight steps 0 .. ksteps-2: load the codes of step s+2 and constants of
+  // step s+3, build the tables of step s+2 (that buffer was last read in the
+  // previous iteration), dequantize this wave's rows of step s+1 while
+  // copying X of step s+1 into the other X buffer.
 #pragma unroll 1
   for (int s = 0; s + 1 < ksteps; ++s) {
     char* const xn = sxb((s + 1) & 1);
-    dequant(s + 1, (s + 1) & 1, wcur, sw[(s + 1) & 1], [&](int q) {
-      if (q < 4) {
-        copy_x_part(xn, s + 1, 2 * q);
-        copy_x_part(xn, s + 1, 2 * q + 1);
-      }
-      if (q == 4) load_codes(wnext, s + 2);
-      if (q == 5) load_consts(wnext, s + 2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cwn[q] = load_code(PR0 + 8 * q, s + 2);
+    load_consts(cn, s + 3);
+    build_table(s + 2, cc);
+    dequant_rows(std::integral_constant<int, 4>(), PR0, cw, s + 1, [&](int q) {
+      copy_x_part(xn, s + 1, 2 * q);
+      copy_x_part(xn, s + 1, 2 * q + 1);
     });
-    store_codes(s & 1, wnext);
-    wcur = wnext;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cw[q] = cwn[q];
+    cc = cn;
     wait_vmem();
     __syncthreads();
   }
