@@ -6,29 +6,29 @@
 // The reduction runs over the weight's rows n while the codes are contiguous
 // along k, so the dequantized weight has to be transposed on its way to the
 // MFMA B operand.  Design:
-//   * 256x256 output tile per workgroup (token rows x input features) of 8
-//     waves, two per SIMD, so that one wave's dequantization arithmetic can
-//     issue while the other wave's MFMAs run.
-//   * Per 64-row reduction step every wave dequantizes 32 of the tile's 256
-//     columns (half an NF4 block column) for all 64 weight rows into a shared
-//     transposed bf16 tile Ŵᵀ[k][n] in LDS; then wave (wm, wk) multiplies
-//     token rows [128wm, +128) by columns [64wk, +64): 64
-//     v_mfma_f32_16x16x32_bf16 per wave and step, operands read from LDS.
-//   * Dequantization goes through a per-row table: for each weight row of
-//     the step one lane writes the 16 values RNE_bf16(fl32(q_j * c')) (its
-//     block's scaled codebook) to LDS; lane (rg, cg) then owns rows
-//     8rg..8rg+7 by columns 4cg..4cg+3 of the wave's slice, each code one
-//     2-byte table read, and packs 8 consecutive rows of one column into one
-//     16-byte store: the values come out already transposed.  Table slots,
-//     tile swizzles and lane maps are chosen so that lookups, stores and
-//     fragment reads are free of LDS bank conflicts (32 banks of 4 bytes).
-//   * The dY tile of the next step is copied straight into LDS; the weight
-//     data of the step after is loaded into registers at the top of an
-//     iteration and stored to LDS at its end.  The MFMAs of step s are
-//     interleaved in issue order with the dequantization of step s+1 into the
-//     other Ŵᵀ buffer, in the first half of the step for one wave of each
-//     SIMD and in the second half for the other.  Rows past N get an all-zero
-//     table.
+//   * 256x256 output tile per workgroup (token rows x input features) of 12
+//     waves, three per SIMD, in two roles.  Waves 0..7 multiply: wave
+//     (wm, wk) owns token rows [128wm, +128) and columns [64wk, +64), 64
+//     v_mfma_f32_16x16x32_bf16 per 64-row reduction step, operands read from
+//     LDS one MFMA group ahead.  Waves 8..11 (one per SIMD) produce: wave
+//     8 + p copies a quarter of the next step's dY tile straight into LDS,
+//     loads the codes of block column p (columns [64p, +64)) for the step
+//     after and stores them transposed to LDS, and builds that block
+//     column's 64 row tables a step ahead.
+//   * The transposed bf16 tile Ŵᵀ[k][n] of a step is dequantized in 8 slices
+//     of 32 columns: producer p takes slice 2p + 1, MFMA wave w < 4 takes
+//     slice 2w after its MFMAs of the step before (waves 4..7, whose MFMAs
+//     issue behind those of waves 0..3 on the same SIMDs, take none).
+//   * Dequantization goes through a per-row table: for each weight row and
+//     block one lane writes the 16 values RNE_bf16(fl32(q_j * c')) to LDS;
+//     in a slice, lane (rg, cg) owns rows 8rg..8rg+7 by columns 4cg..4cg+3,
+//     each code one 2-byte table read, and packs 8 consecutive rows of one
+//     column into one 16-byte store: the values come out already
+//     transposed.  Table slots, tile swizzles and lane maps are chosen so
+//     that lookups, stores and fragment reads are free of LDS bank conflicts
+//     (32 banks of 4 bytes).  Rows past N get an all-zero table.
+//   * One barrier per step: after it the MFMA waves use dY(s) and Ŵᵀ(s)
+//     while the other buffers fill with dY(s+1) and Ŵᵀ(s+1).
 //   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
 //     AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A), both
 //     copied straight into LDS.
@@ -41,9 +41,8 @@ namespace qnf4 {
 namespace {
 
 constexpr int TM = 256, TK = 256, NSTEP = 64;
-constexpr int kWaves = 8, kThreads = 64 * kWaves;
-
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+constexpr int kMfmaWaves = 8, kProdWaves = 4, kWaves = kMfmaWaves + kProdWaves;
+constexpr int kThreads = 64 * kWaves;
 
 // dY tile (token rows, 64 n each): chunk c of row r at physical c ^ (r & 7);
 // a fragment read gives the 8 lanes of one LDS cycle 8 consecutive rows.
@@ -66,320 +65,363 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
                                                               Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sa0[TM * 128], sa1[TM * 128];  // A tiles: dY, then sU
   __shared__ __attribute__((aligned(16))) char sw[2][TK * 128];  // B tiles: Ŵᵀ, then AT2
-  // per wave (all wave-private, so one buffer each): 64 row tables of 32
-  // bytes, the 16 code bytes of each weight row for the wave's 32 columns,
-  // and each table row's e4m3 byte and group scale
-  __shared__ __attribute__((aligned(256))) char slut[kWaves][64 * 32];
-  __shared__ __attribute__((aligned(16))) char scode[kWaves][64 * 16];
-  __shared__ __attribute__((aligned(16))) uint32_t sconst[kWaves][2][64];
+  // per step slot: the row tables of each block column (row 8rg + i at
+  // 256i + 32rg of its 2 KB), and the codes of each 32-column slice
+  // transposed (the 2 bytes of columns 4cg..4cg+3 of row 8rg + i at byte 2i
+  // of 16-byte slot 8rg + (cg ^ rg))
+  __shared__ __attribute__((aligned(256))) char stab[2][4][64 * 32];
+  __shared__ __attribute__((aligned(16))) char scode[2][8][64 * 16];
   int tmi, tki;
   if (!tile_of(blockIdx.x, tiles_m, tiles_k, tmi, tki)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, kq = lane >> 4;
-  const int wm = wave >> 2, wk = wave & 3;
   const int rg = lane >> 3, cg = lane & 7;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, k0 = (int64_t)tki * TK;
-  const int64_t kw0 = k0 + 32 * wave;  // first column of this wave's dequantization slice
   const int nsteps = (int)((N + NSTEP - 1) / NSTEP);
-  const uint32_t kpr = (uint32_t)(K / kBlock);
-  const uint32_t kbw = (uint32_t)(kw0 / kBlock);  // the slice's block column
-  const bool wave_cols_ok = kw0 < K;
-  const float mu = *W.mu;
+  auto sab = [&](int i) { return i ? sa1 : sa0; };
 
-  const rsrc_t rdy = make_rsrc(dY + m0 * N, (M - m0) * N * 2);
+  // Slice sigma (columns [32 sigma, +32)) of step t into Ŵᵀ(t): lane (rg, cg)
+  // reads the codes of its rows and columns (row 2p in the low half of dword
+  // p, row 2p + 1 in its high half), looks each up in its row's table and
+  // stores column c of rows 8rg..8rg+7 at wswz(32 sigma + 4cg + c, rg) =
+  // (st0 ^ 16c) + 128c.  The table of row 8rg + i sits at a 256-byte-aligned
+  // base + 256i + 32rg, so a lookup address is base + 32rg with its low byte
+  // replaced by 32rg | 2*code (one byte permute from codes pre-shifted four
+  // at a time) plus the constant 256i.  Column pair cp2 = columns 2cp2,
+  // 2cp2 + 1: with `overlap` (producers) the lookups of the second pair are
+  // in flight while the first is packed and stored; the MFMA waves, short of
+  // registers, take the pairs one after the other.
+  const int code_rslot = 8 * rg + (cg ^ rg);
+  const uint32_t rg32x4 = (uint32_t)rg * 0x20202020u;
+  auto read_codes = [&](int t, int sigma) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4_t*>(scode[t & 1][sigma] + 16 * code_rslot);
+  };
+  auto lookup_cols = [&](uint32_t lb, const u32x4_t& we, const u32x4_t& wo, int cp2, uint32_t (*v)[8])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t sel = 0x07060500u | (uint32_t)(2 * h + cp2);
+        v[0][2 * p + h] = lds_read_u16(__builtin_amdgcn_perm(lb, we[p], sel) + 256u * (2 * p + h));
+        v[1][2 * p + h] = lds_read_u16(__builtin_amdgcn_perm(lb, wo[p], sel) + 256u * (2 * p + h));
+      }
+  };
+  // (the empty asm pins the wait for the lookups here: otherwise the values
+  // are packed, and so waited for, right after the lookups are issued)
+  auto store_cols = [&](char* dst, uint32_t st0, int cp2, uint32_t (*v)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      asm volatile("" : "+v"(v[cc][0]), "+v"(v[cc][1]), "+v"(v[cc][2]), "+v"(v[cc][3]), "+v"(v[cc][4]),
+                   "+v"(v[cc][5]), "+v"(v[cc][6]), "+v"(v[cc][7]));
+      const int c = 2 * cp2 + cc;
+      u32x4_t o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) o[p] = v[cc][2 * p] | (v[cc][2 * p + 1] << 16);
+      *reinterpret_cast<u32x4_t*>(dst + ((st0 ^ (uint32_t)(16 * c)) + 128u * c)) = o;
+    }
+  };
+  auto dequant_slice = [&](auto overlap, int t, int sigma, const u32x4_t& cw, auto&& issue)
+      __attribute__((always_inline)) {
+    if constexpr (decltype(overlap)::value) {
+      const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)rg;
+      const uint32_t st0 =
+          (uint32_t)((32 * sigma + 4 * cg) * 128 + ((rg ^ cg ^ (4 * (cg & 1))) << 4));
+      u32x4_t we, wo;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        we[p] = ((cw[p] << 1) & 0x1E1E1E1Eu) | rg32x4;  // byte j: 2 * code 2j
+        wo[p] = ((cw[p] >> 3) & 0x1E1E1E1Eu) | rg32x4;  // byte j: 2 * code 2j+1
+      }
+      uint32_t v0[2][8], v1[2][8];
+      lookup_cols(lb, we, wo, 0, v0);
+      issue(0);
+      __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+      lookup_cols(lb, we, wo, 1, v1);
+      issue(1);
+      __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+      store_cols(sw[t & 1], st0, 0, v0);
+      store_cols(sw[t & 1], st0, 1, v1);
+    } else {
+      // one column at a time, addresses straight from the code dwords and
+      // lane offsets recomputed here from an opaque copy of the lane index
+      // (kept from being hoisted out of the MFMA waves' loop, where they
+      // would hold registers through the MFMAs)
+      const int ln = opaque(lane), lrg = ln >> 3, lcg = ln & 7;
+      const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)lrg;
+      const uint32_t st0 =
+          (uint32_t)((32 * sigma + 4 * lcg) * 128 + ((lrg ^ lcg ^ (4 * (lcg & 1))) << 4));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t v[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v[2 * p + h] = lds_read_u16((lb | code_x2(cw[p], 16 * h + 4 * c)) + 256u * (2 * p + h));
+        issue(c);
+        __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
+                     "+v"(v[7]));
+        u32x4_t o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[p] = v[2 * p] | (v[2 * p + 1] << 16);
+        *reinterpret_cast<u32x4_t*>(sw[t & 1] + ((st0 ^ (uint32_t)(16 * c)) + 128u * c)) = o;
+      }
+    }
+  };
+  auto no_issue = [](int) {};
+
+  if (wave < kMfmaWaves) {
+    // ---------------------------------------------------------------- MFMA
+    const int lr = lane & 15, kq = lane >> 4;
+    const int wm = wave >> 2, wk = wave & 3;
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA group g (0..15) of a step: n-half ks = g / 8, token block i = g % 8.
+    // A fragments are read one group ahead: group g first reads the A
+    // fragment of group g + 1, so the read's latency overlaps this group's
+    // MFMAs.  The B fragments of the second n-half are read right after the
+    // MFMAs of group 7.
+    const int arow = 128 * wm + lr, brow = 64 * wk + lr;
+    u32x4_t bfr[4], anext;
+    auto read_b = [&](const char* wb, int ks, u32x4_t* b) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const u32x4_t*>(wb + wswz(brow + 16 * j, 2 * kq + ks));
+    };
+    auto read_a = [&](const char* ya, int g) __attribute__((always_inline)) {
+      return *reinterpret_cast<const u32x4_t*>(ya + xswz(arow + 16 * (g & 7), 2 * kq + (g >> 3)));
+    };
+    auto mfma_step = [&](const char* ya, const char* wb) __attribute__((always_inline)) {
+      read_b(wb, 0, bfr);
+      anext = read_a(ya, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const int i = g & 7;
+        const u32x4_t a = anext;
+        if (g < 15) anext = read_a(ya, g + 1);
+        // keep the reads ahead of the MFMAs (the scheduler would sink them
+        // below to reuse the fragment's registers)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+        if (g == 7) read_b(wb, 1, bfr);
+      }
+    };
+
+    const bool dq = wave < 4;  // dequantizes slice 2w of every step
+    __syncthreads();  // codes and tables of steps 0 and 1 in place
+    auto read_codes_mfma = [&](int t) __attribute__((always_inline)) {
+      const int ln = opaque(lane);
+      return *reinterpret_cast<const u32x4_t*>(scode[t & 1][2 * wave] + 16 * (8 * (ln >> 3) + ((ln & 7) ^ (ln >> 3))));
+    };
+    if (dq) dequant_slice(std::false_type(), 0, 2 * wave, read_codes_mfma(0), no_issue);
+    __syncthreads();  // step 0 in place
+#pragma unroll 1
+    for (int s = 0; s + 1 < nsteps; ++s) {
+      mfma_step(sab(s & 1), sw[s & 1]);
+      if (dq) dequant_slice(std::false_type(), s + 1, 2 * wave, read_codes_mfma(s + 1), no_issue);
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int s = nsteps - 1; s < nsteps + LSTEPS; ++s) {
+      mfma_step(sab(s & 1), sw[s & 1]);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds rows 128wm + 16i + 4kq + v of column k0 + 64wk + 16j + lr
+    int row0 = 128 * wm + 4 * kq, col0 = 64 * wk + lr;
+    asm volatile("" : "+v"(row0), "+v"(col0));
+    const bool full = (m0 + TM <= M) && (k0 + TK <= K);
+    if (dx_bf16) {
+      uint16_t* D = static_cast<uint16_t*>(dX) + (m0 + row0) * K + k0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
+            if (full || (m < M && k < K))
+              D[(16 * i + v) * K + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
+          }
+    } else {
+      float* D = static_cast<float*>(dX) + (m0 + row0) * K + k0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
+            if (full || (m < M && k < K)) D[(16 * i + v) * K + 16 * j] = acc[i][j][v];
+          }
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------ producers
+  const int p = wave - kMfmaWaves;
+  const uint32_t kpr = (uint32_t)(K / kBlock);
+  const uint32_t kb = (uint32_t)(k0 / kBlock) + (uint32_t)p;  // this producer's block column
+  const bool cols_ok = k0 + 64 * p < K;
+  const float mu = *W.mu;
   const rsrc_t rsu = make_rsrc(sU + m0 * 2 * Rp, (M - m0) * 2 * Rp * 2);
   const rsrc_t rc = make_rsrc(W.codes, N * (K / 2));
   const rsrc_t re = make_rsrc(W.e, N * kpr);
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rat = make_rsrc(AT2 + k0 * 2 * Rp, (K - k0) * 2 * Rp * 2);
 
-  // dY tile, copied straight into LDS: thread τ moves 16 bytes of rows
-  // 64c + (τ >> 3), c = 0..3, into physical chunk τ & 7: logical chunk
-  // (τ & 7) ^ ((τ >> 3) & 7); each wave's copy is 1 KB contiguous.  (Written
-  // as assembly: the compiler then inserts no wait for these copies in front
-  // of the LDS reads of the step; the wait before the step's closing
-  // barrier is explicit.)
-  const int ylch = (tid & 7) ^ ((tid >> 3) & 7);
-  const uint32_t vy = (uint32_t)(((tid >> 3) * N + 8 * ylch) * 2);
-  const uint32_t y_gstride = (uint32_t)(64 * N * 2);
+  // dY rows [64p, +64) of a step, copied straight into LDS: part c moves rows
+  // 64p + 8c + (l >> 3), lane l into physical chunk l & 7, so it fetches
+  // logical chunk (l & 7) ^ (l >> 3) (row & 7 = l >> 3).  Each instruction
+  // fills 1 KB of LDS contiguously.  (Written as assembly: the compiler then
+  // inserts no wait for these copies in front of the producer's own LDS
+  // reads; the wait before the step's closing barrier is explicit.)
+  const int ylch = (lane & 7) ^ (lane >> 3);
+  const uint32_t vy = (uint32_t)(((64 * p + (lane >> 3)) * N + 8 * ylch) * 2);
+  const uint32_t y_gstride = (uint32_t)(8 * N * 2);
   const i32x4_t ryw = rsrc_words(dY + m0 * N, (M - m0) * N * 2);
   auto copy_y_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
-    dma_lds16(ryw, t + 64 * c * 128 + 1024 * wave, vy + c * y_gstride, (uint32_t)s * 128u);
+    dma_lds16(ryw, t + (64 * p + 8 * c) * 128, vy + c * y_gstride, (uint32_t)s * 128u);
   };
   auto copy_y = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) copy_y_part(t, s, c);
+    for (int c = 0; c < 8; ++c) copy_y_part(t, s, c);
   };
-  auto sab = [&](int i) { return i ? sa1 : sa0; };
-  // LoRA tiles copied straight into LDS: wave w copies rows 32w + 8c + (i >> 3),
-  // lane i into physical chunk i & 7.  sU rows use xswz, AT2 rows wswz.
-  const uint32_t vsu = (uint32_t)(((32 * wave + (lane >> 3)) * 2 * Rp + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  // LoRA tiles, the same rows: sU rows in the xswz layout, AT2 rows in wswz.
+  const uint32_t vsu = (uint32_t)(((64 * p + (lane >> 3)) * 2 * Rp + 8 * ylch) * 2);
   auto copy_su = [&](char* t, int l) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      buf_load_lds16(rsu, t + (32 * wave + 8 * c) * 128, vsu, c * (uint32_t)(8 * 2 * Rp * 2) + (uint32_t)l * 128u);
+    for (int c = 0; c < 8; ++c)
+      buf_load_lds16(rsu, t + (64 * p + 8 * c) * 128, vsu, c * (uint32_t)(8 * 2 * Rp * 2) + (uint32_t)l * 128u);
   };
   auto copy_at = [&](char* t, int l) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int row = 32 * wave + 8 * c + (lane >> 3);
+    for (int c = 0; c < 8; ++c) {
+      const int row = 64 * p + 8 * c + (lane >> 3);
       const int lch = (lane & 7) ^ ((row ^ (row >> 2)) & 7);
-      buf_load_lds16(rat, t + (32 * wave + 8 * c) * 128, (uint32_t)((row * 2 * Rp + 8 * lch) * 2),
+      buf_load_lds16(rat, t + (64 * p + 8 * c) * 128, (uint32_t)((row * 2 * Rp + 8 * lch) * 2),
                      (uint32_t)l * 128u);
     }
   };
 
-  // Weight data for step t: lane l loads the 16 code bytes of weight row
-  // t*64 + l over the wave's 32 columns, the e4m3 byte of block (row, kbw)
-  // and that block's group scale.
-  const uint32_t vcode = (uint32_t)(lane * (K / 2) + kw0 / 2);
+  // Codes of weight row t*64 + l, columns [64p, +64) of the tile: 32 bytes,
+  // the first 16 for slice 2p, the rest for slice 2p + 1.
+  const uint32_t vcode = (uint32_t)((uint32_t)lane * (uint32_t)(K / 2) + (uint32_t)(k0 / 2) + 32u * (uint32_t)p);
   const uint32_t code_sstride = (uint32_t)(NSTEP * (K / 2));
-  struct WRegs {
-    u32x4_t c;
-    uint32_t e, s;
+  struct Codes {
+    u32x4_t c0, c1;
   };
-  auto load_w = [&](WRegs& r, int t) __attribute__((always_inline)) {
-    r.c = buf_load16(rc, vcode, (uint32_t)t * code_sstride);
-    const uint32_t blk = ((uint32_t)t * NSTEP + lane) * kpr + kbw;
-    r.e = buf_load1(re, blk, 0u);
-    r.s = buf_load4(rs, (blk / kDqBlock) * 4u, 0u);
+  auto load_codes = [&](Codes& r, int t) __attribute__((always_inline)) {
+    r.c0 = buf_load16(rc, vcode, (uint32_t)t * code_sstride);
+    r.c1 = buf_load16(rc, vcode + 16u, (uint32_t)t * code_sstride);
   };
-  // The code bytes go to LDS transposed for the lanes that dequantize them:
-  // the 2 bytes of column pair cg of row 8rg + i sit at byte 2i of 16-byte
-  // slot 8rg + (cg ^ rg), so that lane (rg, cg) later reads its 8 rows'
-  // codes with one 16-byte read.  Slot XOR: the writes of one pair index go
-  // to 8 distinct slots of each 128-byte line, the reads of 8 consecutive
-  // lanes to 8 distinct slots.
   const uint32_t code_wbase = (uint32_t)((lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7));
-  auto store_w = [&](const WRegs& r) __attribute__((always_inline)) {
-    const uint32_t wb = opaque(code_wbase);
+  auto store_codes = [&](int t, const Codes& r) __attribute__((always_inline)) {
 #pragma unroll
-    for (int pc = 0; pc < 8; ++pc)
-      *reinterpret_cast<uint16_t*>(scode[wave] + (wb ^ (uint32_t)(pc << 4))) =
-          (uint16_t)(r.c[pc >> 1] >> (16 * (pc & 1)));
-    sconst[wave][0][lane] = r.e;
-    sconst[wave][1][lane] = r.s;
+    for (int pc = 0; pc < 8; ++pc) {
+      const uint32_t off = code_wbase ^ (uint32_t)(pc << 4);
+      *reinterpret_cast<uint16_t*>(scode[t & 1][2 * p] + off) = (uint16_t)(r.c0[pc >> 1] >> (16 * (pc & 1)));
+      *reinterpret_cast<uint16_t*>(scode[t & 1][2 * p + 1] + off) =
+          (uint16_t)(r.c1[pc >> 1] >> (16 * (pc & 1)));
+    }
   };
 
-  // Dequantization of step t (weight data in the wave's buffers) into dst.
-  // The table of weight row 8rg + i sits at byte 256i + 32rg of the wave's
-  // table area, so a lookup is (base of rg | 2*code) plus the constant 256i.
-  // Lane t builds the table of row 8rg + i with rg = t0 + 2t1 + 4t3 and
-  // i = t4 + 2t5 + 4t2 (t_b = bit b of t) and writes half t2 of it first:
-  // the 8 lanes of each 16-byte write then cover a 128-byte line.
-  const uint32_t lut_addr = lds_offset(slut[wave]);
-  const uint32_t lut_rg = lut_addr + 32u * (uint32_t)rg;
+  // Table of row 8 tb_rg + tb_i of block column p with tb_rg = t0 + 2t1 + 4t3
+  // and tb_i = t4 + 2t5 + 4t2 for lane t (t_b = bit b of t); the lane writes
+  // half t2 of it first, so the 8 lanes of each 16-byte write cover a
+  // 128-byte line.  Its e4m3 byte and group scale are loaded a step ahead.
   const int tb_rg = (lane & 3) | ((lane >> 1) & 4), tb_i = ((lane >> 4) & 3) | (lane & 4);
   const int tb_row = 8 * tb_rg + tb_i;
   const int tb_first = (lane >> 2) & 1;
-  char* const tb_dst = slut[wave] + 256 * tb_i + 32 * tb_rg + 16 * tb_first;
-  auto build_table = [&](int t) __attribute__((always_inline)) {
-    const bool row_ok = wave_cols_ok && ((int64_t)t * NSTEP + tb_row < N);
-    const float cp = decode_constant(sconst[wave][0][tb_row], __uint_as_float(sconst[wave][1][tb_row]), mu);
+  const int tb_off = 256 * tb_i + 32 * tb_rg + 16 * tb_first;
+  struct Consts {
+    uint32_t e, s;
+  };
+  auto load_consts = [&](Consts& r, int t) __attribute__((always_inline)) {
+    const uint32_t blk = ((uint32_t)t * NSTEP + (uint32_t)tb_row) * kpr + kb;
+    r.e = buf_load1(re, blk, 0u);
+    r.s = buf_load4(rs, (blk / kDqBlock) * 4u, 0u);
+  };
+  auto build_table = [&](int t, const Consts& r) __attribute__((always_inline)) {
+    const bool row_ok = cols_ok && ((int64_t)t * NSTEP + tb_row < N);
+    const float cp = decode_constant(r.e, __uint_as_float(r.s), mu);
     u32x4_t t0, t1;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      t0[p] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[2 * p], cp), __fmul_rn(cb.q[2 * p + 1], cp)) : 0u;
-      t1[p] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[8 + 2 * p], cp), __fmul_rn(cb.q[9 + 2 * p], cp)) : 0u;
+    for (int j = 0; j < 4; ++j) {
+      t0[j] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp)) : 0u;
+      t1[j] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp)) : 0u;
     }
-    char* const d = opaque(tb_dst);
+    char* const d = stab[t & 1][p] + tb_off;
     *reinterpret_cast<u32x4_t*>(d) = tb_first ? t1 : t0;
     *reinterpret_cast<u32x4_t*>((char*)((uintptr_t)d ^ 16u)) = tb_first ? t0 : t1;
   };
-  // The codes of rows 8rg..8rg+7, columns 4cg..4cg+3: row 2p in the low
-  // half of dword p, row 2p + 1 in its high half.
-  const int code_rslot = 8 * rg + (cg ^ rg);
-  auto read_codes = [&]() __attribute__((always_inline)) {
-    return *reinterpret_cast<const u32x4_t*>(scode[wave] + 16 * code_rslot);
-  };
-  // Column pair cp2 (columns 4cg + 2cp2, +1) of rows 8rg..8rg+7: 16
-  // lookups, two 16-byte stores of 8 rows each.
-  // Store address of column 4cg + c of the wave's slice, rows 8rg..8rg+7:
-  // wswz(32w + 4cg + c, rg) = (st0 ^ 16c) + 128c.
-  const uint32_t st0 = (uint32_t)((32 * wave + 4 * cg) * 128 + ((rg ^ cg ^ (4 * (cg & 1))) << 4));
-  auto dequant_cols = [&](char* dst, int cp2, const u32x4_t& cw) __attribute__((always_inline)) {
-    const uint32_t lb = opaque(lut_rg);
-    uint16_t v[2][8];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int c = 2 * cp2 + cc;
-        v[cc][2 * p] = lds_read_u16((lb | code_x2(cw[p], 4 * c)) + 256u * (2 * p));
-        v[cc][2 * p + 1] = lds_read_u16((lb | code_x2(cw[p], 16 + 4 * c)) + 256u * (2 * p + 1));
-      }
-    // all 16 lookups are issued before the first result is used (one wait
-    // instead of a chain of them); MFMAs, scalar and global-memory
-    // instructions may still move across
-    __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
-    const uint32_t sb = opaque(st0);
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int c = 2 * cp2 + cc;
-      u32x4_t o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) o[p] = (uint32_t)v[cc][2 * p] | ((uint32_t)v[cc][2 * p + 1] << 16);
-      *reinterpret_cast<u32x4_t*>(dst + ((sb ^ (uint32_t)(16 * c)) + 128u * c)) = o;
-    }
-  };
 
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // MFMA group g (0..15): n-half ks = g / 8, token block i = g % 8; the B
-  // fragments of the half are read at its first group.
-  // Fragment addresses: xswz(128wm + lr + 16i, 2kq + ks) = (a0 ^ 16ks) + 2048i
-  // and wswz(64wk + lr + 16j, 2kq + ks) = (b0 ^ 16(ks + 4(j & 1))) + 2048j.
-  const uint32_t a0 = (uint32_t)((128 * wm + lr) * 128 + (((2 * kq) ^ (lr & 7)) << 4));
-  const uint32_t b0 = (uint32_t)((64 * wk + lr) * 128 + (((2 * kq) ^ ((lr ^ (lr >> 2)) & 7)) << 4));
-  u32x4_t bfr[4];
-  uint32_t abase = 0;
-  auto mfma_group = [&](const char* ya, const char* wb, int g) __attribute__((always_inline)) {
-    const int ks = g >> 3, i = g & 7;
-    if (i == 0) {
-      const uint32_t bb = opaque(b0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4_t*>(wb + ((bb ^ (uint32_t)(16 * (ks + 4 * (j & 1)))) + 2048u * j));
-      abase = opaque(a0) ^ (uint32_t)(16 * ks);
-    }
-    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ya + abase + 2048u * i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
-  };
-  auto mfma_step = [&](const char* ya, const char* wb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int g = 0; g < 16; ++g) mfma_group(ya, wb, g);
-  };
-  // The two waves of a SIMD (w and w + 4, i.e. wm = 0 and 1) dequantize in
-  // different halves of the step (phase P = wm): while one issues table
-  // arithmetic and lookups, the other issues MFMAs.
-  auto mfma_step_dequant = [&](auto P, const char* ya, const char* wb, int t, char* dst,
-                               auto&& after_group) __attribute__((always_inline)) {
-    constexpr int g0 = decltype(P)::value ? 8 : 0;
-    u32x4_t cw;
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      mfma_group(ya, wb, g);
-      after_group(g);
-      if (g == g0) {
-        build_table(t);
-        cw = read_codes();
-      }
-      if (g == g0 + 1 || g == g0 + 3) dequant_cols(dst, (g - g0 - 1) / 2, cw);
-    }
-  };
-
-  // prologue: dY and weight data of step 0; dequantize step 0; weight data
-  // of step 1
+  Codes cn;
+  Consts cc, cnx;
+  // prologue: dY of step 0, codes and tables of steps 0 and 1, slice of step 0
   {
-    WRegs w0;
+    Codes c0;
+    Consts k0c;
     copy_y(sa0, 0);
-    load_w(w0, 0);
-    store_w(w0);
+    load_codes(c0, 0);
+    load_codes(cn, 1);
+    load_consts(k0c, 0);
+    load_consts(cnx, 1);
+    load_consts(cc, 2);
+    store_codes(0, c0);
+    store_codes(1, cn);
+    build_table(0, k0c);
+    build_table(1, cnx);
   }
+  __syncthreads();  // codes and tables of steps 0 and 1 in place
+  dequant_slice(std::true_type(), 0, 2 * p + 1, read_codes(0, 2 * p + 1), no_issue);
   wait_vmem();
-  __syncthreads();  // dY and weight data of step 0
-  build_table(0);
-  {
-    const u32x4_t cw = read_codes();
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) dequant_cols(sw[0], c2, cw);
-  }
-  {
-    WRegs w1;
-    load_w(w1, 1);
-    store_w(w1);
-  }
-  __syncthreads();
+  __syncthreads();  // step 0 in place
 
-  // Reduction steps 0 .. nsteps-2: copy dY of step s+1 into the other dY
-  // buffer and load the weight data of step s+2, issue the MFMAs of step s
-  // interleaved with the dequantization of step s+1 into the other Ŵᵀ
-  // buffer, then store the loaded weight data (the weight buffers are
-  // wave-private and were last read earlier in this iteration).  Weight data
-  // of step nsteps may be loaded: its reads stay inside the buffers or
-  // return zeros, and it is not used.  The loop is instantiated once per
-  // phase.
-  // Global reads queue behind one another in the compute unit's memory
-  // pipeline, and a wave cannot issue past a read that does not fit: the
-  // waves that dequantize first issue theirs at the top, the others one
-  // after each of their first MFMA groups.
-  auto main_loop = [&](auto P) __attribute__((always_inline)) {
-    constexpr bool early = decltype(P)::value == 0;
+  // Reduction steps 0 .. nsteps-2: load the codes of step s+2 and the
+  // constants of step s+3, build the tables of step s+2 (that buffer was
+  // last read in the previous iteration), dequantize slice 2p + 1 of step
+  // s+1 while copying dY of step s+1, then store the codes of step s+2.
+  // Weight data past the last step may be loaded: its reads stay inside the
+  // buffers or return zeros, and it is not used.
 #pragma unroll 1
-    for (int s = 0; s + 1 < nsteps; ++s) {
-      WRegs wr;
-      if constexpr (early) {
-        copy_y(sab((s + 1) & 1), s + 1);
-        load_w(wr, s + 2);
-      }
-      mfma_step_dequant(P, sab(s & 1), sw[s & 1], s + 1, sw[(s + 1) & 1], [&](int g) {
-        if constexpr (!early) {
-          if (g < 4) copy_y_part(sab((s + 1) & 1), s + 1, g);
-          if (g == 4) load_w(wr, s + 2);
-        }
-      });
-      store_w(wr);
-      wait_vmem();
-      __syncthreads();
-    }
-  };
-  if (wm == 0)
-    main_loop(std::integral_constant<int, 0>());
-  else
-    main_loop(std::integral_constant<int, 1>());
-  // last reduction step, copying LoRA step 0 (sU and AT2 tiles) into the
-  // other buffers; then the LoRA steps, unrolled
+  for (int s = 0; s + 1 < nsteps; ++s) {
+    char* const yn = sab((s + 1) & 1);
+    load_codes(cn, s + 2);
+    load_consts(cnx, s + 3);
+    build_table(s + 2, cc);
+    dequant_slice(std::true_type(), s + 1, 2 * p + 1, read_codes(s + 1, 2 * p + 1), [&](int h) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) copy_y_part(yn, s + 1, 4 * h + c);
+    });
+    store_codes(s + 2, cn);
+    cc = cnx;
+    wait_vmem();
+    __syncthreads();
+  }
+  // last reduction step: copy LoRA step 0 (sU and AT2 tiles) into the other
+  // buffers; then the LoRA steps
   copy_su(sab(nsteps & 1), 0);
   copy_at(sw[nsteps & 1], 0);
-  mfma_step(sab((nsteps - 1) & 1), sw[(nsteps - 1) & 1]);
   wait_vmem();
   __syncthreads();
-#pragma unroll
+#pragma unroll 1
   for (int l = 0; l < LSTEPS; ++l) {
     const int s = nsteps + l;
     if (l + 1 < LSTEPS) {
       copy_su(sab((s + 1) & 1), l + 1);
       copy_at(sw[(s + 1) & 1], l + 1);
     }
-    mfma_step(sab(s & 1), sw[s & 1]);
     wait_vmem();
     __syncthreads();
-  }
-
-  // epilogue: lane holds rows 128wm + 16i + 4kq + v of column k0 + 64wk + 16j + lr
-  int row0 = 128 * wm + 4 * kq, col0 = 64 * wk + lr;
-  asm volatile("" : "+v"(row0), "+v"(col0));
-  const bool full = (m0 + TM <= M) && (k0 + TK <= K);
-  if (dx_bf16) {
-    uint16_t* D = static_cast<uint16_t*>(dX) + (m0 + row0) * K + k0 + col0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
-          if (full || (m < M && k < K))
-            D[(16 * i + v) * K + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
-        }
-  } else {
-    float* D = static_cast<float*>(dX) + (m0 + row0) * K + k0 + col0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
-          if (full || (m < M && k < K)) D[(16 * i + v) * K + 16 * j] = acc[i][j][v];
-        }
   }
 }
 
