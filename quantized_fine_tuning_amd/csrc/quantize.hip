@@ -118,13 +118,15 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
   const int sub = lane % LPB, bl = lane / LPB;
   const int64_t chunk0 = (int64_t)blockIdx.x * kChunkBlocks;
 
-  // issue every load of the chunk first (buffer loads: blocks past the
-  // tensor read as zeros)
+  // a ring of RING loads in flight per lane (buffer loads: blocks past the
+  // tensor read as zeros): few registers, so that many workgroups fit on a
+  // compute unit and the grid runs in few rounds
+  constexpr int RING = 3;
   const rsrc_t rw = make_rsrc(W + chunk0 * kBlock, (nb - chunk0) * kBlock * (int64_t)sizeof(WT));
   const uint32_t voff = (uint32_t)(((wave * BPW + bl) * kBlock + sub * EPL) * sizeof(WT));
-  u32x4_t raw[ITERS];
+  u32x4_t raw[RING];
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) raw[it] = buf_load16(rw, voff, (uint32_t)(it * BPI * kBlock * sizeof(WT)));
+  for (int it = 0; it < RING; ++it) raw[it] = buf_load16(rw, voff, (uint32_t)(it * BPI * kBlock * sizeof(WT)));
   if (tid < 2 * kCodeCells) s_tab[tid] = code_cell(tid, cb);
   __syncthreads();
 
@@ -133,7 +135,9 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
     const int local = it * BPI + wave * BPW + bl;
     const int64_t b = chunk0 + local;
     WT v[EPL];
-    __builtin_memcpy(v, &raw[it], sizeof(v));
+    __builtin_memcpy(v, &raw[it % RING], sizeof(v));
+    if (it + RING < ITERS)
+      raw[it % RING] = buf_load16(rw, voff, (uint32_t)((it + RING) * BPI * kBlock * sizeof(WT)));
     float w[EPL];
     float m = 0.0f;
 #pragma unroll
