@@ -14,10 +14,13 @@
 //                         16 (fp32 input) or 8 (bf16 input) lanes per block,
 //                         absmax by xor shuffles; writes packed codes, the fp32
 //                         absmax (workspace) and the chunk's fp64 pairwise sum.
-//   tree_level_kernel     fp64 pairwise sums of aligned groups of 1024 values;
-//                         the last level writes mu = fl32(S / nb).
-//   dq_encode_kernel      one wave per 256 constants: d = c - mu, group max,
-//                         s = max / 448, e = E4M3(d / s).
+//   tree_level_kernel     fp64 pairwise sums of aligned groups of 1024 values,
+//                         only while more than 16 groups of them remain.
+//   dq_encode_kernel      every workgroup sums the remaining partial sums
+//                         itself in the same tree order and takes
+//                         mu = fl32(S / nb); then one wave per 256
+//                         constants: d = c - mu, group max, s = max / 448,
+//                         e = E4M3(d / s).
 //   nf4_dequant_kernel    32 elements per thread, 16-byte loads of codes,
 //                         64-byte contiguous stores of bf16.
 #include <type_traits>
@@ -29,6 +32,7 @@ namespace {
 
 constexpr int kChunkBlocks = 256;  // blocks per quantize workgroup
 constexpr int kLevelGroup = 1024;  // values per tree_level workgroup
+constexpr int kTailGroups = 16;    // groups the encode kernel sums itself
 
 template <typename WT>
 struct QTraits;
@@ -193,14 +197,11 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const WT* __restrict_
   if (tid == 0) partial[blockIdx.x] = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
 }
 
-// Pairwise fp64 sums of aligned groups of 1024 inputs (zero beyond n_in).  If
-// `mu` is non-null the launch has a single group and writes fl32(S / nb).
-__global__ __launch_bounds__(256) void tree_level_kernel(const double* __restrict__ in, int64_t n_in,
-                                                         double* __restrict__ out, float* mu,
-                                                         int64_t nb) {
-  __shared__ double s_w[4];
+// Pairwise fp64 sum of aligned group g of 1024 inputs (zero beyond n_in), by
+// a workgroup of 256 threads: every thread returns the same S.
+__device__ __forceinline__ double group_sum(const double* in, int64_t n_in, int64_t g, double* s_w) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t base = (int64_t)blockIdx.x * kLevelGroup + 4 * tid;
+  const int64_t base = g * kLevelGroup + 4 * tid;
   double x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = (base + i < n_in) ? in[base + i] : 0.0;
@@ -209,21 +210,47 @@ __global__ __launch_bounds__(256) void tree_level_kernel(const double* __restric
   for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
   if (lane == 0) s_w[wave] = v;
   __syncthreads();
-  if (tid == 0) {
-    const double S = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
-    out[blockIdx.x] = S;
-    if (mu) *mu = (float)(S / (double)nb);
-  }
+  const double S = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+  __syncthreads();  // s_w is reused by the next call
+  return S;
 }
 
+// One level of the tree: pairwise fp64 sums of aligned groups of 1024 inputs.
+__global__ __launch_bounds__(256) void tree_level_kernel(const double* __restrict__ in, int64_t n_in,
+                                                         double* __restrict__ out) {
+  __shared__ double s_w[4];
+  const double S = group_sum(in, n_in, blockIdx.x, s_w);
+  if (threadIdx.x == 0) out[blockIdx.x] = S;
+}
+
+// The last levels of the tree, then the encode.  Every workgroup sums the
+// n_in (<= kLevelGroup * kTailGroups) remaining partial sums itself, level by
+// level in the same pairwise order as tree_level_kernel (the same S in every
+// workgroup), and takes mu = fl32(S / nb); workgroup 0 also stores mu.  Then
+// one wave per 256-constant group: d = c - mu, group max, s = max / 448,
+// e = E4M3(d / s).
 __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                        const float* __restrict__ mu_p,
+                                                        const double* __restrict__ part, int64_t n_in,
+                                                        float* __restrict__ mu_out,
                                                         uint8_t* __restrict__ e,
                                                         float* __restrict__ s_out, int64_t ng) {
+  __shared__ double s_w[4];
+  __shared__ double s_lv[kTailGroups];
   const int lane = threadIdx.x & 63;
+  double S;
+  {
+    const int64_t n1 = (n_in + kLevelGroup - 1) / kLevelGroup;
+    for (int64_t gi = 0; gi < n1; ++gi) {
+      const double v = group_sum(part, n_in, gi, s_w);
+      if (threadIdx.x == 0) s_lv[gi] = v;
+    }
+    __syncthreads();
+    S = n1 == 1 ? s_lv[0] : group_sum(s_lv, n1, 0, s_w);
+  }
+  const float mu = (float)(S / (double)nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= ng) return;
-  const float mu = *mu_p;
   const int64_t i0 = g * kDqBlock + 4 * lane;
   float d[4];
   float m = 0.0f;
@@ -326,17 +353,18 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uin
                                          partial, cb);
     if (e != hipSuccess) return e;
   }
+  // tree levels of their own only while more partial sums remain than the
+  // encode kernel sums itself
   const double* in = partial;
   int64_t n_in = L.chunks;
-  for (int i = 0; L.lvl_len[i] != 0; ++i) {
-    const int64_t n_out = L.lvl_len[i];
+  for (int i = 0; n_in > (int64_t)kLevelGroup * kTailGroups; ++i) {
+    const int64_t n_out = (n_in + kLevelGroup - 1) / kLevelGroup;
     double* out = lvl[i & 1];
-    tree_level_kernel<<<(unsigned)n_out, 256, 0, st>>>(in, n_in, out, n_out == 1 ? mu : nullptr,
-                                                       L.nb);
+    tree_level_kernel<<<(unsigned)n_out, 256, 0, st>>>(in, n_in, out);
     in = out;
     n_in = n_out;
   }
-  dq_encode_kernel<<<(unsigned)((L.ng + 3) / 4), 256, 0, st>>>(absmax, L.nb, mu, e, s, L.ng);
+  dq_encode_kernel<<<(unsigned)((L.ng + 3) / 4), 256, 0, st>>>(absmax, L.nb, in, n_in, mu, e, s, L.ng);
   return hipGetLastError();
 }
 

@@ -121,6 +121,19 @@ def test_mlp_weight_sampled():
     assert np.array_equal(w_hat, o._blocks(rows, 0, W.shape[1] // 64))
 
 
+def test_large_tensor_tree_levels():
+    # 16448x16384 (270 M weights): 16448 partial sums of 256 constants, more
+    # than the encode kernel sums itself, so one tree level runs on its own
+    # first; mean, all E4M3 constants and all group scales exact
+    W = random_f32((16448, 16384), seed=4242, scale=0.02)
+    print("16448x16384 fp32 (tree levels)", flush=True)
+    qt = G.gpu_quantize(G.dev_f32(W))
+    o = G.SampledOracle(W)
+    assert G.host(qt.dq_mean).view(np.uint32)[0] == np.float32(o.mu).view(np.uint32)
+    assert np.array_equal(G.host(qt.absmax_e4m3), o.e)
+    assert np.array_equal(G.host(qt.dq_scale).view(np.uint32), o.s.view(np.uint32))
+
+
 def test_deterministic():
     W = random_f32((1024, 1024), seed=9, scale=0.02)
     Wd = G.dev_f32(W)
