@@ -28,10 +28,11 @@ Modules:
   int8       the absmax INT8 scheme of P3 (used as a pin of the absmax
              convention)
   footprint  storage arithmetic (bits per parameter, bytes per tensor)
+  adamw      the AdamW step on the LoRA parameters (fp32 states)
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (page values, closed forms, brute force,
 finite differences); none is "parity unpinned".
 """
 
-from . import nf4, linalg, int8, footprint  # noqa: F401
+from . import nf4, linalg, int8, footprint, adamw  # noqa: F401
