@@ -18,6 +18,10 @@ Extra objects on the JSON line:
                 M = 16, cycling through 64 quantized copies (about 0.55 GB, more
                 than twice the 256 MB last-level cache) so every launch streams
                 from HBM;
+  adamw         the AdamW step on bf16 LoRA parameters with fp32 moments (one
+                launch per step): the six LoRA matrices of the 7B MLP at r = 64,
+                and 8 tensors of 16 M parameters; kernel time and GB/s against
+                24 bytes per parameter;
   cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
                 of the same workload (quantize + dequantize + forward +
                 backward of the three linears at M = 4096).
@@ -269,6 +273,48 @@ def run_gemv(torch, q, args):
     return out
 
 
+def adamw_bytes(n, param_bytes=2):
+    """Bytes one AdamW step must move per parameter: the parameter, gradient
+    and two fp32 moments read, the parameter and the moments written."""
+    return n * (2 * param_bytes + 4 + 4 * 4)
+
+
+def run_adamw(torch, q, args):
+    """The AdamW step on bf16 LoRA parameters with fp32 moments, one launch per
+    step: (a) the six LoRA matrices of the 7B MLP at r = 64 (2.9 M
+    parameters); (b) 8 tensors of 16 M parameters (128 M, beyond the last-level
+    cache).  Kernel time from events attached to the launch."""
+    out = {}
+    cases = {"mlp_lora_r64": [64 * 4096, 11008 * 64, 64 * 4096, 11008 * 64, 64 * 11008, 4096 * 64],
+             "8x16M": [16 << 20] * 8}
+    for name, sizes in cases.items():
+        g = torch.Generator(device="cuda").manual_seed(7)
+        ts = []
+        for n in sizes:
+            p = (torch.randn(n, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            ts.append((p, torch.randn(n, device="cuda", generator=g) * 0.1,
+                       torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")))
+        n_iter = 50
+        evs = timed_events(torch, n_iter)
+        for i in range(5):
+            q.qlora_adamw_step(ts, 1e-4, 0.9, 0.999, 1e-8, 0.01, i + 1)
+        torch.cuda.synchronize()
+        for i in range(n_iter):
+            q.qlora_time_next_launch(q.QLORA_KERNEL_ADAMW, *evs[i])
+            q.qlora_adamw_step(ts, 1e-4, 0.9, 0.999, 1e-8, 0.01, i + 6)
+        torch.cuda.synchronize()
+        durs = sorted(a.elapsed_time(b) for a, b in evs)
+        med = statistics.median(durs)
+        nparams = sum(sizes)
+        nbytes = adamw_bytes(nparams)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        out[name] = {"params": nparams, "kernel_us_median": round(med * 1e3, 3),
+                     "bytes": nbytes, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] AdamW {name}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s")
+        del ts
+    return out
+
+
 def run_cpu_baseline():
     """The oracle as it stands, timed on the host over one whole step of the
     same workload: for each of the three linears, quantize + dequantize + fp64
@@ -331,6 +377,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
+    ap.add_argument("--no-adamw", action="store_true")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -349,6 +396,7 @@ def main():
         copy_calibration(torch, args.copy_calibration)
     mlp = run_mlp(torch, q, args)
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
+    adamw = None if args.no_adamw else run_adamw(torch, q, args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -372,6 +420,7 @@ def main():
         "roofline": mlp["roofline"],
         "cpu_baseline": cpu,
         "gemv": gemv,
+        "adamw": adamw,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in mlp["per_kernel"].items()},
     }

@@ -146,6 +146,42 @@ qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X,
                               qlora_dtype dx_dtype, float* dA, float* dB,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* One tensor of LoRA parameters for qlora_adamw_step (all device memory,
+ * 16-byte aligned when n > 0):
+ *   param       n elements, bf16 or fp32 (the call's param_dtype), updated in
+ *               place;
+ *   grad        fp32 [n] (e.g. dA or dB of qlora_linear_bwd);
+ *   exp_avg     fp32 [n], first moment, updated in place;
+ *   exp_avg_sq  fp32 [n], second moment, updated in place. */
+typedef struct {
+  void* param;
+  const float* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+  int64_t n;
+} qlora_adamw_tensor_t;
+#define QLORA_ADAMW_MAX_TENSORS 8
+
+/* One AdamW step on up to QLORA_ADAMW_MAX_TENSORS tensors in one launch.
+ * (P1 §七 table: only the LoRA parameters are trained, optimizer state exists
+ * only for them, in FP32; P4 §三 English derivation, item 3: a 32-bit AdamW
+ * over the LoRA parameters; P4 §四 ④: the parameters are kept in BF16.)
+ *   tensors      host array of `count` descriptors, 1 <= count <= 8;
+ *   param_dtype  QLORA_BF16 or QLORA_F32 for every tensor's param;
+ *   step         the 1-based step number t (bias corrections 1 - beta^t);
+ *   0 <= beta1, beta2 < 1, eps > 0, lr >= 0, weight_decay >= 0, all finite.
+ * With decay = fl(1 - fl(lr*wd)), omb = fl(1 - beta), bc = fl32(1 - beta^t)
+ * (power in fp64), sbc2 = fl(sqrt(bc2)) and step_size = fl(lr / bc1), each
+ * element takes, one binary32 rounding per operation and no fused
+ * multiply-add: p = fl(p*decay); m = fl(fl(b1*m) + fl(omb1*g));
+ * v = fl(fl(b2*v) + fl(fl(omb2*g)*g)); d = fl(fl(sqrt(v)/sbc2) + eps);
+ * p = fl(p - fl(step_size * fl(m/d))).  A bf16 parameter is widened exactly
+ * before and rounded to nearest-even after.  Tensors must not overlap. */
+qlora_status qlora_adamw_step(const qlora_adamw_tensor_t* tensors, int32_t count,
+                              qlora_dtype param_dtype, float lr, float beta1,
+                              float beta2, float eps, float weight_decay,
+                              int64_t step, void* stream);
+
 /* Benchmark instrumentation.  The next launch of kernel `kernel_id` made by
  * the calling thread is bracketed by hipEventRecord(start_event) and
  * hipEventRecord(stop_event) on that launch's stream; then the request is
@@ -157,6 +193,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X,
 #define QLORA_KERNEL_DX_GEMM 2    /* dequant-in-tile dX GEMM */
 #define QLORA_KERNEL_GEMV 3       /* dequant-GEMV forward (M <= 16) */
 #define QLORA_KERNEL_QUANTIZE 4   /* blockwise NF4 quantization kernel */
+#define QLORA_KERNEL_ADAMW 5      /* AdamW step kernel */
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event);
 
 /* The 16 fp32 NF4 levels as the library computes them (host memory, 16

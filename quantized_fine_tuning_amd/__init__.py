@@ -9,6 +9,7 @@ has not been built (``python -m quantized_fine_tuning_amd.build``).
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    QLORA_ADAMW_MAX_TENSORS,
     QLORA_BF16,
     QLORA_ERR_HIP,
     QLORA_ERR_INVALID_ARG,
@@ -20,10 +21,12 @@ from ._binding import (  # noqa: F401
     QLORA_KERNEL_GEMV,
     QLORA_KERNEL_NONE,
     QLORA_KERNEL_QUANTIZE,
+    QLORA_KERNEL_ADAMW,
     QLORA_OK,
     Nf4Tensor,
     QloraError,
     lib,
+    qlora_adamw_step,
     qlora_dequantize,
     qlora_linear_bwd,
     qlora_linear_fwd,

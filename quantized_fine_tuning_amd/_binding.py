@@ -26,13 +26,15 @@ QLORA_BF16 = 1
 
 EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
-           "qlora_time_next_launch")
+           "qlora_time_next_launch", "qlora_adamw_step")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
 QLORA_KERNEL_DX_GEMM = 2
 QLORA_KERNEL_GEMV = 3
 QLORA_KERNEL_QUANTIZE = 4
+QLORA_KERNEL_ADAMW = 5
+QLORA_ADAMW_MAX_TENSORS = 8
 
 
 class QloraError(RuntimeError):
@@ -52,6 +54,11 @@ class qlora_sizes_t(ctypes.Structure):
                 ("scale_bytes", ctypes.c_size_t), ("mean_bytes", ctypes.c_size_t),
                 ("quantize_ws_bytes", ctypes.c_size_t), ("fwd_ws_bytes", ctypes.c_size_t),
                 ("bwd_ws_bytes", ctypes.c_size_t)]
+
+
+class qlora_adamw_tensor_t(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("n", ctypes.c_int64)]
 
 
 def _load():
@@ -86,6 +93,8 @@ def _load():
     lib.qlora_last_error.restype = ctypes.c_char_p
     lib.qlora_time_next_launch.argtypes = [i32, vp, vp]
     lib.qlora_time_next_launch.restype = i32
+    lib.qlora_adamw_step.argtypes = [P(qlora_adamw_tensor_t), i32, i32, f32, f32, f32, f32, f32, i64, vp]
+    lib.qlora_adamw_step.restype = i32
     return lib
 
 
@@ -220,3 +229,27 @@ def qlora_time_next_launch(kernel_id: int, start_event=None, stop_event=None) ->
     s = ctypes.c_void_p(start_event.cuda_event) if start_event is not None else None
     e = ctypes.c_void_p(stop_event.cuda_event) if stop_event is not None else None
     _check(lib.qlora_time_next_launch(kernel_id, s, e))
+
+
+def qlora_adamw_step(tensors, lr: float, beta1: float, beta2: float, eps: float,
+                     weight_decay: float, step: int, stream=None) -> None:
+    """One AdamW step on up to QLORA_ADAMW_MAX_TENSORS tensors in one launch.
+    tensors: sequence of (param, grad, exp_avg, exp_avg_sq); every param is
+    bf16 or every param is fp32; grad and the moments are fp32 of the same
+    number of elements; all updated in place."""
+    tensors = list(tensors)
+    arr = (qlora_adamw_tensor_t * max(1, len(tensors)))()
+    dt = None
+    for i, (p, g, m, v) in enumerate(tensors):
+        d = _dtype(p, f"tensors[{i}].param")
+        if dt is not None and d != dt:
+            raise ValueError("every param must have the same dtype")
+        dt = d
+        n = p.numel()
+        if not (g.numel() == m.numel() == v.numel() == n):
+            raise ValueError(f"tensors[{i}]: element counts differ")
+        arr[i] = qlora_adamw_tensor_t(_ptr(p, "param"), _ptr(g, "grad"), _ptr(m, "exp_avg"),
+                                      _ptr(v, "exp_avg_sq"), n)
+    _check(lib.qlora_adamw_step(arr, len(tensors), QLORA_BF16 if dt is None else dt, float(lr),
+                                float(beta1), float(beta2), float(eps), float(weight_decay),
+                                int(step), _stream(stream)))

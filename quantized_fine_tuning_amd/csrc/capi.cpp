@@ -3,6 +3,7 @@
 // The declarations and their contracts are in include/qlora_nf4.h.
 #include "qlora_nf4.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -214,9 +215,50 @@ qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* d
                             static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_adamw_step(const qlora_adamw_tensor_t* tensors, int32_t count,
+                              qlora_dtype param_dtype, float lr, float beta1, float beta2, float eps,
+                              float weight_decay, int64_t step, void* stream) {
+  const char* fn = "qlora_adamw_step";
+  if (tensors == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: tensors is NULL", fn);
+  if (count < 1 || count > QLORA_ADAMW_MAX_TENSORS)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: count=%d outside [1, %d]", fn, count, QLORA_ADAMW_MAX_TENSORS);
+  if (param_dtype != QLORA_F32 && param_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: param_dtype=%d", fn, param_dtype);
+  if (step < 1) return fail(QLORA_ERR_INVALID_ARG, "%s: step=%lld < 1", fn, (long long)step);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: betas (%g, %g) outside [0, 1)", fn, beta1, beta2);
+  if (!(eps > 0.0f) || !(eps < INFINITY))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: eps=%g must be positive and finite", fn, eps);
+  if (!(lr >= 0.0f && lr < INFINITY) || !(weight_decay >= 0.0f && weight_decay < INFINITY))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: lr=%g, weight_decay=%g must be finite and >= 0", fn, lr,
+                weight_decay);
+  qnf4::AdamwArgs a{};
+  a.count = count;
+  uint64_t blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const qlora_adamw_tensor_t& t = tensors[i];
+    if (t.n < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: tensors[%d].n=%lld < 0", fn, i, (long long)t.n);
+    if (t.n > 0) {
+      const void* param = t.param;
+      const void* grad = t.grad;
+      const void* exp_avg = t.exp_avg;
+      const void* exp_avg_sq = t.exp_avg_sq;
+      CHECK_PTR(param);
+      CHECK_PTR(grad);
+      CHECK_PTR(exp_avg);
+      CHECK_PTR(exp_avg_sq);
+    }
+    blocks += qnf4::adamw_blocks(t.n);
+    a.t[i] = qnf4::AdamwTensor{t.param, t.grad, t.exp_avg, t.exp_avg_sq, t.n};
+  }
+  if (blocks > 0x7fffffffu) return fail(QLORA_ERR_INVALID_ARG, "%s: too many elements", fn);
+  return hip_status(fn, qnf4::launch_adamw(a, param_dtype == QLORA_BF16, lr, beta1, beta2, eps,
+                                           weight_decay, step, static_cast<hipStream_t>(stream)));
+}
+
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event) {
   const char* fn = "qlora_time_next_launch";
-  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_QUANTIZE)
+  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_ADAMW)
     return fail(QLORA_ERR_INVALID_ARG, "%s: unknown kernel id %d", fn, kernel_id);
   if (kernel_id != QLORA_KERNEL_NONE && (start_event == nullptr || stop_event == nullptr))
     return fail(QLORA_ERR_INVALID_ARG, "%s: NULL event", fn);

@@ -36,7 +36,7 @@ hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t s
   }
   return hipGetLastError();
 }
-enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4 };
+enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5 };
 
 // Round `x` up to a multiple of `a`.
 constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -135,5 +135,23 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                            const float* T_saved, void* dX, bool dx_bf16, float* dA, float* dB,
                            char* ws, const BwdLayout& L, hipStream_t st);
+
+// AdamW on the LoRA parameters ---------------------------------------------
+constexpr int kAdamwMaxTensors = 8;
+struct AdamwTensor {
+  void* p;         // parameter, bf16 or fp32
+  const float* g;  // gradient
+  float* m;        // first moment
+  float* v;        // second moment
+  int64_t n;
+};
+struct AdamwArgs {
+  AdamwTensor t[kAdamwMaxTensors];
+  uint32_t block0[kAdamwMaxTensors + 1];  // first block of each tensor (set by the launcher)
+  int count;
+};
+uint32_t adamw_blocks(int64_t n);
+hipError_t launch_adamw(AdamwArgs a, bool param_bf16, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, int64_t step, hipStream_t st);
 
 }  // namespace qnf4

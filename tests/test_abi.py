@@ -165,6 +165,43 @@ def test_backward_validation():
     assert call(ws=None) == q.QLORA_ERR_INVALID_ARG
 
 
+def test_adamw_validation():
+    lib = q.lib
+    T = q._binding.qlora_adamw_tensor_t
+
+    def arr(*ts):
+        a = (T * max(1, len(ts)))()
+        for i, t in enumerate(ts):
+            a[i] = t
+        return a
+
+    good = T(FAKE, FAKE, FAKE, FAKE, 1000)
+
+    def call(ts=(good,), count=None, dt=q.QLORA_BF16, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0,
+             step=1):
+        a = arr(*ts)
+        return lib.qlora_adamw_step(a, len(ts) if count is None else count, dt, lr, b1, b2, eps, wd,
+                                    step, None)
+
+    assert lib.qlora_adamw_step(None, 1, q.QLORA_BF16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert call(count=0) == q.QLORA_ERR_INVALID_ARG
+    assert call(ts=(good,) * 9) == q.QLORA_ERR_INVALID_ARG
+    assert call(dt=7) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert call(step=0) == q.QLORA_ERR_INVALID_ARG
+    assert call(b1=1.0) == q.QLORA_ERR_INVALID_ARG
+    assert call(b2=-0.1) == q.QLORA_ERR_INVALID_ARG
+    assert call(eps=0.0) == q.QLORA_ERR_INVALID_ARG
+    assert call(lr=-1.0) == q.QLORA_ERR_INVALID_ARG
+    assert call(wd=float("inf")) == q.QLORA_ERR_INVALID_ARG
+    assert call(ts=(T(FAKE, None, FAKE, FAKE, 10),)) == q.QLORA_ERR_INVALID_ARG
+    assert call(ts=(T(FAKE, FAKE, FAKE + 4, FAKE, 10),)) == q.QLORA_ERR_INVALID_ARG
+    assert "aligned" in lib.qlora_last_error().decode()
+    assert call(ts=(good, T(FAKE, FAKE, FAKE, FAKE, -1))) == q.QLORA_ERR_INVALID_ARG
+    # an empty tensor needs no pointers; all-empty enqueues nothing
+    assert call(ts=(T(None, None, None, None, 0),)) == q.QLORA_OK
+
+
 def test_status_strings():
     for s in range(5):
         assert q.lib.qlora_status_string(s).decode()
