@@ -29,10 +29,12 @@ Modules:
              convention)
   footprint  storage arithmetic (bits per parameter, bytes per tensor)
   adamw      the AdamW step on the LoRA parameters (fp32 states)
+  merge      the LoRA adapter merged into the dequantized weight (16-bit
+             output) and its re-quantization
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (page values, closed forms, brute force,
 finite differences); none is "parity unpinned".
 """
 
-from . import nf4, linalg, int8, footprint, adamw  # noqa: F401
+from . import nf4, linalg, int8, footprint, adamw, merge  # noqa: F401
