@@ -22,6 +22,10 @@ Extra objects on the JSON line:
                 launch per step): the six LoRA matrices of the 7B MLP at r = 64,
                 and 8 tensors of 16 M parameters; kernel time and GB/s against
                 24 bytes per parameter;
+  merge         the LoRA adapter merged into the dequantized weight (bf16
+                out) for the three 7B MLP weights at r = 64: kernel time and
+                GB/s; and on the gate weight, the error of re-quantizing the
+                merged weight, relative to it and to the adapter's change;
   cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
                 of the same workload (quantize + dequantize + forward +
                 backward of the three linears at M = 4096).
@@ -33,6 +37,7 @@ is taken from the summary under profiles/ and reported only while the
 kernel's sources are byte-identical to the ones profiled; otherwise null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-gemv] [--no-adamw] [--no-merge]
 """
 
 import argparse
@@ -315,6 +320,67 @@ def run_adamw(torch, q, args):
     return out
 
 
+def merge_bytes(N, K, r):
+    """Bytes the merge kernel must move: packed codes, e4m3 constants, group
+    scales, mean, A and B in; the 16-bit merged weight out."""
+    nb = N * K // 64
+    return N * K // 2 + nb + 4 * ((nb + 255) // 256) + 4 + 2 * r * K + 2 * N * r + 2 * N * K
+
+
+def run_merge(torch, q, args):
+    """The LoRA merge (bf16 output) of the 7B MLP's three weights at r = 64:
+    median kernel time per weight from events attached to the launch; then,
+    on the gate weight, what re-quantizing the merged weight costs in error."""
+    from workloads import Inputs
+
+    w = Inputs(3)
+    r, alpha = w.w.rank, w.w.alpha
+    out = {"layers": {}}
+    for li, (name, N, K) in enumerate(w.w.layers):
+        Wd = torch.from_numpy(w.weight(li)).cuda()
+        qt = q.Nf4Tensor.empty(N, K)
+        q.qlora_nf4_quantize(Wd, qt, q.workspace(q.qlora_nf4_sizes(N, K, 0, r)["quantize_ws_bytes"]))
+        A, B = dev_bf16(torch, w.lora_A(li)), dev_bf16(torch, w.lora_B(li))
+        Wm = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+        n_iter = 30
+        evs = timed_events(torch, n_iter)
+        for _ in range(3):
+            q.qlora_merge_lora(qt, A, B, r, alpha, Wm)
+        torch.cuda.synchronize()
+        for i in range(n_iter):
+            q.qlora_time_next_launch(q.QLORA_KERNEL_MERGE, *evs[i])
+            q.qlora_merge_lora(qt, A, B, r, alpha, Wm)
+        torch.cuda.synchronize()
+        med = statistics.median(a.elapsed_time(b) for a, b in evs)
+        nbytes = merge_bytes(N, K, r)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        out["layers"][name] = {"N": N, "K": K, "kernel_us_median": round(med * 1e3, 3), "bytes": nbytes,
+                               "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] merge {name} {N}x{K}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s")
+        if li == 0:
+            # re-quantization of the merged weight (the error merging and
+            # re-quantizing brings back); norms in fp64 on the device
+            W_hat = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+            q.qlora_dequantize(qt, W_hat)
+            qt2 = q.Nf4Tensor.empty(N, K)
+            q.qlora_nf4_quantize(Wm, qt2, q.workspace(q.qlora_nf4_sizes(N, K, 0, r)["quantize_ws_bytes"]))
+            back = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+            q.qlora_dequantize(qt2, back)
+            f = lambda t: t.double()  # noqa: E731
+            delta = f(Wm) - f(W_hat)
+            out["requantize_gate"] = {
+                "nf4_error_vs_weight": float((f(W_hat) - Wd.double()).norm() / Wd.double().norm()),
+                "requant_error_vs_merged": float((f(back) - f(Wm)).norm() / f(Wm).norm()),
+                "adapter_delta_norm_vs_weight": float(delta.norm() / f(Wm).norm()),
+                "requant_error_vs_adapter_delta": float((f(back) - f(Wm)).norm() / delta.norm()),
+                "codes_changed_fraction": float((qt2.codes != qt.codes).double().mean()),
+            }
+            log(f"[bench] re-quantized merge: {out['requantize_gate']}")
+            del W_hat, qt2, back, delta
+        del Wd, qt, A, B, Wm
+    return out
+
+
 def run_cpu_baseline():
     """The oracle as it stands, timed on the host over one whole step of the
     same workload: for each of the three linears, quantize + dequantize + fp64
@@ -378,6 +444,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-adamw", action="store_true")
+    ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -397,6 +464,7 @@ def main():
     mlp = run_mlp(torch, q, args)
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
     adamw = None if args.no_adamw else run_adamw(torch, q, args)
+    merge = None if args.no_merge else run_merge(torch, q, args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -421,6 +489,7 @@ def main():
         "cpu_baseline": cpu,
         "gemv": gemv,
         "adamw": adamw,
+        "merge": merge,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in mlp["per_kernel"].items()},
     }

@@ -47,6 +47,7 @@ typedef int32_t qlora_status;
 typedef int32_t qlora_dtype;
 #define QLORA_F32 0
 #define QLORA_BF16 1
+#define QLORA_F16 2  /* output of qlora_merge_lora only */
 
 /* One NF4 + double-quantized weight (P4 §三 English derivation; P1 §二).
  * All four arrays are device memory:
@@ -182,6 +183,25 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor_t* tensors, int32_t count
                               float beta2, float eps, float weight_decay,
                               int64_t step, void* stream);
 
+/* The LoRA adapter merged into the dequantized weight, for serving (P5,
+ * follow-up 1: the fine-tuned model converted once to 16 bits with the LoRA
+ * weights merged into the dequantized weight; P1 §七 dataflow figure: the
+ * layer is X·(Ŵ + s·B·A)ᵀ; P1 §五: merging and re-quantizing can bring the
+ * quantization error back -- re-quantize by passing a bf16 result to
+ * qlora_nf4_quantize):
+ *   W_m[n][k] = RND(fl32(ŵ[n][k] + fl32(s · Σ_j B[n][j]·A[j][k]))),
+ * with ŵ the dequantized bf16 weight of qlora_dequantize, s = fl32(alpha/r),
+ * the rank-r sum accumulated in fp32 and RND the round to nearest even into
+ * out_dtype.  Against the exact sum rounded once to out_dtype the result is
+ * within one unit in the last place.
+ *   W          NF4 weight [N, K];
+ *   A          device bf16 [r, K];  B  device bf16 [N, r];  1 <= r <= 256;
+ *   out        device [N, K], QLORA_BF16 or QLORA_F16 (out_dtype);
+ * Limits: N*K <= 2^31, r*K <= 2^29, N*r <= 2^29.  No workspace. */
+qlora_status qlora_merge_lora(const qlora_nf4_t* W, const void* A,
+                              const void* B, int32_t r, float alpha,
+                              void* out, qlora_dtype out_dtype, void* stream);
+
 /* Benchmark instrumentation.  The next launch of kernel `kernel_id` made by
  * the calling thread is bracketed by hipEventRecord(start_event) and
  * hipEventRecord(stop_event) on that launch's stream; then the request is
@@ -194,6 +214,7 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor_t* tensors, int32_t count
 #define QLORA_KERNEL_GEMV 3       /* dequant-GEMV forward (M <= 16) */
 #define QLORA_KERNEL_QUANTIZE 4   /* blockwise NF4 quantization kernel */
 #define QLORA_KERNEL_ADAMW 5      /* AdamW step kernel */
+#define QLORA_KERNEL_MERGE 6      /* LoRA merge kernel */
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event);
 
 /* The 16 fp32 NF4 levels as the library computes them (host memory, 16

@@ -3,7 +3,7 @@
 The computation lives in libqlora_nf4.so (hand-written HIP kernels behind the C
 ABI of include/qlora_nf4.h); this package is a thin ctypes binding whose
 functions carry the C entry points' names.  Importing it fails if the library
-has not been built (``python -m quantized_fine_tuning_amd.build``).
+has not been built (``python quantized_fine_tuning_amd/build.py``).
 """
 
 from ._binding import (  # noqa: F401
@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     QLORA_ADAMW_MAX_TENSORS,
     QLORA_BF16,
+    QLORA_F16,
     QLORA_ERR_HIP,
     QLORA_ERR_INVALID_ARG,
     QLORA_ERR_UNSUPPORTED_DTYPE,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     QLORA_KERNEL_NONE,
     QLORA_KERNEL_QUANTIZE,
     QLORA_KERNEL_ADAMW,
+    QLORA_KERNEL_MERGE,
     QLORA_OK,
     Nf4Tensor,
     QloraError,
@@ -30,6 +32,7 @@ from ._binding import (  # noqa: F401
     qlora_dequantize,
     qlora_linear_bwd,
     qlora_linear_fwd,
+    qlora_merge_lora,
     qlora_nf4_codebook,
     qlora_nf4_quantize,
     qlora_nf4_sizes,

@@ -23,10 +23,11 @@ QLORA_ERR_WORKSPACE_TOO_SMALL = 3
 QLORA_ERR_HIP = 4
 QLORA_F32 = 0
 QLORA_BF16 = 1
+QLORA_F16 = 2
 
 EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
-           "qlora_time_next_launch", "qlora_adamw_step")
+           "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -34,6 +35,7 @@ QLORA_KERNEL_DX_GEMM = 2
 QLORA_KERNEL_GEMV = 3
 QLORA_KERNEL_QUANTIZE = 4
 QLORA_KERNEL_ADAMW = 5
+QLORA_KERNEL_MERGE = 6
 QLORA_ADAMW_MAX_TENSORS = 8
 
 
@@ -71,7 +73,7 @@ def _load():
 
     if not LIB_PATH.exists():
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m quantized_fine_tuning_amd.build` (hipcc, gfx950)")
+                          "`python quantized_fine_tuning_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(str(LIB_PATH))
     i64, i32, vp, sz, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
     P = ctypes.POINTER
@@ -95,6 +97,8 @@ def _load():
     lib.qlora_time_next_launch.restype = i32
     lib.qlora_adamw_step.argtypes = [P(qlora_adamw_tensor_t), i32, i32, f32, f32, f32, f32, f32, i64, vp]
     lib.qlora_adamw_step.restype = i32
+    lib.qlora_merge_lora.argtypes = [P(qlora_nf4_t), vp, vp, i32, f32, vp, i32, vp]
+    lib.qlora_merge_lora.restype = i32
     return lib
 
 
@@ -131,7 +135,9 @@ def _dtype(t, name: str) -> int:
         return QLORA_F32
     if t.dtype == torch.bfloat16:
         return QLORA_BF16
-    raise ValueError(f"{name}: dtype {t.dtype} is neither float32 nor bfloat16")
+    if t.dtype == torch.float16:
+        return QLORA_F16  # (accepted by qlora_merge_lora's output only)
+    raise ValueError(f"{name}: dtype {t.dtype} is not float32, bfloat16 or float16")
 
 
 def _stream(stream):
@@ -253,3 +259,10 @@ def qlora_adamw_step(tensors, lr: float, beta1: float, beta2: float, eps: float,
     _check(lib.qlora_adamw_step(arr, len(tensors), QLORA_BF16 if dt is None else dt, float(lr),
                                 float(beta1), float(beta2), float(eps), float(weight_decay),
                                 int(step), _stream(stream)))
+
+
+def qlora_merge_lora(W: Nf4Tensor, A, B, r: int, alpha: float, out, stream=None) -> None:
+    """out [N, K] (bf16 or fp16) = Ŵ + (alpha / r)·B·A, rounded once."""
+    st = W.c_struct()
+    _check(lib.qlora_merge_lora(ctypes.byref(st), _ptr(A, "A"), _ptr(B, "B"), r, float(alpha),
+                                _ptr(out, "out"), _dtype(out, "out"), _stream(stream)))

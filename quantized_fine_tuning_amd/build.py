@@ -1,6 +1,8 @@
 """Builds libqlora_nf4.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m quantized_fine_tuning_amd.build
+    python quantized_fine_tuning_amd/build.py
+
+(run as a file: importing the package first would load the library it builds)
 
 Flags: -O3; no fast-math; fp contraction off (every fp32 operation rounds once,
 which the bit-exact parts of the library rely on); correctly rounded fp32
@@ -20,7 +22,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"  # the C ABI header
 LIB = PKG / "libqlora_nf4.so"
-SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "linear.hip", "lora.hip", "fwd.hip", "dx.hip", "gemv.hip", "adamw.hip"]
+SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "linear.hip", "lora.hip", "fwd.hip", "dx.hip", "gemv.hip", "adamw.hip", "merge.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -256,9 +256,29 @@ qlora_status qlora_adamw_step(const qlora_adamw_tensor_t* tensors, int32_t count
                                            weight_decay, step, static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_merge_lora(const qlora_nf4_t* W, const void* A, const void* B, int32_t r, float alpha,
+                              void* out, qlora_dtype out_dtype, void* stream) {
+  const char* fn = "qlora_merge_lora";
+  qlora_status st = check_tensor(fn, W);
+  if (st != QLORA_OK) return st;
+  if ((st = check_rank(fn, r)) != QLORA_OK) return st;
+  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype=%d (expected BF16 or F16)", fn, out_dtype);
+  const int64_t N = W->n_rows, K = W->n_cols;
+  if (N > (int64_t(1) << 31) / K || (int64_t)r * K > (int64_t(1) << 29) || N * r > (int64_t(1) << 29))
+    return fail(QLORA_ERR_INVALID_ARG, "%s: N*K, r*K or N*r too large", fn);
+  CHECK_PTR(A);
+  CHECK_PTR(B);
+  CHECK_PTR(out);
+  return hip_status(fn, qnf4::launch_merge(view(W), static_cast<const uint16_t*>(A),
+                                           static_cast<const uint16_t*>(B), r, alpha / (float)r,
+                                           static_cast<uint16_t*>(out), out_dtype == QLORA_F16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event) {
   const char* fn = "qlora_time_next_launch";
-  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_ADAMW)
+  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_MERGE)
     return fail(QLORA_ERR_INVALID_ARG, "%s: unknown kernel id %d", fn, kernel_id);
   if (kernel_id != QLORA_KERNEL_NONE && (start_event == nullptr || stop_event == nullptr))
     return fail(QLORA_ERR_INVALID_ARG, "%s: NULL event", fn);

@@ -36,7 +36,7 @@ hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t s
   }
   return hipGetLastError();
 }
-enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5 };
+enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5, kKernMerge = 6 };
 
 // Round `x` up to a multiple of `a`.
 constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -153,5 +153,9 @@ struct AdamwArgs {
 uint32_t adamw_blocks(int64_t n);
 hipError_t launch_adamw(AdamwArgs a, bool param_bf16, float lr, float beta1, float beta2, float eps,
                         float weight_decay, int64_t step, hipStream_t st);
+
+// LoRA merge -----------------------------------------------------------------
+hipError_t launch_merge(const Nf4View& W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                        uint16_t* out, bool out_f16, hipStream_t st);
 
 }  // namespace qnf4

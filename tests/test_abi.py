@@ -202,6 +202,31 @@ def test_adamw_validation():
     assert call(ts=(T(None, None, None, None, 0),)) == q.QLORA_OK
 
 
+def test_merge_validation():
+    lib = q.lib
+    m = lib.qlora_merge_lora
+
+    def call(d=None, A=FAKE, B=FAKE, r=8, out=FAKE, od=q.QLORA_BF16):
+        d = desc() if d is None else d
+        return m(ctypes.byref(d), A, B, r, 16.0, out, od, None)
+
+    assert call(od=q.QLORA_F32) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert call(od=7) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert call(r=0) == q.QLORA_ERR_INVALID_ARG
+    assert call(r=257) == q.QLORA_ERR_INVALID_ARG
+    assert call(A=None) == q.QLORA_ERR_INVALID_ARG
+    assert call(B=FAKE + 2) == q.QLORA_ERR_INVALID_ARG
+    assert call(out=None) == q.QLORA_ERR_INVALID_ARG
+    assert call(d=desc(k=100)) == q.QLORA_ERR_INVALID_ARG
+    # 2^31 parameters is the limit of the 32-bit code offsets
+    assert call(d=desc(n=1 << 16, k=1 << 16)) == q.QLORA_ERR_INVALID_ARG
+    assert "too large" in lib.qlora_last_error().decode()
+    assert m(None, FAKE, FAKE, 8, 16.0, FAKE, q.QLORA_BF16, None) == q.QLORA_ERR_INVALID_ARG
+    # F16 is an output of the merge only
+    d = desc()
+    assert lib.qlora_dequantize(ctypes.byref(d), FAKE, q.QLORA_F16, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+
+
 def test_status_strings():
     for s in range(5):
         assert q.lib.qlora_status_string(s).decode()
