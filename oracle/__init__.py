@@ -31,10 +31,12 @@ Modules:
   adamw      the AdamW step on the LoRA parameters (fp32 states)
   merge      the LoRA adapter merged into the dequantized weight (16-bit
              output) and its re-quantization
+  variants   comparison formats: NF4 without double quantization, absmax
+             INT4 and INT8 (fp32 constant per 64-block)
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (page values, closed forms, brute force,
 finite differences); none is "parity unpinned".
 """
 
-from . import nf4, linalg, int8, footprint, adamw, merge  # noqa: F401
+from . import nf4, linalg, int8, footprint, adamw, merge, variants  # noqa: F401
