@@ -26,6 +26,10 @@ Extra objects on the JSON line:
                 out) for the three 7B MLP weights at r = 64: kernel time and
                 GB/s; and on the gate weight, the error of re-quantizing the
                 merged weight, relative to it and to the adapter's change;
+  formats       the comparison formats (NF4 without double quantization,
+                absmax INT4 and INT8) on the q_proj weight: reconstruction
+                error against the fp32 weight, and dequant-GEMV time and GB/s
+                at M = 1 and 16;
   cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
                 of the same workload (quantize + dequantize + forward +
                 backward of the three linears at M = 4096).
@@ -37,7 +41,7 @@ is taken from the summary under profiles/ and reported only while the
 kernel's sources are byte-identical to the ones profiled; otherwise null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-gemv] [--no-adamw] [--no-merge]
+                       [--no-gemv] [--no-adamw] [--no-merge] [--no-formats]
 """
 
 import argparse
@@ -381,6 +385,66 @@ def run_merge(torch, q, args):
     return out
 
 
+def format_gemv_bytes(fmt, N, K, M):
+    """Bytes the comparison-format GEMV must move: codes, fp32 block
+    constants and X in; Y (bf16) out."""
+    code_bytes = N * K if fmt == "int8" else N * K // 2
+    return code_bytes + 4 * (N * K // 64) + 2 * M * K + 2 * M * N
+
+
+def run_formats(torch, q, args):
+    """The comparison formats (NF4 with double quantization off, absmax INT4
+    and INT8, one fp32 constant per 64-block) on the 4096 x 4096 q_proj weight
+    of the GEMV workload: reconstruction error of each against the fp32
+    weight (NF4 with double quantization beside them), and the dequant-GEMV
+    kernel time at M = 1 and 16 over copies that do not fit the last-level
+    cache."""
+    from workloads import Inputs
+
+    w = Inputs(2)
+    N, K = w.shape(0)
+    Wd = torch.from_numpy(w.weight(0)).cuda()
+    W64 = Wd.double()
+    out = {"weight": [N, K], "formats": {}}
+    rel = lambda a: float((a.double() - W64).norm() / W64.norm())  # noqa: E731
+    # NF4 with double quantization, the main format
+    qt = q.Nf4Tensor.empty(N, K)
+    q.qlora_nf4_quantize(Wd, qt, q.workspace(q.qlora_nf4_sizes(N, K, 0, 1)["quantize_ws_bytes"]))
+    back = torch.empty(N, K, dtype=torch.bfloat16, device="cuda")
+    q.qlora_dequantize(qt, back)
+    out["nf4_dq_rel_error"] = rel(back)
+    del qt
+    for fmt in ("nf4", "int4", "int8"):
+        copies = []
+        for _ in range(args.gemv_copies):
+            t = q.QTensor.empty(N, K, fmt)
+            q.qlora_quantize_format(Wd, t)
+            copies.append(t)
+        q.qlora_dequantize_format(copies[0], back)
+        rec = {"rel_error": rel(back), "bits_per_weight": (8 if fmt == "int8" else 4) + 32 / 64}
+        for M in (1, 16):
+            X = dev_bf16(torch, w.X(0, M))
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            n = args.gemv_iters
+            evs = timed_events(torch, n)
+            for i in range(10):
+                q.qlora_gemv_format(copies[i % len(copies)], X, Y)
+            torch.cuda.synchronize()
+            for i in range(n):
+                q.qlora_time_next_launch(q.QLORA_KERNEL_FORMAT_GEMV, *evs[i])
+                q.qlora_gemv_format(copies[i % len(copies)], X, Y)
+            torch.cuda.synchronize()
+            med = statistics.median(a.elapsed_time(b) for a, b in evs)
+            nbytes = format_gemv_bytes(fmt, N, K, M)
+            gbs = nbytes / (med * 1e-3) / 1e9
+            rec[f"gemv_m{M}"] = {"kernel_us_median": round(med * 1e3, 3), "bytes": nbytes,
+                                 "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        out["formats"][fmt] = rec
+        log(f"[bench] format {fmt}: {rec}")
+        del copies
+    return out
+
+
 def run_cpu_baseline():
     """The oracle as it stands, timed on the host over one whole step of the
     same workload: for each of the three linears, quantize + dequantize + fp64
@@ -445,6 +509,7 @@ def main():
     ap.add_argument("--no-gemv", action="store_true")
     ap.add_argument("--no-adamw", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--no-formats", action="store_true")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -465,6 +530,7 @@ def main():
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
     adamw = None if args.no_adamw else run_adamw(torch, q, args)
     merge = None if args.no_merge else run_merge(torch, q, args)
+    formats = None if args.no_formats else run_formats(torch, q, args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -490,6 +556,7 @@ def main():
         "gemv": gemv,
         "adamw": adamw,
         "merge": merge,
+        "formats": formats,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in mlp["per_kernel"].items()},
     }

@@ -202,6 +202,48 @@ qlora_status qlora_merge_lora(const qlora_nf4_t* W, const void* A,
                               const void* B, int32_t r, float alpha,
                               void* out, qlora_dtype out_dtype, void* stream);
 
+/* Comparison formats of the frozen weight (a second workload: P4 §三, NF4's
+ * fp32 block constants before double quantization; P2 §4.1 and P4 trade-off
+ * ②, uniform 4-bit integers against NF4; P3 公式导读 2, absmax INT8).  Each
+ * keeps one fp32 absmax c per 64-block of the flattened weight and no double
+ * quantization; w' = RNE_bf16(fl32(L[code]·c)):
+ *   QLORA_FMT_NF4   NF4 codes (those of qlora_nf4_quantize), packed 2 per
+ *                   byte; L = the NF4 levels;
+ *   QLORA_FMT_INT4  k = round(fl32(w · fl32(7/c))), halves away from zero,
+ *                   k in [-7, 7], stored as the nibble k + 8, packed 2 per
+ *                   byte; L = fl32(k/7);
+ *   QLORA_FMT_INT8  the same with 127, one byte per weight (two's complement);
+ *                   L = fl32(k/127).
+ * A block of zeros gets the zero code.  codes: N*K/2 bytes (NF4, INT4) or
+ * N*K bytes (INT8); absmax: N*K/64 floats; both device memory. */
+#define QLORA_FMT_NF4 1
+#define QLORA_FMT_INT4 2
+#define QLORA_FMT_INT8 3
+typedef struct {
+  int64_t n_rows;    /* N */
+  int64_t n_cols;    /* K, a multiple of 64 */
+  int32_t format;    /* QLORA_FMT_* */
+  uint8_t* codes;
+  float* absmax;
+} qlora_qtensor_t;
+
+/* Quantize W [N, K] (fp32 or bf16, device) into `out`'s format; no
+ * workspace.  Errors as qlora_nf4_quantize, plus an unknown format. */
+qlora_status qlora_quantize_format(const void* W, qlora_dtype w_dtype,
+                                   int64_t N, int64_t K, qlora_qtensor_t* out,
+                                   void* stream);
+
+/* w' of every weight into out [N, K] bf16 (device; out_dtype QLORA_BF16). */
+qlora_status qlora_dequantize_format(const qlora_qtensor_t* q, void* out,
+                                     qlora_dtype out_dtype, void* stream);
+
+/* The dequant-GEMV Y = X·Ŵᵀ for 0 <= M <= 16 tokens (no adapter): X device
+ * bf16 [M, K]; Y device [M, N], bf16 or fp32 (y_dtype); fp32 accumulation.
+ * Limits: codes and absmax of one 16-row slice below 2^31 bytes. */
+qlora_status qlora_gemv_format(const qlora_qtensor_t* q, const void* X,
+                               int64_t M, void* Y, qlora_dtype y_dtype,
+                               void* stream);
+
 /* Benchmark instrumentation.  The next launch of kernel `kernel_id` made by
  * the calling thread is bracketed by hipEventRecord(start_event) and
  * hipEventRecord(stop_event) on that launch's stream; then the request is
@@ -215,6 +257,7 @@ qlora_status qlora_merge_lora(const qlora_nf4_t* W, const void* A,
 #define QLORA_KERNEL_QUANTIZE 4   /* blockwise NF4 quantization kernel */
 #define QLORA_KERNEL_ADAMW 5      /* AdamW step kernel */
 #define QLORA_KERNEL_MERGE 6      /* LoRA merge kernel */
+#define QLORA_KERNEL_FORMAT_GEMV 7 /* dequant-GEMV of the comparison formats */
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event);
 
 /* The 16 fp32 NF4 levels as the library computes them (host memory, 16

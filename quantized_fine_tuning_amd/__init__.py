@@ -24,8 +24,10 @@ from ._binding import (  # noqa: F401
     QLORA_KERNEL_QUANTIZE,
     QLORA_KERNEL_ADAMW,
     QLORA_KERNEL_MERGE,
+    QLORA_KERNEL_FORMAT_GEMV,
     QLORA_OK,
     Nf4Tensor,
+    QTensor,
     QloraError,
     lib,
     qlora_adamw_step,
@@ -33,6 +35,10 @@ from ._binding import (  # noqa: F401
     qlora_linear_bwd,
     qlora_linear_fwd,
     qlora_merge_lora,
+    qlora_quantize_format,
+    qlora_dequantize_format,
+    qlora_gemv_format,
+    qlora_qtensor_t,
     qlora_nf4_codebook,
     qlora_nf4_quantize,
     qlora_nf4_sizes,

@@ -27,7 +27,8 @@ QLORA_F16 = 2
 
 EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
-           "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora")
+           "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora",
+           "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -36,6 +37,11 @@ QLORA_KERNEL_GEMV = 3
 QLORA_KERNEL_QUANTIZE = 4
 QLORA_KERNEL_ADAMW = 5
 QLORA_KERNEL_MERGE = 6
+QLORA_KERNEL_FORMAT_GEMV = 7
+QLORA_FMT_NF4 = 1
+QLORA_FMT_INT4 = 2
+QLORA_FMT_INT8 = 3
+FORMATS = {"nf4": QLORA_FMT_NF4, "int4": QLORA_FMT_INT4, "int8": QLORA_FMT_INT8}
 QLORA_ADAMW_MAX_TENSORS = 8
 
 
@@ -61,6 +67,11 @@ class qlora_sizes_t(ctypes.Structure):
 class qlora_adamw_tensor_t(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
                 ("exp_avg_sq", ctypes.c_void_p), ("n", ctypes.c_int64)]
+
+
+class qlora_qtensor_t(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64), ("format", ctypes.c_int32),
+                ("codes", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
 
 
 def _load():
@@ -99,6 +110,11 @@ def _load():
     lib.qlora_adamw_step.restype = i32
     lib.qlora_merge_lora.argtypes = [P(qlora_nf4_t), vp, vp, i32, f32, vp, i32, vp]
     lib.qlora_merge_lora.restype = i32
+    lib.qlora_quantize_format.argtypes = [vp, i32, i64, i64, P(qlora_qtensor_t), vp]
+    lib.qlora_dequantize_format.argtypes = [P(qlora_qtensor_t), vp, i32, vp]
+    lib.qlora_gemv_format.argtypes = [P(qlora_qtensor_t), vp, i64, vp, i32, vp]
+    for name in ("qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format"):
+        getattr(lib, name).restype = i32
     return lib
 
 
@@ -266,3 +282,40 @@ def qlora_merge_lora(W: Nf4Tensor, A, B, r: int, alpha: float, out, stream=None)
     st = W.c_struct()
     _check(lib.qlora_merge_lora(ctypes.byref(st), _ptr(A, "A"), _ptr(B, "B"), r, float(alpha),
                                 _ptr(out, "out"), _dtype(out, "out"), _stream(stream)))
+
+
+class QTensor:
+    """A weight in one of the comparison formats ("nf4", "int4", "int8"):
+    codes (uint8) and one fp32 absmax per 64-block, device tensors."""
+
+    def __init__(self, n_rows: int, n_cols: int, fmt: str, codes, absmax):
+        self.n_rows, self.n_cols, self.fmt = n_rows, n_cols, fmt
+        self.codes, self.absmax = codes, absmax
+
+    @classmethod
+    def empty(cls, n_rows: int, n_cols: int, fmt: str, device="cuda"):
+        torch = _torch()
+        nbytes = n_rows * n_cols if fmt == "int8" else n_rows * n_cols // 2
+        return cls(n_rows, n_cols, fmt, torch.empty(nbytes, dtype=torch.uint8, device=device),
+                   torch.empty(n_rows * n_cols // 64, dtype=torch.float32, device=device))
+
+    def c_struct(self) -> qlora_qtensor_t:
+        return qlora_qtensor_t(self.n_rows, self.n_cols, FORMATS[self.fmt], _ptr(self.codes, "codes"),
+                               _ptr(self.absmax, "absmax"))
+
+
+def qlora_quantize_format(W, out: QTensor, stream=None) -> None:
+    N, K = W.shape
+    st = out.c_struct()
+    _check(lib.qlora_quantize_format(_ptr(W, "W"), _dtype(W, "W"), N, K, ctypes.byref(st), _stream(stream)))
+
+
+def qlora_dequantize_format(q: QTensor, out, stream=None) -> None:
+    st = q.c_struct()
+    _check(lib.qlora_dequantize_format(ctypes.byref(st), _ptr(out, "out"), _dtype(out, "out"), _stream(stream)))
+
+
+def qlora_gemv_format(q: QTensor, X, Y, stream=None) -> None:
+    st = q.c_struct()
+    _check(lib.qlora_gemv_format(ctypes.byref(st), _ptr(X, "X"), X.shape[0], _ptr(Y, "Y"), _dtype(Y, "Y"),
+                                 _stream(stream)))

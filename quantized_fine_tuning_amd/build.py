@@ -22,7 +22,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 INCLUDE = PKG.parent / "include"  # the C ABI header
 LIB = PKG / "libqlora_nf4.so"
-SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "linear.hip", "lora.hip", "fwd.hip", "dx.hip", "gemv.hip", "adamw.hip", "merge.hip"]
+SOURCES = ["codebook.cpp", "capi.cpp", "quantize.hip", "linear.hip", "lora.hip", "fwd.hip", "dx.hip", "gemv.hip", "adamw.hip", "merge.hip", "variants.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

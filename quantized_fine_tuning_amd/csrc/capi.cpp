@@ -276,9 +276,74 @@ qlora_status qlora_merge_lora(const qlora_nf4_t* W, const void* A, const void* B
                                            static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+qlora_status check_qtensor(const char* fn, const qlora_qtensor_t* q) {
+  if (q == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: tensor descriptor is NULL", fn);
+  qlora_status st = check_shape(fn, q->n_rows, q->n_cols);
+  if (st != QLORA_OK) return st;
+  if (q->format != QLORA_FMT_NF4 && q->format != QLORA_FMT_INT4 && q->format != QLORA_FMT_INT8)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: format=%d", fn, q->format);
+  const uint8_t* codes = q->codes;
+  const float* absmax = q->absmax;
+  CHECK_PTR(codes);
+  CHECK_PTR(absmax);
+  return QLORA_OK;
+}
+
+}  // namespace
+
+qlora_status qlora_quantize_format(const void* W, qlora_dtype w_dtype, int64_t N, int64_t K,
+                                   qlora_qtensor_t* out, void* stream) {
+  const char* fn = "qlora_quantize_format";
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: w_dtype=%d (expected F32 or BF16)", fn, w_dtype);
+  qlora_status st = check_shape(fn, N, K);
+  if (st != QLORA_OK) return st;
+  CHECK_PTR(W);
+  if ((st = check_qtensor(fn, out)) != QLORA_OK) return st;
+  if (out->n_rows != N || out->n_cols != K)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: descriptor shape %lldx%lld != %lldx%lld", fn,
+                (long long)out->n_rows, (long long)out->n_cols, (long long)N, (long long)K);
+  return hip_status(fn, qnf4::launch_format_quantize(W, w_dtype == QLORA_BF16, N, K, out->format, out->codes,
+                                                     out->absmax, static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_dequantize_format(const qlora_qtensor_t* q, void* out, qlora_dtype out_dtype,
+                                     void* stream) {
+  const char* fn = "qlora_dequantize_format";
+  qlora_status st = check_qtensor(fn, q);
+  if (st != QLORA_OK) return st;
+  if (out_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype=%d (only BF16)", fn, out_dtype);
+  CHECK_PTR(out);
+  return hip_status(fn, qnf4::launch_format_dequantize(q->codes, q->absmax, q->format, q->n_rows, q->n_cols,
+                                                       static_cast<uint16_t*>(out),
+                                                       static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_gemv_format(const qlora_qtensor_t* q, const void* X, int64_t M, void* Y,
+                               qlora_dtype y_dtype, void* stream) {
+  const char* fn = "qlora_gemv_format";
+  qlora_status st = check_qtensor(fn, q);
+  if (st != QLORA_OK) return st;
+  if (M < 0 || M > 16) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld outside [0, 16]", fn, (long long)M);
+  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: y_dtype=%d", fn, y_dtype);
+  // one 16-row slice of codes must stay below 2^31 bytes (32-bit offsets)
+  if (16 * q->n_cols > (int64_t(1) << 30)) return fail(QLORA_ERR_INVALID_ARG, "%s: K too large", fn);
+  if (M > 0) {
+    CHECK_PTR(X);
+    CHECK_PTR(Y);
+  }
+  return hip_status(fn, qnf4::launch_format_gemv(q->codes, q->absmax, q->format, q->n_rows, q->n_cols,
+                                                 static_cast<const uint16_t*>(X), M, Y, y_dtype == QLORA_BF16,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* stop_event) {
   const char* fn = "qlora_time_next_launch";
-  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_MERGE)
+  if (kernel_id < QLORA_KERNEL_NONE || kernel_id > QLORA_KERNEL_FORMAT_GEMV)
     return fail(QLORA_ERR_INVALID_ARG, "%s: unknown kernel id %d", fn, kernel_id);
   if (kernel_id != QLORA_KERNEL_NONE && (start_event == nullptr || stop_event == nullptr))
     return fail(QLORA_ERR_INVALID_ARG, "%s: NULL event", fn);

@@ -36,7 +36,7 @@ hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t s
   }
   return hipGetLastError();
 }
-enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5, kKernMerge = 6 };
+enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5, kKernMerge = 6, kKernFormatGemv = 7 };
 
 // Round `x` up to a multiple of `a`.
 constexpr int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -157,5 +157,14 @@ hipError_t launch_adamw(AdamwArgs a, bool param_bf16, float lr, float beta1, flo
 // LoRA merge -----------------------------------------------------------------
 hipError_t launch_merge(const Nf4View& W, const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                         uint16_t* out, bool out_f16, hipStream_t st);
+
+// Comparison formats ------------------------------------------------------------
+// fmt: 1 NF4 (double quantization off), 2 absmax INT4, 3 absmax INT8
+hipError_t launch_format_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, int fmt, uint8_t* codes,
+                                  float* absmax, hipStream_t st);
+hipError_t launch_format_dequantize(const uint8_t* codes, const float* absmax, int fmt, int64_t N, int64_t K,
+                                    uint16_t* out, hipStream_t st);
+hipError_t launch_format_gemv(const uint8_t* codes, const float* absmax, int fmt, int64_t N, int64_t K,
+                              const uint16_t* X, int64_t M, void* Y, bool y_bf16, hipStream_t st);
 
 }  // namespace qnf4

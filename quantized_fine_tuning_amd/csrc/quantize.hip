@@ -23,6 +23,7 @@
 //                         e = E4M3(d / s).
 //   nf4_dequant_kernel    32 elements per thread, 16-byte loads of codes,
 //                         64-byte contiguous stores of bf16.
+#include <algorithm>
 #include <type_traits>
 
 #include "host.h"
@@ -276,6 +277,95 @@ __global__ __launch_bounds__(256) void dq_encode_kernel(const float* __restrict_
 }
 
 // 32 elements (16 bytes of codes, half a block) per thread.
+// Comparison formats (one fp32 absmax per 64-block, no double
+// quantization): FMT 1 = NF4 codes (the codes of nf4_quantize_kernel), 2 =
+// absmax INT4 (k = round(fl32(w · fl32(7/c))), halves away from zero, nibble
+// k + 8), 3 = absmax INT8 (the same with 127, one byte per weight).  One
+// group of LPB lanes per block and iteration, grid-stride over the blocks.
+// (from the exact fraction p - trunc(p): floor(|p| + 0.5) would round the
+// sum itself, e.g. 0.5 - 2^-25 + 0.5 ties to 1.0 in binary32)
+__device__ __forceinline__ int round_half_away(float p) {
+  const float t = __builtin_truncf(p);
+  const int k = (int)t;
+  const float d = __fsub_rn(p, t);  // exact
+  return d >= 0.5f ? k + 1 : (d <= -0.5f ? k - 1 : k);
+}
+
+template <typename WT, int FMT>
+__global__ __launch_bounds__(256) void format_quantize_kernel(const WT* __restrict__ W, int64_t nb,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ absmax, Codebook cb) {
+  constexpr int EPL = QTraits<WT>::kEpl;
+  constexpr int LPB = kBlock / EPL;
+  __shared__ uint2 s_tab[2 * kCodeCells];
+  if (FMT == 1 && threadIdx.x < 2 * kCodeCells) s_tab[threadIdx.x] = code_cell(threadIdx.x, cb);
+  __syncthreads();
+  const int sub = threadIdx.x % LPB;
+  const int64_t groups = (int64_t)gridDim.x * (256 / LPB);
+  for (int64_t b = (int64_t)blockIdx.x * (256 / LPB) + threadIdx.x / LPB; b - (threadIdx.x / LPB) < nb;
+       b += groups) {
+    // (the loop bound keeps the whole wave in the loop while any of its
+    // blocks is in range, so that the max over lanes sees complete groups)
+    const bool live = b < nb;
+    WT v[EPL];
+    if (live) {
+      __builtin_memcpy(v, W + b * kBlock + sub * EPL, sizeof(v));
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) v[i] = WT(0);
+    }
+    float w[EPL];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      w[i] = QTraits<WT>::to_f32(v[i]);
+      m = fmaxf(m, fabsf(w[i]));
+    }
+    m = group_max<LPB>(m);
+    uint32_t code[EPL];
+    if constexpr (FMT == 1) {
+      // x = fl32(w / m), then the nearest level through the cell table
+      const float den = m != 0.0f ? m : 1.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float x = __fdiv_rn(w[i], den);
+        const uint2 cell = s_tab[code_cell_index(x)];
+        code[i] = cell.y + (x > __uint_as_float(cell.x) ? 1u : 0u);
+      }
+    } else {
+      constexpr float qmax = FMT == 2 ? 7.0f : 127.0f;
+      const float alpha = m != 0.0f ? __fdiv_rn(qmax, m) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int k = min(max(round_half_away(__fmul_rn(w[i], alpha)), -(int)qmax), (int)qmax);
+        code[i] = FMT == 2 ? (uint32_t)(k + 8) : (uint32_t)k & 0xffu;
+      }
+    }
+    if (!live) continue;
+    if constexpr (FMT == 3) {
+      uint8_t* dst = codes + b * kBlock + sub * EPL;
+      if constexpr (EPL == 4) {
+        *reinterpret_cast<uint32_t*>(dst) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      } else {
+        *reinterpret_cast<u32x2_t*>(dst) =
+            u32x2_t{code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24),
+                    code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24)};
+      }
+    } else {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) packed |= code[i] << (4 * i);
+      uint8_t* dst = codes + b * (kBlock / 2) + sub * (EPL / 2);
+      if constexpr (EPL == 4) {
+        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+      }
+    }
+    if (sub == 0) absmax[b] = m;
+  }
+}
+
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ e,
                                                           const float* __restrict__ s,
@@ -375,6 +465,23 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* e, const float
   int64_t grid = (units + 255) / 256;
   if (grid > 65536) grid = 65536;
   nf4_dequant_kernel<<<(unsigned)grid, 256, 0, st>>>(codes, e, s, mu, units, out, codebook());
+  return hipGetLastError();
+}
+
+hipError_t launch_format_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, int fmt, uint8_t* codes,
+                                  float* absmax, hipStream_t st) {
+  const int64_t nb = N * K / kBlock;
+  if (nb == 0) return hipSuccess;
+  const int per_wg = w_bf16 ? 256 / (kBlock / 8) : 256 / (kBlock / 4);  // blocks per workgroup and pass
+  const unsigned grid = (unsigned)std::min<int64_t>((nb + per_wg - 1) / per_wg, 256 * 16);
+  const Codebook& cb = codebook();
+#define QNF4_FQ(WT, F) format_quantize_kernel<WT, F><<<grid, 256, 0, st>>>(static_cast<const WT*>(W), nb, codes, absmax, cb)
+  if (w_bf16) {
+    if (fmt == 1) QNF4_FQ(uint16_t, 1); else if (fmt == 2) QNF4_FQ(uint16_t, 2); else QNF4_FQ(uint16_t, 3);
+  } else {
+    if (fmt == 1) QNF4_FQ(float, 1); else if (fmt == 2) QNF4_FQ(float, 2); else QNF4_FQ(float, 3);
+  }
+#undef QNF4_FQ
   return hipGetLastError();
 }
 

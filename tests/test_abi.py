@@ -227,6 +227,34 @@ def test_merge_validation():
     assert lib.qlora_dequantize(ctypes.byref(d), FAKE, q.QLORA_F16, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
 
 
+def test_format_validation():
+    lib = q.lib
+    QT = q.qlora_qtensor_t
+
+    def qt(n=256, k=256, fmt=q._binding.QLORA_FMT_INT4, codes=FAKE, absmax=FAKE):
+        return QT(n, k, fmt, codes, absmax)
+
+    quant = lib.qlora_quantize_format
+    assert quant(FAKE, q.QLORA_F16, 256, 256, ctypes.byref(qt()), None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert quant(FAKE, q.QLORA_F32, 256, 100, ctypes.byref(qt(k=100)), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(FAKE, q.QLORA_F32, 256, 256, ctypes.byref(qt(fmt=0)), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(FAKE, q.QLORA_F32, 256, 256, ctypes.byref(qt(fmt=4)), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(FAKE, q.QLORA_F32, 256, 256, ctypes.byref(qt(n=128)), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(None, q.QLORA_F32, 256, 256, ctypes.byref(qt()), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(FAKE, q.QLORA_F32, 256, 256, ctypes.byref(qt(absmax=FAKE + 4)), None) == q.QLORA_ERR_INVALID_ARG
+    assert quant(FAKE, q.QLORA_F32, 256, 256, None, None) == q.QLORA_ERR_INVALID_ARG
+    deq = lib.qlora_dequantize_format
+    assert deq(ctypes.byref(qt()), FAKE, q.QLORA_F32, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert deq(ctypes.byref(qt()), None, q.QLORA_BF16, None) == q.QLORA_ERR_INVALID_ARG
+    assert deq(ctypes.byref(qt(codes=None)), FAKE, q.QLORA_BF16, None) == q.QLORA_ERR_INVALID_ARG
+    gemv = lib.qlora_gemv_format
+    assert gemv(ctypes.byref(qt()), FAKE, 17, FAKE, q.QLORA_F32, None) == q.QLORA_ERR_INVALID_ARG
+    assert gemv(ctypes.byref(qt()), FAKE, -1, FAKE, q.QLORA_F32, None) == q.QLORA_ERR_INVALID_ARG
+    assert gemv(ctypes.byref(qt()), FAKE, 1, FAKE, q.QLORA_F16, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert gemv(ctypes.byref(qt()), None, 1, FAKE, q.QLORA_F32, None) == q.QLORA_ERR_INVALID_ARG
+    assert gemv(ctypes.byref(qt(fmt=9)), FAKE, 1, FAKE, q.QLORA_F32, None) == q.QLORA_ERR_INVALID_ARG
+
+
 def test_status_strings():
     for s in range(5):
         assert q.lib.qlora_status_string(s).decode()

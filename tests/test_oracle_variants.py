@@ -57,6 +57,17 @@ def test_halves_round_away_from_zero(fmt, qmax):
     assert list(codes_int(codes, fmt)[:4]) == [1, -1, 2, -2]
 
 
+def test_just_below_a_half_rounds_down():
+    # p = fl32(w · fl32(7/c)) = 0.5 - 2^-25 rounds to 0: the rounding is taken
+    # on p itself (in binary32, p + 0.5 would already tie up to 1.0)
+    w = block([0.012129448, 0.16981228])
+    codes, c = variants.quantize(w, "int4")
+    alpha = F32(7) / c[0]
+    assert F32(F32(0.012129448) * alpha) == F32(0.5) - F32(2.0 ** -25)
+    assert F32(F32(0.5) - F32(2.0 ** -25)) + F32(0.5) == F32(1.0)
+    assert codes_int(codes, "int4")[0] == 0
+
+
 def test_zero_block_gets_the_zero_code():
     w = np.zeros((2, 64), F32)
     w[1, 5] = 0.25
