@@ -288,27 +288,50 @@ def bf16_to_f32(b16: np.ndarray) -> np.ndarray:
     return (np.asarray(b16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def f16_bits(x32: np.ndarray) -> np.ndarray:
+    """Round fp32 to IEEE binary16 (nearest, ties to even, subnormals kept,
+    overflow to infinity); returns the uint16 bit patterns.  (numpy's
+    float-to-half conversion, one rounding.)"""
+    with np.errstate(over="ignore"):
+        return np.asarray(x32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_to_f32(b16: np.ndarray) -> np.ndarray:
+    return np.asarray(b16, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def round16(x32: np.ndarray, fmt16: str) -> np.ndarray:
+    """fp32 -> 16-bit bit patterns in the compute format ("bf16" or "f16")."""
+    if fmt16 == "bf16":
+        return bf16_bits(x32)
+    if fmt16 == "f16":
+        return f16_bits(x32)
+    raise ValueError(fmt16)
+
+
 def dequantize(packed: np.ndarray, e: np.ndarray, s: np.ndarray, mu,
-               q32: np.ndarray | None = None) -> np.ndarray:
-    """ŵ_i = RNE_bf16(fl32(q[code_i] * c'_b)); returns uint16 bf16 bits,
-    flattened row-major.  Signed zeros follow IEEE (code 7 with c' < 0 gives
-    -0)."""
+               q32: np.ndarray | None = None, fmt16: str = "bf16") -> np.ndarray:
+    """ŵ_i = RNE16(fl32(q[code_i] * c'_b)) with RNE16 the rounding into the
+    compute format (bf16 by default; fp16 for the fp16 compute path, P1 §四
+    and §七 naming FP16 beside BF16); returns uint16 bit patterns, flattened
+    row-major.  Signed zeros follow IEEE (code 7 with c' < 0 gives -0)."""
     codes = unpack_nibbles(packed).reshape(-1, BLOCK)
-    return dequantize_blocks(codes, np.arange(codes.shape[0]), e, s, mu, q32).reshape(-1)
+    return dequantize_blocks(codes, np.arange(codes.shape[0]), e, s, mu, q32, fmt16).reshape(-1)
 
 
 def dequantize_blocks(codes: np.ndarray, block_ids: np.ndarray, e: np.ndarray, s: np.ndarray,
-                      mu, q32: np.ndarray | None = None) -> np.ndarray:
+                      mu, q32: np.ndarray | None = None, fmt16: str = "bf16") -> np.ndarray:
     """The same dequantization for a subset of blocks: ``codes`` holds the
     unpacked codes of the listed blocks ([len(block_ids), 64]); ``e``, ``s`` and
-    ``mu`` are the whole tensor's constants.  Returns uint16 bf16 bits
-    [len(block_ids), 64].  (Blocks dequantize independently of each other.)"""
+    ``mu`` are the whole tensor's constants.  Returns uint16 bit patterns of
+    the compute format [len(block_ids), 64].  (Blocks dequantize
+    independently of each other.)"""
     if q32 is None:
         q32 = codebook()
     codes = np.asarray(codes, dtype=np.uint8).reshape(-1, BLOCK)
     cp = decode_constants(e, s, mu)[np.asarray(block_ids)]
     w32 = (q32[codes] * cp[:, None]).astype(np.float32)
-    return bf16_bits(w32)
+    return round16(w32, fmt16)
 
 
 def quantize(w32: np.ndarray):
