@@ -30,6 +30,8 @@ Extra objects on the JSON line:
                 absmax INT4 and INT8) on the q_proj weight: reconstruction
                 error against the fp32 weight, and dequant-GEMV time and GB/s
                 at M = 1 and 16;
+  f16_step      the same MLP step in the fp16 compute format (5 timed steps):
+                ms per step, TFLOP/s and the two GEMMs' average times;
   cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
                 of the same workload (quantize + dequantize + forward +
                 backward of the three linears at M = 4096).
@@ -41,7 +43,7 @@ is taken from the summary under profiles/ and reported only while the
 kernel's sources are byte-identical to the ones profiled; otherwise null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-gemv] [--no-adamw] [--no-merge] [--no-formats]
+                       [--no-gemv] [--no-adamw] [--no-merge] [--no-formats] [--no-f16]
 """
 
 import argparse
@@ -142,8 +144,14 @@ def timed_events(torch, n):
     return evs
 
 
-def run_mlp(torch, q, args):
+def run_mlp(torch, q, args, f16=False, steps=None, warmup=None):
+    """The timed MLP step.  f16: the same step in the fp16 compute format
+    (the workloads' bf16 inputs converted to fp16 on the device)."""
     from workloads import Inputs
+
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    cvt = (lambda x: x.to(torch.float16)) if f16 else (lambda x: x)  # noqa: E731
 
     w = Inputs(3)
     M, r, alpha = w.w.tokens[0], w.w.rank, w.w.alpha
@@ -152,18 +160,18 @@ def run_mlp(torch, q, args):
         t0 = time.time()
         L = {"name": name, "N": N, "K": K}
         L["W"] = torch.from_numpy(w.weight(li)).cuda()
-        L["X"] = dev_bf16(torch, w.X(li, M))
-        L["dY"] = dev_bf16(torch, w.dY(li, M))
-        L["A"] = dev_bf16(torch, w.lora_A(li))
-        L["B"] = dev_bf16(torch, w.lora_B(li))
+        L["X"] = cvt(dev_bf16(torch, w.X(li, M)))
+        L["dY"] = cvt(dev_bf16(torch, w.dY(li, M)))
+        L["A"] = cvt(dev_bf16(torch, w.lora_A(li)))
+        L["B"] = cvt(dev_bf16(torch, w.lora_B(li)))
         sz = q.qlora_nf4_sizes(N, K, M, r)
         L["qt"] = q.Nf4Tensor.empty(N, K)
         L["wsq"] = q.workspace(sz["quantize_ws_bytes"])
         L["wsf"] = q.workspace(sz["fwd_ws_bytes"])
         L["wsb"] = q.workspace(sz["bwd_ws_bytes"])
-        L["Y"] = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        L["Y"] = torch.empty(M, N, dtype=torch.float16 if f16 else torch.bfloat16, device="cuda")
         L["T"] = torch.empty(M, r, dtype=torch.float32, device="cuda")
-        L["dX"] = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        L["dX"] = torch.empty(M, K, dtype=torch.float16 if f16 else torch.bfloat16, device="cuda")
         L["dA"] = torch.empty(r, K, dtype=torch.float32, device="cuda")
         L["dB"] = torch.empty(N, r, dtype=torch.float32, device="cuda")
         layers.append(L)
@@ -178,7 +186,7 @@ def run_mlp(torch, q, args):
 
     def step(i=None):
         for li, L in enumerate(layers):
-            j = li if i == args.steps - 1 else None
+            j = li if i == steps - 1 else None
             if j is not None:
                 q.qlora_time_next_launch(kid["quantize"], *events["quantize"][j])
             q.qlora_nf4_quantize(L["W"], L["qt"], L["wsq"])
@@ -190,20 +198,20 @@ def run_mlp(torch, q, args):
             q.qlora_linear_bwd(L["qt"], L["X"], L["dY"], L["A"], L["B"], r, alpha, L["T"],
                                L["dX"], L["dA"], L["dB"], L["wsb"])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] {args.warmup} warmup steps done")
+    log(f"[bench] {warmup} warmup steps done")
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     t_end.record()
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    log(f"[bench] {steps} timed steps: {ms_per_step:.3f} ms/step")
 
     flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
     per_kernel = {}
@@ -510,6 +518,7 @@ def main():
     ap.add_argument("--no-adamw", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-formats", action="store_true")
+    ap.add_argument("--no-f16", action="store_true")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -531,6 +540,14 @@ def main():
     adamw = None if args.no_adamw else run_adamw(torch, q, args)
     merge = None if args.no_merge else run_merge(torch, q, args)
     formats = None if args.no_formats else run_formats(torch, q, args)
+    f16_step = None
+    if not args.no_f16:
+        m16 = run_mlp(torch, q, args, f16=True, steps=5, warmup=2)
+        f16_step = {"ms_per_step": round(m16["ms_per_step"], 4),
+                    "TFLOP/s": round(m16["flops"] / (m16["ms_per_step"] * 1e-3) / 1e12, 2),
+                    "fwd_gemm_ms": round(m16["per_kernel"]["fwd_gemm"]["avg_ms"], 4),
+                    "dx_gemm_ms": round(m16["per_kernel"]["dx_gemm"]["avg_ms"], 4)}
+        log(f"[bench] fp16 compute step: {f16_step}")
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -557,6 +574,7 @@ def main():
         "adamw": adamw,
         "merge": merge,
         "formats": formats,
+        "f16_step": f16_step,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in mlp["per_kernel"].items()},
     }

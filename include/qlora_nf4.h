@@ -47,7 +47,8 @@ typedef int32_t qlora_status;
 typedef int32_t qlora_dtype;
 #define QLORA_F32 0
 #define QLORA_BF16 1
-#define QLORA_F16 2  /* output of qlora_merge_lora only */
+#define QLORA_F16 2  /* IEEE binary16: the alternative compute format (the *_ex
+                        entry points), dequantize and merge outputs */
 
 /* One NF4 + double-quantized weight (P4 §三 English derivation; P1 §二).
  * All four arrays are device memory:
@@ -104,7 +105,8 @@ qlora_status qlora_nf4_quantize(const void* W, qlora_dtype w_dtype, int64_t N,
 /* Dequantize to bf16 (P1 §七: the 4-bit base is dequantized block by block to
  * BF16 before the matmul; P4 §四 ①: Ŵ = Dequant(W^NF4)·c).
  *   q        host struct describing the quantized weight (device arrays);
- *   out      device, [N, K] bf16; out_dtype must be QLORA_BF16.
+ *   out      device, [N, K] bf16 (out_dtype QLORA_BF16) or fp16 (QLORA_F16,
+ *            the same product rounded into binary16).
  * ŵ = RNE_bf16(fl32(q[code] * c')) with
  * c' = fl32(fl32(dec(e) * s_g) + mu); bit-exact, signed zeros kept. */
 qlora_status qlora_dequantize(const qlora_nf4_t* q, void* out,
@@ -146,6 +148,26 @@ qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X,
                               const float* T_saved, void* dX,
                               qlora_dtype dx_dtype, float* dA, float* dB,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* The same two passes in either 16-bit compute format (P1 §四 and §七 name
+ * FP16 beside BF16 as the precision the dequantized weight is multiplied in):
+ * compute_dtype QLORA_BF16 (what qlora_linear_fwd / qlora_linear_bwd use) or
+ * QLORA_F16.  X, dY, A and B are in the compute format; the weight is
+ * dequantized into it (RNE16(fl32(q·c'))); the hi/lo splits of s·T and s·U are
+ * pairs of that format; accumulation is fp32.  y_dtype / dx_dtype: QLORA_F32
+ * or the compute format.  Everything else as above. */
+qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M,
+                                 const void* A, const void* B, int32_t r,
+                                 float alpha, void* Y, qlora_dtype y_dtype,
+                                 float* T_save, void* ws, size_t ws_bytes,
+                                 qlora_dtype compute_dtype, void* stream);
+qlora_status qlora_linear_bwd_ex(const qlora_nf4_t* W, const void* X,
+                                 const void* dY, int64_t M, const void* A,
+                                 const void* B, int32_t r, float alpha,
+                                 const float* T_saved, void* dX,
+                                 qlora_dtype dx_dtype, float* dA, float* dB,
+                                 void* ws, size_t ws_bytes,
+                                 qlora_dtype compute_dtype, void* stream);
 
 /* One tensor of LoRA parameters for qlora_adamw_step (all device memory,
  * 16-byte aligned when n > 0):

@@ -34,6 +34,8 @@ from ._binding import (  # noqa: F401
     qlora_dequantize,
     qlora_linear_bwd,
     qlora_linear_fwd,
+    qlora_linear_fwd_ex,
+    qlora_linear_bwd_ex,
     qlora_merge_lora,
     qlora_quantize_format,
     qlora_dequantize_format,

@@ -28,7 +28,8 @@ QLORA_F16 = 2
 EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_linear_fwd",
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
            "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora",
-           "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format")
+           "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format",
+           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -110,6 +111,12 @@ def _load():
     lib.qlora_adamw_step.restype = i32
     lib.qlora_merge_lora.argtypes = [P(qlora_nf4_t), vp, vp, i32, f32, vp, i32, vp]
     lib.qlora_merge_lora.restype = i32
+    lib.qlora_linear_fwd_ex.argtypes = [P(qlora_nf4_t), vp, i64, vp, vp, i32, f32, vp, i32, vp, vp,
+                                        sz, i32, vp]
+    lib.qlora_linear_bwd_ex.argtypes = [P(qlora_nf4_t), vp, vp, i64, vp, vp, i32, f32, vp, vp, i32,
+                                        vp, vp, vp, sz, i32, vp]
+    lib.qlora_linear_fwd_ex.restype = i32
+    lib.qlora_linear_bwd_ex.restype = i32
     lib.qlora_quantize_format.argtypes = [vp, i32, i64, i64, P(qlora_qtensor_t), vp]
     lib.qlora_dequantize_format.argtypes = [P(qlora_qtensor_t), vp, i32, vp]
     lib.qlora_gemv_format.argtypes = [P(qlora_qtensor_t), vp, i64, vp, i32, vp]
@@ -226,23 +233,35 @@ def qlora_dequantize(q: Nf4Tensor, out, stream=None) -> None:
 
 def qlora_linear_fwd(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, ws,
                      stream=None) -> None:
+    """Forward in the compute format of X (bf16 or fp16: qlora_linear_fwd_ex)."""
+    qlora_linear_fwd_ex(W, X, A, B, r, alpha, Y, T_save, ws, _dtype(X, "X"), stream)
+
+
+def qlora_linear_fwd_ex(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, ws, compute_dtype: int,
+                        stream=None) -> None:
     M = X.shape[0]
     st = W.c_struct()
-    _check(lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X, "X"), M, _ptr(A, "A"), _ptr(B, "B"),
-                                r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
-                                _ptr(T_save, "T_save"), _ptr(ws, "ws"),
-                                ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib.qlora_linear_fwd_ex(ctypes.byref(st), _ptr(X, "X"), M, _ptr(A, "A"), _ptr(B, "B"),
+                                   r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
+                                   _ptr(T_save, "T_save"), _ptr(ws, "ws"),
+                                   ws.numel() * ws.element_size(), compute_dtype, _stream(stream)))
 
 
 def qlora_linear_bwd(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,
                      stream=None) -> None:
+    """Backward in the compute format of X (bf16 or fp16: qlora_linear_bwd_ex)."""
+    qlora_linear_bwd_ex(W, X, dY, A, B, r, alpha, T_saved, dX, dA, dB, ws, _dtype(X, "X"), stream)
+
+
+def qlora_linear_bwd_ex(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,
+                        compute_dtype: int, stream=None) -> None:
     M = X.shape[0]
     st = W.c_struct()
-    _check(lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X, "X"), _ptr(dY, "dY"), M, _ptr(A, "A"),
-                                _ptr(B, "B"), r, float(alpha), _ptr(T_saved, "T_saved"),
-                                _ptr(dX, "dX"), _dtype(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
-                                _ptr(ws, "ws"), ws.numel() * ws.element_size(),
-                                _stream(stream)))
+    _check(lib.qlora_linear_bwd_ex(ctypes.byref(st), _ptr(X, "X"), _ptr(dY, "dY"), M, _ptr(A, "A"),
+                                   _ptr(B, "B"), r, float(alpha), _ptr(T_saved, "T_saved"),
+                                   _ptr(dX, "dX"), _dtype(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
+                                   _ptr(ws, "ws"), ws.numel() * ws.element_size(), compute_dtype,
+                                   _stream(stream)))
 
 
 def qlora_time_next_launch(kernel_id: int, start_event=None, stop_event=None) -> None:

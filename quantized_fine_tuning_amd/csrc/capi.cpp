@@ -144,24 +144,33 @@ qlora_status qlora_dequantize(const qlora_nf4_t* q, void* out, qlora_dtype out_d
   const char* fn = "qlora_dequantize";
   qlora_status st = check_tensor(fn, q);
   if (st != QLORA_OK) return st;
-  if (out_dtype != QLORA_BF16)
-    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype=%d (only BF16)", fn, out_dtype);
+  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: out_dtype=%d (BF16 or F16)", fn, out_dtype);
   CHECK_PTR(out);
   return hip_status(fn, qnf4::launch_dequantize(q->codes, q->absmax_e4m3, q->dq_scale, q->dq_mean,
                                                 q->n_rows, q->n_cols, static_cast<uint16_t*>(out),
-                                                static_cast<hipStream_t>(stream)));
+                                                out_dtype == QLORA_F16, static_cast<hipStream_t>(stream)));
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
                               const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
                               float* T_save, void* ws, size_t ws_bytes, void* stream) {
+  return qlora_linear_fwd_ex(W, X, M, A, B, r, alpha, Y, y_dtype, T_save, ws, ws_bytes, QLORA_BF16, stream);
+}
+
+qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
+                                 const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
+                                 float* T_save, void* ws, size_t ws_bytes, qlora_dtype compute_dtype,
+                                 void* stream) {
   const char* fn = "qlora_linear_fwd";
   qlora_status st = check_tensor(fn, W);
   if (st != QLORA_OK) return st;
+  if (compute_dtype != QLORA_BF16 && compute_dtype != QLORA_F16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: compute_dtype=%d (BF16 or F16)", fn, compute_dtype);
   if ((st = check_rank(fn, r)) != QLORA_OK) return st;
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
-  if (y_dtype != QLORA_F32 && y_dtype != QLORA_BF16)
-    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: y_dtype=%d", fn, y_dtype);
+  if (y_dtype != QLORA_F32 && y_dtype != compute_dtype)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: y_dtype=%d (F32 or the compute dtype)", fn, y_dtype);
   CHECK_PTR(A);
   CHECK_PTR(B);
   if (M > 0) {
@@ -177,21 +186,32 @@ qlora_status qlora_linear_fwd(const qlora_nf4_t* W, const void* X, int64_t M, co
   return hip_status(fn, qnf4::launch_forward(
                             view(W), static_cast<const uint16_t*>(X), M,
                             static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), r,
-                            alpha / (float)r, Y, y_dtype == QLORA_BF16, T_save,
-                            static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+                            alpha / (float)r, Y, y_dtype != QLORA_F32, T_save,
+                            static_cast<char*>(ws), L, compute_dtype == QLORA_F16, static_cast<hipStream_t>(stream)));
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* dY, int64_t M,
                               const void* A, const void* B, int32_t r, float alpha,
                               const float* T_saved, void* dX, qlora_dtype dx_dtype, float* dA,
                               float* dB, void* ws, size_t ws_bytes, void* stream) {
+  return qlora_linear_bwd_ex(W, X, dY, M, A, B, r, alpha, T_saved, dX, dx_dtype, dA, dB, ws, ws_bytes, QLORA_BF16,
+                             stream);
+}
+
+qlora_status qlora_linear_bwd_ex(const qlora_nf4_t* W, const void* X, const void* dY, int64_t M,
+                                 const void* A, const void* B, int32_t r, float alpha,
+                                 const float* T_saved, void* dX, qlora_dtype dx_dtype, float* dA,
+                                 float* dB, void* ws, size_t ws_bytes, qlora_dtype compute_dtype,
+                                 void* stream) {
   const char* fn = "qlora_linear_bwd";
   qlora_status st = check_tensor(fn, W);
   if (st != QLORA_OK) return st;
+  if (compute_dtype != QLORA_BF16 && compute_dtype != QLORA_F16)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: compute_dtype=%d (BF16 or F16)", fn, compute_dtype);
   if ((st = check_rank(fn, r)) != QLORA_OK) return st;
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
-  if (dx_dtype != QLORA_F32 && dx_dtype != QLORA_BF16)
-    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: dx_dtype=%d", fn, dx_dtype);
+  if (dx_dtype != QLORA_F32 && dx_dtype != compute_dtype)
+    return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: dx_dtype=%d (F32 or the compute dtype)", fn, dx_dtype);
   CHECK_PTR(A);
   CHECK_PTR(B);
   CHECK_PTR(dA);
@@ -211,7 +231,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* d
                             view(W), static_cast<const uint16_t*>(X),
                             static_cast<const uint16_t*>(dY), M, static_cast<const uint16_t*>(A),
                             static_cast<const uint16_t*>(B), r, alpha / (float)r, T_saved, dX,
-                            dx_dtype == QLORA_BF16, dA, dB, static_cast<char*>(ws), L,
+                            dx_dtype != QLORA_F32, dA, dB, static_cast<char*>(ws), L, compute_dtype == QLORA_F16,
                             static_cast<hipStream_t>(stream)));
 }
 

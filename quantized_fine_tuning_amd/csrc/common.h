@@ -15,6 +15,8 @@ namespace qnf4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -39,6 +41,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   p.x = (__bf16)lo;
   p.y = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// The same into IEEE binary16 (nearest, ties to even, subnormals kept):
+// v_cvt_f16_f32 under the default rounding and denormal modes.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t p;
+  p.x = (_Float16)lo;
+  p.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+// Two values rounded into the 16-bit compute format (F16: binary16, else bf16).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (F16) {
+    return pack_f16x2(lo, hi);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
+}
+// A 16-bit compute-format value widened to fp32 (exact).
+template <bool F16>
+__device__ __forceinline__ float widen16(uint32_t v16) {
+  if constexpr (F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)v16);
+  } else {
+    return __uint_as_float(v16 << 16);
+  }
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -101,6 +130,16 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+// The same layout for either 16-bit compute format (F16: v_mfma_f32_16x16x32_f16).
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  } else {
+    return mfma_16x16x32(a, b, c);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Buffer loads: a scalar resource (base, size in bytes) plus a per-lane 32-bit
@@ -161,6 +200,19 @@ __device__ __forceinline__ void split_hilo(float v, uint16_t& hi, uint16_t& lo) 
   const float rem = __fsub_rn(v, __uint_as_float(h << 16));
   hi = (uint16_t)h;
   lo = (uint16_t)(pack_bf16x2(rem, 0.0f) & 0xffffu);
+}
+// The same split into the 16-bit compute format (binary16 pairs carry about
+// 22 significant bits while the low part stays above the subnormal range).
+template <bool F16>
+__device__ __forceinline__ void split_hilo16(float v, uint16_t& hi, uint16_t& lo) {
+  if constexpr (F16) {
+    const uint32_t h = pack_f16x2(v, 0.0f) & 0xffffu;
+    const float rem = __fsub_rn(v, widen16<true>(h));
+    hi = (uint16_t)h;
+    lo = (uint16_t)(pack_f16x2(rem, 0.0f) & 0xffffu);
+  } else {
+    split_hilo(v, hi, lo);
+  }
 }
 
 // Returns x unchanged, but hides where it came from: values derived from it

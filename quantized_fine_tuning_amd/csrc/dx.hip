@@ -56,7 +56,7 @@ __device__ __forceinline__ int wswz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row ^ (row >> 2)) & 7)) << 4);
 }
 
-template <int LSTEPS>
+template <int LSTEPS, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const uint16_t* __restrict__ dY,
                                                               int64_t M, const uint16_t* __restrict__ sU,
                                                               const uint16_t* __restrict__ AT2,
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
         // below to reuse the fragment's registers)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<F16>(a, bfr[j], acc[i][j]);
         if (g == 7) read_b(wb, 1, bfr);
       }
     };
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
           for (int j = 0; j < 4; ++j) {
             const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
             if (full || (m < M && k < K))
-              D[(16 * i + v) * K + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
+              D[(16 * i + v) * K + 16 * j] = (uint16_t)(pack16<F16>(acc[i][j][v], 0.0f) & 0xffffu);
           }
     } else {
       float* D = static_cast<float*>(dX) + (m0 + row0) * K + k0 + col0;
@@ -356,8 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     u32x4_t t0, t1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      t0[j] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp)) : 0u;
-      t1[j] = row_ok ? pack_bf16x2(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp)) : 0u;
+      t0[j] = row_ok ? pack16<F16>(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp)) : 0u;
+      t1[j] = row_ok ? pack16<F16>(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp)) : 0u;
     }
     char* const d = stab[t & 1][p] + tb_off;
     *reinterpret_cast<u32x4_t*>(d) = tb_first ? t1 : t0;
@@ -428,15 +428,17 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 }  // namespace
 
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx_bf16, hipStream_t st) {
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st) {
   const int tm = (int)((M + TM - 1) / TM), tk = (int)((W.K + TK - 1) / TK);
   const unsigned grid = tile_grid(tm, tk);
-  const int db = dx_bf16 ? 1 : 0;
+  const int db = dx16 ? 1 : 0;
   switch (2 * Rp / NSTEP) {
 #define QNF4_DX_CASE(LS)                                                                      \
   case LS:                                                                                    \
-    return timed_launch(kKernDxGemm, dx_gemm_kernel<LS>, dim3(grid), dim3(kThreads), st, W, dY, M, \
-                        (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook());
+    return f16 ? timed_launch(kKernDxGemm, dx_gemm_kernel<LS, true>, dim3(grid), dim3(kThreads), st, W, dY, M, \
+                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook()) \
+               : timed_launch(kKernDxGemm, dx_gemm_kernel<LS, false>, dim3(grid), dim3(kThreads), st, W, dY, M, \
+                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook());
     QNF4_DX_CASE(1)
     QNF4_DX_CASE(2)
     QNF4_DX_CASE(3)

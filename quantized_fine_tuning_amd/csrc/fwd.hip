@@ -58,7 +58,7 @@ __device__ __forceinline__ int xswz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
 
-template <int LSTEPS>
+template <int LSTEPS, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const uint16_t* __restrict__ X,
                                                                int64_t M, const uint16_t* __restrict__ sT,
                                                                const uint16_t* __restrict__ B2,
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
         // below to reuse the fragment's registers)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(a, bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<F16>(a, bfr[j], acc[i][j]);
         if (g == 7) read_b(wb, 1, bfr);
       }
     };
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
           for (int j = 0; j < 4; ++j) {
             const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
             if (full || (m < M && n < N))
-              Yb[(16 * i + v) * N + 16 * j] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xffffu);
+              Yb[(16 * i + v) * N + 16 * j] = (uint16_t)(pack16<F16>(acc[i][j][v], 0.0f) & 0xffffu);
           }
     } else {
       float* Yf = static_cast<float*>(Y) + (m0 + row0) * N + n0 + col0;
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     u32x4_t t0, t1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      t0[j] = pack_bf16x2(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
-      t1[j] = pack_bf16x2(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp));
+      t0[j] = pack16<F16>(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
+      t1[j] = pack16<F16>(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp));
     }
     char* const d = stab[t & 1] + tb_off;
     *reinterpret_cast<u32x4_t*>(d) = t0;
@@ -388,17 +388,19 @@ hipError_t launch_pad_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp
 
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
-                           bool y_bf16, hipStream_t st) {
+                           bool y16, bool f16, hipStream_t st) {
   hipError_t e = launch_pad_lora_b(B, W.N, r, Rp, B2, st);
   if (e != hipSuccess) return e;
   const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
   const unsigned grid = tile_grid(tm, tn);
-  const int yb = y_bf16 ? 1 : 0;
+  const int yb = y16 ? 1 : 0;
   switch (2 * Rp / KSTEP) {
 #define QNF4_FWD_CASE(LS)                                                                   \
   case LS:                                                                                  \
-    return timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS>, dim3(grid), dim3(kThreads), st, W, X, M, \
-                        (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook());
+    return f16 ? timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, true>, dim3(grid), dim3(kThreads), st, W, X, M, \
+                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook()) \
+               : timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, false>, dim3(grid), dim3(kThreads), st, W, X, M, \
+                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook());
     QNF4_FWD_CASE(1)
     QNF4_FWD_CASE(2)
     QNF4_FWD_CASE(3)

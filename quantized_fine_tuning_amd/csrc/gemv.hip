@@ -39,6 +39,7 @@ constexpr int kDownSteps = 8;  // 32-wide K steps per wave and pass
 // the loads of 8 steps before their MFMAs (for K = 4096 one pass: every load
 // of the kernel is in flight at once).  The 16 partial tiles are combined in
 // a fixed order.
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_t* __restrict__ X,
                                                                    int M, int64_t K,
                                                                    const uint16_t* __restrict__ A,
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_
       ab[u] = buf_load16(ra, vx, off);
     }
 #pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) acc = mfma_16x16x32(xa[u], ab[u], acc);
+    for (int u = 0; u < kDownSteps; ++u) acc = mfma16<F16>(xa[u], ab[u], acc);
   }
   s_acc[wave][lane] = acc;
   __syncthreads();
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_
 constexpr int GEMV_ROWS = 16;
 constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
 
+template <bool F16>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
                                                             int M, const float* __restrict__ T,
                                                             const uint16_t* __restrict__ B, int r,
@@ -146,9 +148,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
       u32x4_t bfrag;
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        bfrag[p] = pack_bf16x2(__fmul_rn(sq[(w >> (8 * p)) & 15u], cp),
+        bfrag[p] = pack16<F16>(__fmul_rn(sq[(w >> (8 * p)) & 15u], cp),
                                __fmul_rn(sq[(w >> (8 * p + 4)) & 15u], cp));
-      acc = mfma_16x16x32(g.x[t], bfrag, acc);
+      acc = mfma16<F16>(g.x[t], bfrag, acc);
     }
   };
 
@@ -175,14 +177,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       uint16_t h0, l0, h1, l1;
-      split_hilo(__fmul_rn(scale, l.t[2 * p]), h0, l0);
-      split_hilo(__fmul_rn(scale, l.t[2 * p + 1]), h1, l1);
+      split_hilo16<F16>(__fmul_rn(scale, l.t[2 * p]), h0, l0);
+      split_hilo16<F16>(__fmul_rn(scale, l.t[2 * p + 1]), h1, l1);
       hi[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
       lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
       bf[p] = (l.b[2 * p] & 0xffffu) | (l.b[2 * p + 1] << 16);
     }
-    acc = mfma_16x16x32(hi, bf, acc);
-    acc = mfma_16x16x32(lo, bf, acc);
+    acc = mfma16<F16>(hi, bf, acc);
+    acc = mfma16<F16>(lo, bf, acc);
   };
   const int rsteps = (r + 31) / 32;
 
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
 #pragma unroll
       for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
       if (y_bf16)
-        static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu);
+        static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack16<F16>(y, 0.0f) & 0xffffu);
       else
         static_cast<float*>(Y)[(int64_t)m * N + nn] = y;
     }
@@ -239,12 +241,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
 }  // namespace
 
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                       const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
-                       hipStream_t st) {
-  lora_down_small_kernel<<<(unsigned)((r + 15) / 16), kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
+                       const uint16_t* B, int32_t r, float scale, void* Y, bool y16, float* T,
+                       bool f16, hipStream_t st) {
+  const unsigned gd = (unsigned)((r + 15) / 16);
+  if (f16)
+    lora_down_small_kernel<true><<<gd, kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
+  else
+    lora_down_small_kernel<false><<<gd, kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
   const unsigned grid = (unsigned)((W.N + GEMV_ROWS - 1) / GEMV_ROWS);
-  return timed_launch(kKernGemv, gemv_kernel, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
-                      (const float*)T, B, r, scale, Y, y_bf16 ? 1 : 0, codebook());
+  return f16 ? timed_launch(kKernGemv, gemv_kernel<true>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
+                            (const float*)T, B, r, scale, Y, y16 ? 1 : 0, codebook())
+             : timed_launch(kKernGemv, gemv_kernel<false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
+                            (const float*)T, B, r, scale, Y, y16 ? 1 : 0, codebook());
 }
 
 }  // namespace qnf4

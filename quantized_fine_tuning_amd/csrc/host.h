@@ -57,7 +57,7 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uin
                            uint8_t* e, float* s, float* mu, char* ws, const QuantLayout& L,
                            hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* e, const float* s,
-                             const float* mu, int64_t N, int64_t K, uint16_t* out,
+                             const float* mu, int64_t N, int64_t K, uint16_t* out, bool f16,
                              hipStream_t st);
 
 // Shared view of a quantized weight for the GEMM kernels.
@@ -89,14 +89,14 @@ size_t colred_partial_bytes(const SkPlan& p);
 int64_t lora_mp(int64_t M);
 // Partial tiles of Σ_k L[m][k]·R[j][k] (rows of R past rrows read as zero).
 hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl, const uint16_t* R,
-                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, hipStream_t st);
+                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, bool f16, hipStream_t st);
 // Sums them → optional fp32 T [M, r], the hi/lo split of scale·T [M, 2Rp]
 // and optionally its transpose [2Rp, Mp].
 hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
-                                float scale, float* T, uint16_t* out, uint16_t* outT, hipStream_t st);
+                                float scale, float* T, uint16_t* out, uint16_t* outT, bool f16, hipStream_t st);
 // Partial tiles of Σ_m L[m][p]·(S[j][m] + S[Rp + j][m]).
 hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, hipStream_t st);
+                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, bool f16, hipStream_t st);
 // Sums them → out [Pn, r], or out [r, Pn] when transposed.
 hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
                                 float* out, hipStream_t st);
@@ -105,7 +105,7 @@ hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int
 // Bᵀ zero-padded; AT2 [K, 2Rp] = [Aᵀ | Aᵀ] zero-padded.
 hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, float scale, uint16_t* sT,
                            uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
-                           int64_t K, uint16_t* AT2, hipStream_t st);
+                           int64_t K, uint16_t* AT2, bool f16, hipStream_t st);
 hipError_t launch_zero(float* a, int64_t n, hipStream_t st);
 
 // Forward ------------------------------------------------------------------
@@ -118,8 +118,8 @@ struct FwdLayout {
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                          const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16,
-                          float* T, char* ws, const FwdLayout& L, hipStream_t st);
+                          const uint16_t* B, int32_t r, float scale, void* Y, bool y16,
+                          float* T, char* ws, const FwdLayout& L, bool f16, hipStream_t st);
 
 // Backward -----------------------------------------------------------------
 struct BwdLayout {
@@ -133,8 +133,8 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,
-                           const float* T_saved, void* dX, bool dx_bf16, float* dA, float* dB,
-                           char* ws, const BwdLayout& L, hipStream_t st);
+                           const float* T_saved, void* dX, bool dx16, float* dA, float* dB,
+                           char* ws, const BwdLayout& L, bool f16, hipStream_t st);
 
 // AdamW on the LoRA parameters ---------------------------------------------
 constexpr int kAdamwMaxTensors = 8;

@@ -13,13 +13,13 @@
 namespace qnf4 {
 
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx_bf16, hipStream_t st);
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
-                           bool y_bf16, hipStream_t st);
+                           bool y16, bool f16, hipStream_t st);
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                       const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16, float* T,
-                       hipStream_t st);
+                       const uint16_t* B, int32_t r, float scale, void* Y, bool y16, float* T,
+                       bool f16, hipStream_t st);
 
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdLayout L{};
@@ -77,28 +77,28 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                          const uint16_t* B, int32_t r, float scale, void* Y, bool y_bf16,
-                          float* T, char* ws, const FwdLayout& L, hipStream_t st) {
+                          const uint16_t* B, int32_t r, float scale, void* Y, bool y16,
+                          float* T, char* ws, const FwdLayout& L, bool f16, hipStream_t st) {
   if (M == 0) return hipSuccess;
   if (M <= 16) {
     float* Tw = T ? T : reinterpret_cast<float*>(ws + L.off_T);
-    return launch_gemv(W, X, M, A, B, r, scale, Y, y_bf16, Tw, st);
+    return launch_gemv(W, X, M, A, B, r, scale, Y, y16, Tw, f16, st);
   }
   const int64_t Rp = lora_rp(r);
   uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
   float* P = reinterpret_cast<float*>(ws + L.off_P);
-  hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, L.pT, P, st);
+  hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, L.pT, P, f16, st);
   if (e != hipSuccess) return e;
-  e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, st);
+  e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, f16, st);
   if (e != hipSuccess) return e;
   uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
-  return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y_bf16, st);
+  return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y16, f16, st);
 }
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,
-                           const float* T_saved, void* dX, bool dx_bf16, float* dA, float* dB,
-                           char* ws, const BwdLayout& L, hipStream_t st) {
+                           const float* T_saved, void* dX, bool dx16, float* dA, float* dB,
+                           char* ws, const BwdLayout& L, bool f16, hipStream_t st) {
   const int64_t Rp = lora_rp(r), Mp = lora_mp(M);
   const int64_t N = W.N, K = W.K;
   float* P = reinterpret_cast<float*>(ws + L.off_P);
@@ -115,26 +115,26 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   uint16_t* BT = reinterpret_cast<uint16_t*>(ws + L.off_BT);
   uint16_t* AT2 = reinterpret_cast<uint16_t*>(ws + L.off_AT2);
   // operand copies: s·T (hi/lo and transposed) from the saved T, Bᵀ, [Aᵀ | Aᵀ]
-  e = launch_bwd_prep(T_saved, M, r, Rp, scale, sT, sTT, B, N, BT, A, K, AT2, st);
+  e = launch_bwd_prep(T_saved, M, r, Rp, scale, sT, sTT, B, N, BT, A, K, AT2, f16, st);
   if (e != hipSuccess) return e;
   if (!T_saved) {  // s·T recomputed
-    e = launch_rowred(X, M, K, K, A, r, K, L.pT, P, st);
-    if (e == hipSuccess) e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, st);
+    e = launch_rowred(X, M, K, K, A, r, K, L.pT, P, f16, st);
+    if (e == hipSuccess) e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, f16, st);
     if (e != hipSuccess) return e;
   }
   // s·U, U = dY·B
-  e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, st);
-  if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, st);
+  e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, f16, st);
+  if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, f16, st);
   if (e != hipSuccess) return e;
   // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
-  e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx_bf16, st);
+  e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx16, f16, st);
   if (e != hipSuccess) return e;
   // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
-  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, st);
+  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, f16, st);
   if (e == hipSuccess) e = launch_colred_finish(P, L.pA, K, r, true, dA, st);
   if (e != hipSuccess) return e;
   // dB[n][j] = Σ_m dY[m][n] · (sT_hi + sT_lo)[m][j]
-  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.pB, P, st);
+  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.pB, P, f16, st);
   if (e == hipSuccess) e = launch_colred_finish(P, L.pB, N, r, false, dB, st);
   return e;
 }

@@ -84,6 +84,7 @@ __device__ __host__ inline uint32_t sk_owner(uint32_t u, uint32_t U, uint32_t G)
 // ldr); rows past M or rrows and columns past Kred read as zero.  Tile t =
 // mb·jt + jb; 4 waves of 32 x 32.  Partial tiles [tiles, cmax, 64, 64].
 // ---------------------------------------------------------------------------
+template <bool F16>
 __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict__ L, int64_t M,
                                                      int64_t Kred, int64_t ldl,
                                                      const uint16_t* __restrict__ R, int64_t rrows,
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256) void rowred_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<F16>(a[i], b[j], acc[i][j]);
     }
   };
   // one stage: wait for it, open it, refill the stage read before it, multiply
@@ -210,6 +211,7 @@ __device__ __forceinline__ int lswz(int row, int chunk) {
   return row * 256 + ((chunk ^ (((row >> 3) & 7) << 1)) << 4);
 }
 
+template <bool F16>
 __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict__ L, int64_t Mred,
                                                      int64_t Pn, int64_t ldl,
                                                      const uint16_t* __restrict__ S, int64_t lds,
@@ -291,8 +293,8 @@ __global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict_
         const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(st + xswz(64 + 16 * jf + lr, 4 * mh + kq));
 #pragma unroll
         for (int pf = 0; pf < 2; ++pf) {
-          acc[pf][jf] = mfma_16x16x32(a[pf], bh, acc[pf][jf]);
-          acc[pf][jf] = mfma_16x16x32(a[pf], bl, acc[pf][jf]);
+          acc[pf][jf] = mfma16<F16>(a[pf], bh, acc[pf][jf]);
+          acc[pf][jf] = mfma16<F16>(a[pf], bl, acc[pf][jf]);
         }
       }
     }
@@ -348,6 +350,7 @@ __device__ __forceinline__ int sk_count(uint32_t t, uint32_t ut, uint32_t U, uin
 // j >= r) and, if outT is non-null, its transpose outT [2Rp, Mp] (zeros for
 // m >= M).  One workgroup of 256 per 32 rows of a tile (8 values a thread,
 // each slot's 8 loads issued together).
+template <bool F16>
 __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restrict__ P, int jt, uint32_t ut,
                                                             uint32_t U, uint32_t G, int cmax, int64_t M,
                                                             int64_t Mp, int r, int64_t Rp, float scale,
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
     uint16_t hi = 0, lo = 0;
     if (m < M && j < r) {
       if (T) T[m * r + j] = acc[e];
-      split_hilo(__fmul_rn(scale, acc[e]), hi, lo);
+      split_hilo16<F16>(__fmul_rn(scale, acc[e]), hi, lo);
     }
     if (m < M && j < Rp) {
       out[m * 2 * Rp + j] = hi;
@@ -442,6 +445,7 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
 // [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r] (no
 // blocks when T is null); [b1, b2): BT [Rp, Np] = Bᵀ zero-padded; [b2, ...):
 // AT2 [K, 2Rp], AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r, else 0.
+template <bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ T, int64_t M, int64_t Mp,
                                                        int r, int64_t Rp, float scale, uint16_t* __restrict__ sT,
                                                        uint16_t* __restrict__ sTT, const uint16_t* __restrict__ B,
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     const int64_t j = rem / 64, m = mblk * 64 + rem % 64;
     uint16_t hi = 0, lo = 0;
     if (m < M) {
-      if (j < r) split_hilo(__fmul_rn(scale, T[m * r + j]), hi, lo);
+      if (j < r) split_hilo16<F16>(__fmul_rn(scale, T[m * r + j]), hi, lo);
       sT[m * 2 * Rp + j] = hi;
       sT[m * 2 * Rp + Rp + j] = lo;
     }
@@ -517,21 +521,31 @@ size_t colred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax *
 int64_t lora_mp(int64_t M) { return round_up(std::max<int64_t>(M, 1), 64); }
 
 hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl, const uint16_t* R,
-                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, hipStream_t st) {
-  rowred_kernel<<<p.G, 256, 0, st>>>(L, M, Kred, ldl, R, rrows, ldr, p.jt, p.ut, p.U, p.cmax, P);
+                         int64_t rrows, int64_t ldr, const SkPlan& p, float* P, bool f16, hipStream_t st) {
+  if (f16)
+    rowred_kernel<true><<<p.G, 256, 0, st>>>(L, M, Kred, ldl, R, rrows, ldr, p.jt, p.ut, p.U, p.cmax, P);
+  else
+    rowred_kernel<false><<<p.G, 256, 0, st>>>(L, M, Kred, ldl, R, rrows, ldr, p.jt, p.ut, p.U, p.cmax, P);
   return hipGetLastError();
 }
 
 hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
-                                float scale, float* T, uint16_t* out, uint16_t* outT, hipStream_t st) {
-  rowred_finish_kernel<<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M), r, Rp,
-                                                          scale, T, out, outT);
+                                float scale, float* T, uint16_t* out, uint16_t* outT, bool f16, hipStream_t st) {
+  if (f16)
+    rowred_finish_kernel<true><<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M),
+                                                                       r, Rp, scale, T, out, outT);
+  else
+    rowred_finish_kernel<false><<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M),
+                                                                        r, Rp, scale, T, out, outT);
   return hipGetLastError();
 }
 
 hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, hipStream_t st) {
-  colred_kernel<<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
+                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, bool f16, hipStream_t st) {
+  if (f16)
+    colred_kernel<true><<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
+  else
+    colred_kernel<false><<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
   return hipGetLastError();
 }
 
@@ -544,12 +558,15 @@ hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int
 
 hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, float scale, uint16_t* sT,
                            uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
-                           int64_t K, uint16_t* AT2, hipStream_t st) {
+                           int64_t K, uint16_t* AT2, bool f16, hipStream_t st) {
   const int64_t Mp = lora_mp(M), Np = round_up(N, 64);
   const unsigned b1 = T ? cdiv(Mp * Rp, 256) : 0u;
   const unsigned b2 = b1 + cdiv(Rp * Np, 256);
   const unsigned b3 = b2 + cdiv(K * 2 * Rp, 256);
-  bwd_prep_kernel<<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
+  if (f16)
+    bwd_prep_kernel<true><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
+  else
+    bwd_prep_kernel<false><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
   return hipGetLastError();
 }
 

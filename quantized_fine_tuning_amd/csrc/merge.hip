@@ -48,8 +48,6 @@ constexpr int kMergeRows = 64, kMergeCols = 256, kMergeThreads = 256;
 constexpr int kMergeChunk = 64;            // ranks per chunk (two slices of 32)
 constexpr int kMergeWorkgroups = 2 * 256;  // about two per compute unit
 
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-
 // Byte offset of element (row, j) of a B slice (64-byte rows, 16-byte chunk c
 // of row `row` at physical chunk c ^ ((row >> 1) & 3)): the 8 lanes of one
 // 16-byte fragment read (rows 0..7 of a tile) hit distinct banks.

@@ -366,6 +366,7 @@ __global__ __launch_bounds__(256) void format_quantize_kernel(const WT* __restri
   }
 }
 
+template <bool F16>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ e,
                                                           const float* __restrict__ s,
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(const uint8_t* __restr
       for (int p = 0; p < 4; ++p) {
         const float a = __fmul_rn(s_q[(w[wi] >> (8 * p)) & 15u], cp);
         const float c = __fmul_rn(s_q[(w[wi] >> (8 * p + 4)) & 15u], cp);
-        r[p] = pack_bf16x2(a, c);
+        r[p] = pack16<F16>(a, c);
       }
       o[wi] = u32x4_t{r[0], r[1], r[2], r[3]};
     }
@@ -459,12 +460,15 @@ hipError_t launch_quantize(const void* W, bool w_bf16, int64_t N, int64_t K, uin
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* e, const float* s,
-                             const float* mu, int64_t N, int64_t K, uint16_t* out,
+                             const float* mu, int64_t N, int64_t K, uint16_t* out, bool f16,
                              hipStream_t st) {
   const int64_t units = N * K / 32;
   int64_t grid = (units + 255) / 256;
   if (grid > 65536) grid = 65536;
-  nf4_dequant_kernel<<<(unsigned)grid, 256, 0, st>>>(codes, e, s, mu, units, out, codebook());
+  if (f16)
+    nf4_dequant_kernel<true><<<(unsigned)grid, 256, 0, st>>>(codes, e, s, mu, units, out, codebook());
+  else
+    nf4_dequant_kernel<false><<<(unsigned)grid, 256, 0, st>>>(codes, e, s, mu, units, out, codebook());
   return hipGetLastError();
 }
 

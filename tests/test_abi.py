@@ -202,6 +202,31 @@ def test_adamw_validation():
     assert call(ts=(T(None, None, None, None, 0),)) == q.QLORA_OK
 
 
+def test_compute_dtype_validation():
+    lib = q.lib
+    d = desc()
+    big = 1 << 30
+
+    def fwd(cd, yd):
+        return lib.qlora_linear_fwd_ex(ctypes.byref(d), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, yd, None, FAKE,
+                                       big, cd, None)
+
+    def bwd(cd, dxd):
+        return lib.qlora_linear_bwd_ex(ctypes.byref(d), FAKE, FAKE, 32, FAKE, FAKE, 8, 16.0, None, FAKE, dxd,
+                                       FAKE, FAKE, FAKE, big, cd, None)
+
+    assert fwd(q.QLORA_F32, q.QLORA_F32) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert fwd(7, q.QLORA_F32) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert fwd(q.QLORA_F16, q.QLORA_BF16) == q.QLORA_ERR_UNSUPPORTED_DTYPE  # 16-bit output in the other format
+    assert fwd(q.QLORA_BF16, q.QLORA_F16) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert bwd(q.QLORA_F32, q.QLORA_F32) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert bwd(q.QLORA_F16, q.QLORA_BF16) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    # the original entry points are the bf16 forms
+    assert lib.qlora_linear_fwd(ctypes.byref(d), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, q.QLORA_F16, None, FAKE,
+                                big, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert lib.qlora_dequantize(ctypes.byref(d), FAKE, q.QLORA_F32, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
+
+
 def test_merge_validation():
     lib = q.lib
     m = lib.qlora_merge_lora
@@ -222,9 +247,6 @@ def test_merge_validation():
     assert call(d=desc(n=1 << 16, k=1 << 16)) == q.QLORA_ERR_INVALID_ARG
     assert "too large" in lib.qlora_last_error().decode()
     assert m(None, FAKE, FAKE, 8, 16.0, FAKE, q.QLORA_BF16, None) == q.QLORA_ERR_INVALID_ARG
-    # F16 is an output of the merge only
-    d = desc()
-    assert lib.qlora_dequantize(ctypes.byref(d), FAKE, q.QLORA_F16, None) == q.QLORA_ERR_UNSUPPORTED_DTYPE
 
 
 def test_format_validation():
