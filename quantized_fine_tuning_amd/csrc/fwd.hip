@@ -368,29 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   }
 }
 
-// B2[n][j] = B[n][j mod Rp] for (j mod Rp) < r, else 0;  [N, 2Rp] bf16.
-__global__ void pad_lora_b_kernel(const uint16_t* __restrict__ B, int64_t N, int r, int64_t Rp,
-                                  uint16_t* __restrict__ B2) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * 2 * Rp) return;
-  const int64_t n = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
-  B2[idx] = j < r ? B[n * r + j] : (uint16_t)0;
-}
-
 }  // namespace
 
-hipError_t launch_pad_lora_b(const uint16_t* B, int64_t N, int32_t r, int64_t Rp, uint16_t* B2,
-                             hipStream_t st) {
-  const int64_t n2 = N * 2 * Rp;
-  pad_lora_b_kernel<<<(unsigned)((n2 + 255) / 256), 256, 0, st>>>(B, N, r, Rp, B2);
-  return hipGetLastError();
-}
-
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
-                           const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
-                           bool y16, bool f16, hipStream_t st) {
-  hipError_t e = launch_pad_lora_b(B, W.N, r, Rp, B2, st);
-  if (e != hipSuccess) return e;
+                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, bool f16, hipStream_t st) {
   const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
   const unsigned grid = tile_grid(tm, tn);
   const int yb = y16 ? 1 : 0;

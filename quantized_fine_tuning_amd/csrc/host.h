@@ -91,9 +91,11 @@ int64_t lora_mp(int64_t M);
 hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl, const uint16_t* R,
                          int64_t rrows, int64_t ldr, const SkPlan& p, float* P, bool f16, hipStream_t st);
 // Sums them → optional fp32 T [M, r], the hi/lo split of scale·T [M, 2Rp]
-// and optionally its transpose [2Rp, Mp].
+// and optionally its transpose [2Rp, Mp]; if B2 is given, the same launch
+// also writes B2 [N, 2Rp] = [B | B] zero-padded (the forward GEMM's operand).
 hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
-                                float scale, float* T, uint16_t* out, uint16_t* outT, bool f16, hipStream_t st);
+                                float scale, float* T, uint16_t* out, uint16_t* outT, const uint16_t* B,
+                                int64_t N, uint16_t* B2, bool f16, hipStream_t st);
 // Partial tiles of Σ_m L[m][p]·(S[j][m] + S[Rp + j][m]).
 hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
                          int64_t lds, int64_t Rp, const SkPlan& p, float* P, bool f16, hipStream_t st);

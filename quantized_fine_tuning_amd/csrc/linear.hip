@@ -15,8 +15,7 @@ namespace qnf4 {
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
                           const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
-                           const uint16_t* B, int32_t r, int64_t Rp, uint16_t* B2, void* Y,
-                           bool y16, bool f16, hipStream_t st);
+                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, bool f16, hipStream_t st);
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
                        const uint16_t* B, int32_t r, float scale, void* Y, bool y16, float* T,
                        bool f16, hipStream_t st);
@@ -89,10 +88,10 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
   float* P = reinterpret_cast<float*>(ws + L.off_P);
   hipError_t e = launch_rowred(X, M, W.K, W.K, A, r, W.K, L.pT, P, f16, st);
   if (e != hipSuccess) return e;
-  e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, f16, st);
-  if (e != hipSuccess) return e;
   uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
-  return launch_fwd_gemm(W, X, M, sT, B, r, Rp, B2, Y, y16, f16, st);
+  e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, B, W.N, B2, f16, st);
+  if (e != hipSuccess) return e;
+  return launch_fwd_gemm(W, X, M, sT, B2, Rp, Y, y16, f16, st);
 }
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
@@ -119,12 +118,13 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   if (e != hipSuccess) return e;
   if (!T_saved) {  // s·T recomputed
     e = launch_rowred(X, M, K, K, A, r, K, L.pT, P, f16, st);
-    if (e == hipSuccess) e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, f16, st);
+    if (e == hipSuccess)
+      e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, nullptr, sT, sTT, nullptr, 0, nullptr, f16, st);
     if (e != hipSuccess) return e;
   }
   // s·U, U = dY·B
   e = launch_rowred(dY, M, N, N, BT, Rp, round_up(N, 64), L.pU, P, f16, st);
-  if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, f16, st);
+  if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, nullptr, 0, nullptr, f16, st);
   if (e != hipSuccess) return e;
   // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
   e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx16, f16, st);

@@ -355,8 +355,20 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
                                                             uint32_t U, uint32_t G, int cmax, int64_t M,
                                                             int64_t Mp, int r, int64_t Rp, float scale,
                                                             float* __restrict__ T, uint16_t* __restrict__ out,
-                                                            uint16_t* __restrict__ outT) {
+                                                            uint16_t* __restrict__ outT,
+                                                            const uint16_t* __restrict__ B, int64_t N,
+                                                            uint16_t* __restrict__ B2, uint32_t pad_b0) {
   __shared__ uint32_t sh[64][33];  // hi | lo << 16 of (j, m), padded
+  if (blockIdx.x >= pad_b0) {
+    // blocks past the tiles' (only when B2 is given): the forward GEMM's
+    // LoRA operand, in the same launch: B2[n][j] = B[n][j mod Rp] for
+    // (j mod Rp) < r, else 0 ([N, 2Rp])
+    const int64_t idx = (int64_t)(blockIdx.x - pad_b0) * 256 + threadIdx.x;
+    if (idx >= N * 2 * Rp) return;
+    const int64_t n = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
+    B2[idx] = j < r ? B[n * r + j] : (uint16_t)0;
+    return;
+  }
   const uint32_t t = blockIdx.x >> 1, half = blockIdx.x & 1;
   const int64_t m0 = (int64_t)(t / jt) * 64 + 32 * half, j0 = (int64_t)(t % jt) * 64;
   const int cnt = sk_count(t, ut, U, G);
@@ -530,13 +542,16 @@ hipError_t launch_rowred(const uint16_t* L, int64_t M, int64_t Kred, int64_t ldl
 }
 
 hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int32_t r, int64_t Rp,
-                                float scale, float* T, uint16_t* out, uint16_t* outT, bool f16, hipStream_t st) {
+                                float scale, float* T, uint16_t* out, uint16_t* outT, const uint16_t* B,
+                                int64_t N, uint16_t* B2, bool f16, hipStream_t st) {
+  const uint32_t b0 = (uint32_t)(2 * p.tiles);
+  const unsigned grid = b0 + (B2 ? cdiv(N * 2 * Rp, 256) : 0u);
   if (f16)
-    rowred_finish_kernel<true><<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M),
-                                                                       r, Rp, scale, T, out, outT);
+    rowred_finish_kernel<true><<<grid, 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M), r, Rp, scale, T,
+                                                     out, outT, B, N, B2, b0);
   else
-    rowred_finish_kernel<false><<<(unsigned)(2 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M),
-                                                                        r, Rp, scale, T, out, outT);
+    rowred_finish_kernel<false><<<grid, 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M), r, Rp, scale, T,
+                                                      out, outT, B, N, B2, b0);
   return hipGetLastError();
 }
 
