@@ -17,7 +17,9 @@ Extra objects on the JSON line:
   gemv          the dequant-GEMV forward of the 4096x4096 q_proj at M = 1 and
                 M = 16, cycling through 64 quantized copies (about 0.55 GB, more
                 than twice the 256 MB last-level cache) so every launch streams
-                from HBM;
+                from HBM; also the whole forward (LoRA-down + GEMV kernels) per
+                call when the 64 forwards are captured in one graph and
+                replayed;
   adamw         the AdamW step on bf16 LoRA parameters with fp32 moments (one
                 launch per step): the six LoRA matrices of the 7B MLP at r = 64,
                 and 8 tensors of 16 M parameters; kernel time and GB/s against
@@ -286,7 +288,35 @@ def run_gemv(torch, q, args):
                         "call_us_mean": round(c0.elapsed_time(c1) / n * 1e3, 3),
                         "bytes": nbytes, "GB/s": round(gbs, 1),
                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
-        log(f"[bench] GEMV M={M}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s")
+        # the same forwards captured in one graph (one per quantized copy) and
+        # replayed: the launch-bound decode loop without per-call host work
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for qt in copies:
+                q.qlora_linear_fwd(qt, X, A, B, r, alpha, Y, T, wsf)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for qt in copies:
+                q.qlora_linear_fwd(qt, X, A, B, r, alpha, Y, T, wsf)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        per = g0.elapsed_time(g1) / (reps * len(copies)) * 1e3
+        out[f"M{M}"]["graph_us_per_forward"] = round(per, 3)
+        out[f"M{M}"]["graph_GB/s"] = round(nbytes / (per * 1e-6) / 1e9, 1)
+        del g
+        log(f"[bench] GEMV M={M}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s; "
+            f"graph-replayed forward {per:.2f} us")
     return out
 
 
