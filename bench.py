@@ -34,6 +34,10 @@ Extra objects on the JSON line:
                 at M = 1 and 16;
   f16_step      the same MLP step in the fp16 compute format (5 timed steps):
                 ms per step, TFLOP/s and the two GEMMs' average times;
+  measured_peaks  in-run reference points beside the spec peaks: a 1 GiB
+                device copy (GB/s) and torch's bf16 matmul on the 4096 x 11008
+                x 4096 product (TFLOP/s); roofline.frac_of_measured_matmul is
+                the dominant GEMM against the latter;
   cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
                 of the same workload (quantize + dequantize + forward +
                 backward of the three linears at M = 4096).
@@ -538,6 +542,38 @@ def copy_calibration(torch, mib):
     del src, dst
 
 
+def measured_peaks(torch):
+    """In-run reference points beside the spec peaks: a streaming device copy
+    of 1 GiB (read + write bytes / time) and torch's bf16 matmul (hipBLASLt)
+    on the 7B MLP's largest product shape, each the median of 10 runs."""
+    def med_ms(fn, n=10):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = med_ms(lambda: dst.copy_(src))
+    del src, dst
+    M, N, K = 4096, 11008, 4096
+    a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+    mm_ms = med_ms(lambda: torch.matmul(a, b))
+    del a, b
+    out = {"copy_GB/s": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+           "bf16_matmul_TFLOP/s": round(2 * M * N * K / (mm_ms * 1e-3) / 1e12, 1),
+           "bf16_matmul_shape": [M, N, K]}
+    log(f"[bench] measured peaks: {out}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,6 +614,8 @@ def main():
                     "fwd_gemm_ms": round(m16["per_kernel"]["fwd_gemm"]["avg_ms"], 4),
                     "dx_gemm_ms": round(m16["per_kernel"]["dx_gemm"]["avg_ms"], 4)}
         log(f"[bench] fp16 compute step: {f16_step}")
+    peaks = measured_peaks(torch)
+    mlp["roofline"]["frac_of_measured_matmul"] = round(mlp["roofline"]["achieved"] / peaks["bf16_matmul_TFLOP/s"], 4)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -599,6 +637,7 @@ def main():
                    "lora_alpha": mlp["alpha"], "layers": mlp["layers"],
                    "flop_per_step": mlp["flops"], "parallelism": "single GPU"},
         "roofline": mlp["roofline"],
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "gemv": gemv,
         "adamw": adamw,
