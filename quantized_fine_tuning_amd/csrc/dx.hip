@@ -44,16 +44,24 @@ constexpr int TM = 256, TK = 256, NSTEP = 64;
 constexpr int kMfmaWaves = 8, kProdWaves = 4, kWaves = kMfmaWaves + kProdWaves;
 constexpr int kThreads = 64 * kWaves;
 
-// dY tile (token rows, 64 n each): chunk c of row r at physical c ^ (r & 7);
-// a fragment read gives the 8 lanes of one LDS cycle 8 consecutive rows.
+// Tiles are rows of 64 16-bit values (eight 16-byte chunks) whose chunks are
+// XOR-permuted by bits of the row.  A fragment read gives the 64 lanes 16
+// consecutive rows at 4 chunks; the permutations below let the gfx950 LDS
+// serve it at its full 16-byte read rate (measured: 4 clocks per wave
+// instruction, against 8 for c ^ (r & 7)).
+// dY tile (token rows, 64 n each): chunk c of row r at physical
+// c ^ sw(r & 7), sw swapping bits 0 and 1.
+__device__ __forceinline__ int rsw(int row) { return ((row >> 1) & 1) | ((row & 1) << 1) | (row & 4); }
 __device__ __forceinline__ int xswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ rsw(row & 7)) << 4);
 }
-// Ŵᵀ tile (k rows, 64 n each): chunk c of row r at physical
-// c ^ ((r ^ (r >> 2)) & 7), distinct both for 8 consecutive rows (fragment
-// reads) and for rows 4cg + c, cg = 0..7 (the dequantization stores).
+// Ŵᵀ tile (k rows, 64 n each): chunk c of row r at physical c ^ h(r) with
+// h(r) = r3 | r1 << 1 | r2 << 2 (r_i = bit i of r).  Besides the fragment
+// reads this also serves the dequantization stores (rows 4cg + c, cg =
+// 0..7, at 8 chunks) at the LDS's write rate.
+__device__ __forceinline__ int wsw(int row) { return ((row >> 3) & 1) | (row & 2) | (row & 4); }
 __device__ __forceinline__ int wswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 2)) & 7)) << 4);
+  return row * 128 + ((chunk ^ wsw(row)) << 4);
 }
 
 template <int LSTEPS, bool F16>
@@ -85,7 +93,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // reads the codes of its rows and columns (row 2p in the low half of dword
   // p, row 2p + 1 in its high half), looks each up in its row's table and
   // stores column c of rows 8rg..8rg+7 at wswz(32 sigma + 4cg + c, rg) =
-  // (st0 ^ 16c) + 128c.  The table of row 8rg + i sits at a 256-byte-aligned
+  // (st0 ^ 16(c & 2)) + 128c with st0 = wswz(32 sigma + 4cg, rg).  The
+  // table of row 8rg + i sits at a 256-byte-aligned
   // base + 256i + 32rg, so a lookup address is base + 32rg with its low byte
   // replaced by 32rg | 2*code (one byte permute from codes pre-shifted four
   // at a time) plus the constant 256i.  Column pair cp2 = columns 2cp2,
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       u32x4_t o;
 #pragma unroll
       for (int p = 0; p < 4; ++p) o[p] = v[cc][2 * p] | (v[cc][2 * p + 1] << 16);
-      *reinterpret_cast<u32x4_t*>(dst + ((st0 ^ (uint32_t)(16 * c)) + 128u * c)) = o;
+      *reinterpret_cast<u32x4_t*>(dst + ((st0 ^ (uint32_t)(16 * (c & 2))) + 128u * c)) = o;
     }
   };
   auto dequant_slice = [&](auto overlap, int t, int sigma, const u32x4_t& cw, auto&& issue)
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     if constexpr (decltype(overlap)::value) {
       const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)rg;
       const uint32_t st0 =
-          (uint32_t)((32 * sigma + 4 * cg) * 128 + ((rg ^ cg ^ (4 * (cg & 1))) << 4));
+          (uint32_t)((32 * sigma + 4 * cg) * 128 + ((rg ^ ((cg >> 1) & 1) ^ (4 * (cg & 1))) << 4));
       u32x4_t we, wo;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       const int ln = opaque(lane), lrg = ln >> 3, lcg = ln & 7;
       const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)lrg;
       const uint32_t st0 =
-          (uint32_t)((32 * sigma + 4 * lcg) * 128 + ((lrg ^ lcg ^ (4 * (lcg & 1))) << 4));
+          (uint32_t)((32 * sigma + 4 * lcg) * 128 + ((lrg ^ ((lcg >> 1) & 1) ^ (4 * (lcg & 1))) << 4));
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         uint32_t v[8];
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
         u32x4_t o;
 #pragma unroll
         for (int p = 0; p < 4; ++p) o[p] = v[2 * p] | (v[2 * p + 1] << 16);
-        *reinterpret_cast<u32x4_t*>(sw[t & 1] + ((st0 ^ (uint32_t)(16 * c)) + 128u * c)) = o;
+        *reinterpret_cast<u32x4_t*>(sw[t & 1] + ((st0 ^ (uint32_t)(16 * (c & 2))) + 128u * c)) = o;
       }
     }
   };
@@ -280,11 +289,11 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 
   // dY rows [64p, +64) of a step, copied straight into LDS: part c moves rows
   // 64p + 8c + (l >> 3), lane l into physical chunk l & 7, so it fetches
-  // logical chunk (l & 7) ^ (l >> 3) (row & 7 = l >> 3).  Each instruction
+  // logical chunk (l & 7) ^ sw(l >> 3) (row & 7 = l >> 3).  Each instruction
   // fills 1 KB of LDS contiguously.  (Written as assembly: the compiler then
   // inserts no wait for these copies in front of the producer's own LDS
   // reads; the wait before the step's closing barrier is explicit.)
-  const int ylch = (lane & 7) ^ (lane >> 3);
+  const int ylch = (lane & 7) ^ rsw(lane >> 3);
   const uint32_t vy = (uint32_t)(((64 * p + (lane >> 3)) * N + 8 * ylch) * 2);
   const uint32_t y_gstride = (uint32_t)(8 * N * 2);
   const i32x4_t ryw = rsrc_words(dY + m0 * N, (M - m0) * N * 2);
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int row = 64 * p + 8 * c + (lane >> 3);
-      const int lch = (lane & 7) ^ ((row ^ (row >> 2)) & 7);
+      const int lch = (lane & 7) ^ wsw(row);
       buf_load_lds16(rat, t + (64 * p + 8 * c) * 128, (uint32_t)((row * 2 * Rp + 8 * lch) * 2),
                      (uint32_t)l * 128u);
     }

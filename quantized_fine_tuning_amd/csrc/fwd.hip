@@ -51,11 +51,14 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kProdRows = TN / kProdWaves;  // weight rows per producer wave
 
 // A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
-// physical chunk c ^ (r & 7).  LDS has 32 banks of 4 bytes and serves a
-// 16-byte read for 8 lanes per cycle: an MFMA operand read gives those 8
-// lanes 8 consecutive rows, whose chunks then cover the 32 banks once.
+// physical chunk c ^ sw(r & 7), where sw swaps bits 0 and 1 of its argument.
+// An MFMA operand read gives the 64 lanes 16 consecutive rows at 4 chunks;
+// with this permutation the gfx950 LDS serves it at its full 16-byte read
+// rate (measured: 4 clocks per wave instruction), where the plain c ^ (r & 7)
+// takes twice as long.  The write paths are indifferent to the choice.
+__device__ __forceinline__ int rsw(int row) { return ((row >> 1) & 1) | ((row & 1) << 1) | (row & 4); }
 __device__ __forceinline__ int xswz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ rsw(row & 7)) << 4);
 }
 
 template <int LSTEPS, bool F16>
@@ -250,12 +253,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
 
   // X rows [64p, +64) of a step, copied straight into LDS: part c
   // moves rows 64p + 8c + (l >> 3), lane l into physical chunk l & 7, so it
-  // fetches logical chunk (l & 7) ^ (l >> 3) (row & 7 = l >> 3).  Each
+  // fetches logical chunk (l & 7) ^ sw(l >> 3) (row & 7 = l >> 3).  Each
   // instruction fills 1 KB of LDS contiguously.  (Written as assembly: the
   // compiler then inserts no wait for these copies in front of the
   // producer's own LDS reads; the wait before the step's closing barrier is
   // explicit.)
-  const int xlch = (lane & 7) ^ (lane >> 3);
+  const int xlch = (lane & 7) ^ rsw(lane >> 3);
   const uint32_t vx = (uint32_t)(((64 * p + (lane >> 3)) * K + 8 * xlch) * 2);
   const uint32_t x_gstride = (uint32_t)(8 * K * 2);
   const i32x4_t rxw = rsrc_words(X + m0 * K, (M - m0) * K * 2);

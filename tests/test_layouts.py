@@ -5,9 +5,16 @@ The kernels place tiles, tables and codes in LDS with XOR swizzles, lane
 permutations and byte-permute address arithmetic.  These tests restate each
 map in Python and check, over every lane and index, what the kernels rely on:
 writes and reads of one datum meet at the same address, every write map is a
-bijection onto its buffer, and the accesses the LDS serves in one cycle (8
-lanes for a 16-byte access, 32 lanes for 2- and 4-byte accesses; 32 banks of
-4 bytes) hit distinct banks or the same dword.
+bijection onto its buffer, and the 2-byte table lookups of one half-wave hit
+distinct banks or the same dword (the gfx950 LDS serves 2- and 4-byte
+accesses 32 lanes per clock on 32 banks of 4 bytes).
+
+The 16-byte accesses follow no such simple rule on gfx950: reads stream at
+256 bytes per clock for some lane patterns and half that for others, and
+writes at about 80 bytes per clock whatever the pattern.  The chunk
+permutations of the tiles were chosen by timing the kernels' exact read
+patterns on the hardware; the tests below pin the permutations themselves
+(the fragment reads see, in every 16-row group, the measured arrangement).
 """
 
 import random
@@ -33,12 +40,6 @@ def perm(s0, s1, sel):
     return out
 
 
-def conflict_free_16(addrs):
-    """A 16-byte access of 8 lanes in one cycle: the 32 dwords are on 32 banks."""
-    banks = [bank(a + 4 * d) for a in addrs for d in range(4)]
-    return len(set(banks)) == len(banks)
-
-
 def conflict_free_small(addrs):
     """2- or 4-byte accesses of 32 lanes: lanes on one bank read one dword."""
     seen = {}
@@ -52,8 +53,30 @@ def conflict_free_small(addrs):
 # ------------------------------------------------------------------ fwd.hip
 
 
+def rsw(r):
+    """Bits 0 and 1 of r swapped (r < 8)."""
+    return ((r >> 1) & 1) | ((r & 1) << 1) | (r & 4)
+
+
 def xswz(row, chunk):
-    return row * 128 + ((chunk ^ (row & 7)) << 4)
+    return row * 128 + ((chunk ^ rsw(row & 7)) << 4)
+
+
+def fragment_slots(swz, base, ks):
+    """(row parity, physical chunk) of each lane of an MFMA fragment read:
+    lane l reads row base + (l & 15) at chunk 2(l >> 4) + ks."""
+    out = []
+    for l in range(64):
+        a = swz(base + (l & 15), 2 * (l >> 4) + ks)
+        out.append(((a // 128) & 1, (a % 128) // 16))
+    return out
+
+
+# The chunk permutation of every 16-row group that the fragment reads met at
+# the full read rate when timed: row r (r = 0..15 of the group) puts logical
+# chunk c at physical c ^ P[r].
+MEASURED_FAST_X = [0, 2, 1, 3, 4, 6, 5, 7, 0, 2, 1, 3, 4, 6, 5, 7]
+MEASURED_FAST_W = [0, 0, 2, 2, 4, 4, 6, 6, 1, 1, 3, 3, 5, 5, 7, 7]
 
 
 def test_xswz_is_a_bijection_on_a_tile():
@@ -63,33 +86,31 @@ def test_xswz_is_a_bijection_on_a_tile():
 
 @pytest.mark.parametrize("ks", [0, 1])
 @pytest.mark.parametrize("wm", [0, 1])
-def test_fwd_a_fragment_reads_are_conflict_free(wm, ks):
+def test_fwd_a_fragment_reads_use_the_measured_permutation(wm, ks):
     for i in range(8):
-        addrs = []
         for lane in range(64):
             lr, kq = lane & 15, lane >> 4
-            addrs.append(xswz(128 * wm + lr + 16 * i, 2 * kq + ks))
-        for g in range(8):
-            assert conflict_free_16(addrs[8 * g:8 * g + 8])
+            a = xswz(128 * wm + lr + 16 * i, 2 * kq + ks)
+            assert a == (128 * wm + lr + 16 * i) * 128 + (((2 * kq + ks) ^ MEASURED_FAST_X[lr]) << 4)
 
 
 @pytest.mark.parametrize("wn", range(4))
 def test_fwd_b_fragment_reads_are_conflict_free(wn):
     for ks in range(2):
         for j in range(4):
-            addrs = [xswz(64 * wn + (l & 15) + 16 * j, 2 * (l >> 4) + ks) for l in range(64)]
-            for g in range(8):
-                assert conflict_free_16(addrs[8 * g:8 * g + 8])
+            for l in range(64):
+                row = 64 * wn + (l & 15) + 16 * j
+                assert xswz(row, 2 * (l >> 4) + ks) == row * 128 + (((2 * (l >> 4) + ks) ^ MEASURED_FAST_X[l & 15]) << 4)
 
 
 @pytest.mark.parametrize("p", range(4))
 def test_fwd_x_copy_lands_on_the_swizzled_tile(p):
     # instruction c of producer p fills 1 KB at (64p + 8c) * 128 + 16 * lane;
-    # the lane fetches logical chunk (lane & 7) ^ (lane >> 3) of its row
+    # the lane fetches logical chunk (lane & 7) ^ sw(lane >> 3) of its row
     for c in range(8):
         for lane in range(64):
             row = 64 * p + 8 * c + (lane >> 3)
-            logical = (lane & 7) ^ (lane >> 3)
+            logical = (lane & 7) ^ rsw(lane >> 3)
             assert (64 * p + 8 * c) * 128 + 16 * lane == xswz(row, logical)
 
 
@@ -140,19 +161,22 @@ def test_fwd_lookups_are_conflict_free_for_any_codes():
             assert conflict_free_small(addrs)
 
 
-def test_fwd_w_tile_stores_are_conflict_free():
+def test_fwd_w_tile_stores_cover_their_rows():
     for R in range(0, 256, 8):
         addrs = [xswz(R + (l >> 3), l & 7) for l in range(64)]
         assert sorted(addrs) == list(range(R * 128, (R + 8) * 128, 16))
-        for g in range(8):
-            assert conflict_free_16(addrs[8 * g:8 * g + 8])
 
 
 # ------------------------------------------------------------------- dx.hip
 
 
+def wsw(row):
+    """r3 | r1 << 1 | r2 << 2 for bits r_i of row."""
+    return ((row >> 3) & 1) | (row & 2) | (row & 4)
+
+
 def wswz(row, chunk):
-    return row * 128 + ((chunk ^ ((row ^ (row >> 2)) & 7)) << 4)
+    return row * 128 + ((chunk ^ wsw(row)) << 4)
 
 
 def test_wswz_is_a_bijection_on_a_tile():
@@ -161,26 +185,45 @@ def test_wswz_is_a_bijection_on_a_tile():
 
 
 @pytest.mark.parametrize("wk", range(4))
-def test_dx_b_fragment_reads_are_conflict_free(wk):
+def test_dx_b_fragment_reads_use_the_measured_permutation(wk):
     for ks in range(2):
         for j in range(4):
-            addrs = [wswz(64 * wk + (l & 15) + 16 * j, 2 * (l >> 4) + ks) for l in range(64)]
-            for g in range(8):
-                assert conflict_free_16(addrs[8 * g:8 * g + 8])
+            for l in range(64):
+                row = 64 * wk + (l & 15) + 16 * j
+                assert wswz(row, 2 * (l >> 4) + ks) == row * 128 + (((2 * (l >> 4) + ks) ^ MEASURED_FAST_W[l & 15]) << 4)
+
+
+def test_dx_a_tile_uses_the_forward_permutation():
+    for row in range(256):
+        for c in range(8):
+            assert xswz(row, c) == row * 128 + ((c ^ MEASURED_FAST_X[row & 15]) << 4)
+
+
+@pytest.mark.parametrize("p", range(4))
+def test_dx_at2_copy_lands_on_the_swizzled_tile(p):
+    # copy_at: instruction c fills 1 KB at (64p + 8c) * 128 + 16 * lane with
+    # logical chunk (lane & 7) ^ wsw(row) of row 64p + 8c + (lane >> 3)
+    seen = set()
+    for c in range(8):
+        for lane in range(64):
+            row = 64 * p + 8 * c + (lane >> 3)
+            lch = (lane & 7) ^ wsw(row)
+            assert (64 * p + 8 * c) * 128 + 16 * lane == wswz(row, lch)
+            seen.add((row, lch))
+    assert len(seen) == 512
 
 
 @pytest.mark.parametrize("sigma", range(8))
-def test_dx_slice_store_identity_and_conflicts(sigma):
+def test_dx_slice_store_identity(sigma):
+    seen = set()
     for c in range(4):
-        addrs = []
         for lane in range(64):
             rg, cg = lane >> 3, lane & 7
-            st0 = (32 * sigma + 4 * cg) * 128 + ((rg ^ cg ^ (4 * (cg & 1))) << 4)
-            a = (st0 ^ (16 * c)) + 128 * c
+            st0 = (32 * sigma + 4 * cg) * 128 + ((rg ^ ((cg >> 1) & 1) ^ (4 * (cg & 1))) << 4)
+            a = (st0 ^ (16 * (c & 2))) + 128 * c
             assert a == wswz(32 * sigma + 4 * cg + c, rg)
-            addrs.append(a)
-        for g in range(8):
-            assert conflict_free_16(addrs[8 * g:8 * g + 8])
+            seen.add(a)
+    assert sorted(seen) == list(range(32 * sigma * 128, (32 * sigma + 32) * 128, 16))
 
 
 def test_dx_code_transpose_meets_its_readers():
@@ -227,9 +270,6 @@ def test_dx_table_writers_cover_the_tables_without_conflicts():
         second.append(d ^ 16)
     assert sorted(halves) == list(range(0, 64 * 32, 16))
     assert len({r for r, _ in halves.values()}) == 64
-    for g in range(8):
-        assert conflict_free_16(first[8 * g:8 * g + 8])
-        assert conflict_free_16(second[8 * g:8 * g + 8])
 
 
 def test_dx_lookup_address_by_byte_permute():
