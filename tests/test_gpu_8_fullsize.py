@@ -1,0 +1,177 @@
+"""Full-size parity of the dequantizing GEMMs and the dequant-GEMV.
+
+1. One-hot pins (B = 0, so the adapter term is exactly zero): every output of
+   X·Ŵᵀ with one-hot rows of X is one exact product 1·ŵ, and every output of
+   dY·Ŵ with one-hot rows of dY likewise.  So
+     X = I_K  ⇒ Y = Ŵᵀ      (forward GEMM, every tile and every tile round),
+     dY = I_N ⇒ dX = Ŵ      (dX GEMM),
+     16 one-hot rows per call, 256 calls ⇒ every column of Ŵ (GEMV, M = 16),
+   bit for bit against the oracle's dequantized weight.  A zero output is
+   compared without its sign: 1·(−0) + 0·ŵ' sums to +0 in any order.
+2. Unsampled comparisons at the 7B MLP shape (M = 4096, r = 64): every
+   element of Y, dX, dA and dB against the oracle's fp64 result, by relative
+   Frobenius error (the target's bar) and element by element: the error of
+   each output divided by the sum of the magnitudes of all products in its
+   full expansion (Σ|x||ŵ| + |s|Σ_j(Σ_k|x||a|)|b| for Y, likewise for the
+   others) must stay within the rounding bound of fp32 accumulation over the
+   chained reduction lengths n (n·2⁻²⁴), the hi/lo split of the low-rank
+   factors (2⁻¹⁵) and, for 16-bit outputs, the final rounding (2⁻⁹).
+
+P1 "QLoRA 的原理是什么？" §七 (分清存储精度与计算精度): the 4-bit weight is
+dequantized to BF16 before the matmul, so the product must see exactly the
+dequantized values.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import linalg, nf4
+from tests import gpu_util as G
+from workloads import Inputs, random_bf16, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def canon_zero(bits):
+    b = np.asarray(bits, dtype=np.uint16)
+    return np.where((b & 0x7FFF) == 0, np.uint16(0), b)
+
+
+def eye_bf16(n):
+    t = torch()
+    return t.eye(n, dtype=t.bfloat16, device="cuda")
+
+
+def oracle_w_hat_bits(W32):
+    ref = nf4.quantize(W32)
+    return nf4.dequantize(ref["codes"], ref["absmax_e4m3"], ref["dq_scale"],
+                          ref["dq_mean"]).reshape(W32.shape)
+
+
+@pytest.mark.parametrize("layer", [0, 2])
+def test_mlp_7b_one_hot_pins_bit_exact(layer):
+    """gate (11008x4096) and down (4096x11008): Y = Ŵᵀ with X = I and
+    dX = Ŵ with dY = I, over every output tile of both GEMMs."""
+    t = torch()
+    w = Inputs(3)
+    name, N, K = w.w.layers[layer]
+    r, alpha = w.w.rank, w.w.alpha
+    print(f"one-hot pins {name} {N}x{K}", flush=True)
+    W32 = w.weight(layer)
+    qt = G.gpu_quantize(G.dev_f32(W32))
+    w_hat = canon_zero(oracle_w_hat_bits(W32))
+    A = G.dev_bf16(w.lora_A(layer))
+    B0 = t.zeros(N, r, dtype=t.bfloat16, device="cuda")
+    # forward: X = I_K (M = K tokens), Y = Ŵᵀ
+    X = eye_bf16(K)
+    Y, _ = G.gpu_forward(qt, X, A, B0, r, alpha, t.bfloat16)
+    got = canon_zero(G.host_bf16(Y))
+    bad = int(np.count_nonzero(got != w_hat.T))
+    print(f"  forward X = I_{K}: {bad} of {got.size} outputs differ", flush=True)
+    assert bad == 0
+    del X, Y
+    # dX: dY = I_N (M = N tokens), dX = Ŵ
+    dY = eye_bf16(N)
+    Xb = G.dev_bf16(random_bf16((N, K), seed=7 + layer))
+    dX, dA, dB = G.gpu_backward(qt, Xb, dY, A, B0, r, alpha, None, t.bfloat16)
+    got = canon_zero(G.host_bf16(dX))
+    bad = int(np.count_nonzero(got != w_hat))
+    print(f"  dX with dY = I_{N}: {bad} of {got.size} outputs differ", flush=True)
+    assert bad == 0
+    assert np.all(G.host(dA) == 0)  # U = dY·B = 0
+
+
+def test_qproj_gemv_one_hot_covers_every_column():
+    """q_proj 4096x4096 at M = 16: call c has X[m] = e_{16c+m}; 256 calls
+    give Y[m][n] = Ŵ[n][16c + m] for every (n, k), bf16 and fp32 outputs."""
+    t = torch()
+    import quantized_fine_tuning_amd as q
+    w = Inputs(2)
+    N, K = w.shape(0)
+    r, alpha = w.w.rank, w.w.alpha
+    W32 = w.weight(0)
+    qt = G.gpu_quantize(G.dev_f32(W32))
+    w_hat = oracle_w_hat_bits(W32)
+    A = G.dev_bf16(w.lora_A(0))
+    B0 = t.zeros(N, r, dtype=t.bfloat16, device="cuda")
+    ws = q.workspace(q.qlora_nf4_sizes(N, K, 16, r)["fwd_ws_bytes"])
+    Yb = t.empty(K // 16, 16, N, dtype=t.bfloat16, device="cuda")
+    Yf = t.empty(K // 16, 16, N, dtype=t.float32, device="cuda")
+    eye = t.eye(K, dtype=t.bfloat16, device="cuda")
+    for c in range(K // 16):
+        X = eye[16 * c:16 * c + 16]
+        q.qlora_linear_fwd(qt, X, A, B0, r, alpha, Yb[c], None, ws)
+        q.qlora_linear_fwd(qt, X, A, B0, r, alpha, Yf[c], None, ws)
+    got = canon_zero(G.host_bf16(Yb).reshape(K, N))
+    bad = int(np.count_nonzero(got != canon_zero(w_hat.T)))
+    print(f"GEMV one-hot: {bad} of {got.size} bf16 outputs differ", flush=True)
+    assert bad == 0
+    gotf = G.host(Yf).reshape(K, N)
+    ref = linalg.bf16_to_f64(w_hat).T
+    assert np.array_equal(gotf.astype(np.float64), ref)
+
+
+def elementwise_bound(n, out16):
+    return n * 2.0 ** -24 + 2.0 ** -15 + (2.0 ** -9 if out16 else 0.0)
+
+
+def check_elementwise(got, ref, scale, n, out16, what):
+    err = linalg.rel_fro(got, ref)
+    den = np.where(scale > 0, scale, 1.0)
+    e = float(np.max(np.abs(got - ref) / den))
+    bound = elementwise_bound(n, out16)
+    print(f"  {what}: rel Frobenius {err:.2e}, max |err| / sum|terms| {e:.2e} (bound {bound:.2e})",
+          flush=True)
+    assert np.all(np.isfinite(got))
+    assert e <= bound, f"{what}: element error {e:.3e} above {bound:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_mlp_7b_full_size_every_element(layer):
+    """Every element of Y, dX, dA and dB of one 7B MLP linear at M = 4096,
+    r = 64, in the launch configuration the benchmark times."""
+    t = torch()
+    w = Inputs(3)
+    name, N, K = w.w.layers[layer]
+    M = w.w.tokens[0]
+    r, alpha = w.w.rank, w.w.alpha
+    s = alpha / r
+    print(f"7b MLP {name} {N}x{K} M={M} r={r}: every element", flush=True)
+    W32 = w.weight(layer)
+    qt = G.gpu_quantize(G.dev_f32(W32))
+    Wh = linalg.bf16_to_f64(oracle_w_hat_bits(W32))
+    Xb, Ab, Bb, dYb = w.X(layer, M), w.lora_A(layer), w.lora_B(layer), w.dY(layer, M)
+    Xd, Ad, Bd, dYd = (G.dev_bf16(a) for a in (Xb, Ab, Bb, dYb))
+    X, A, B, dY = (linalg.bf16_to_f64(a) for a in (Xb, Ab, Bb, dYb))
+    Yb, T = G.gpu_forward(qt, Xd, Ad, Bd, r, alpha, t.bfloat16)
+    Yf, _ = G.gpu_forward(qt, Xd, Ad, Bd, r, alpha, t.float32, save_T=False)
+    Y_ref, T_ref = linalg.linear_fwd(X, Wh, A, B, alpha, r)
+    XA = np.abs(X) @ np.abs(A).T  # magnitudes behind T
+    S = np.abs(X) @ np.abs(Wh).T + abs(s) * (XA @ np.abs(B).T)
+    n = K + 2 * r
+    eb = check_elementwise(G.out_f64(Yb), Y_ref, S, n, True, "Y bf16")
+    check_elementwise(G.out_f64(Yf), Y_ref, S, n, False, "Y fp32")
+    check_elementwise(G.out_f64(T), T_ref, XA, K, False, "T")
+    assert eb <= G.TOL_BF16
+    del Yb, Yf, Y_ref, S
+    dXb, dA, dB = G.gpu_backward(qt, Xd, dYd, Ad, Bd, r, alpha, T, t.bfloat16)
+    dXf, _, _ = G.gpu_backward(qt, Xd, dYd, Ad, Bd, r, alpha, None, t.float32)
+    dX_ref, dA_ref, dB_ref = linalg.linear_bwd(X, dY, Wh, A, B, alpha, r)
+    YB = np.abs(dY) @ np.abs(B)  # magnitudes behind U = dY·B
+    S = np.abs(dY) @ np.abs(Wh) + abs(s) * (YB @ np.abs(A))
+    n = N + 2 * r
+    ex = check_elementwise(G.out_f64(dXb), dX_ref, S, n, True, "dX bf16")
+    check_elementwise(G.out_f64(dXf), dX_ref, S, n, False, "dX fp32")
+    assert ex <= G.TOL_BF16
+    del S
+    SA = abs(s) * (YB.T @ np.abs(X))
+    SB = abs(s) * (np.abs(dY).T @ XA)
+    ea = check_elementwise(G.out_f64(dA), dA_ref, SA, N + M, False, "dA")
+    eB = check_elementwise(G.out_f64(dB), dB_ref, SB, K + M, False, "dB")
+    assert ea <= G.TOL_F32 and eB <= G.TOL_F32
