@@ -26,6 +26,11 @@
  *   - Shapes: W is [N, K] = [out_features, in_features] with K % 64 == 0 and
  *     N % 8 == 0; X is [M, K]; Y and dY are [M, N]; LoRA A is [r, K], B is
  *     [N, r], 1 <= r <= 256; s = alpha / r.  M may be 0.
+ *   - Limits of one linear pass (forward or backward), from the kernels'
+ *     32-bit buffer offsets: N*K/2 < 2^31 (packed codes),
+ *     M*max(N, K) < 2^30 (activations and gradients of one call) and
+ *     2*Rp*round_up(M, 64)*2 < 2^31 with Rp = round_up(r, 32); beyond them
+ *     the call returns QLORA_ERR_INVALID_ARG.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H

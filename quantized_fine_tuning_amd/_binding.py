@@ -152,6 +152,33 @@ def _ptr(t, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name: str, shape, dtypes):
+    """Host-side check of a tensor's shape and dtype before its pointer goes to
+    the library (a wrong shape would otherwise become an out-of-bounds device
+    access or silently reinterpreted data)."""
+    if t is None:
+        raise ValueError(f"{name} is None")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+
+
+def _expect_numel(t, name: str, n: int, dtype):
+    if t is None:
+        raise ValueError(f"{name} is None")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 1 or t.numel() < n:
+        raise ValueError(f"{name}: needs a 1-d tensor of at least {n} elements, got shape {tuple(t.shape)}")
+
+
+def _bytes(t, name: str) -> int:
+    if t is None:
+        raise ValueError(f"{name} is None")
+    return t.numel() * t.element_size()
+
+
 def _dtype(t, name: str) -> int:
     torch = _torch()
     if t.dtype == torch.float32:
@@ -189,6 +216,12 @@ class Nf4Tensor:
                    torch.empty(1, dtype=torch.float32, device=device))
 
     def c_struct(self) -> qlora_nf4_t:
+        torch = _torch()
+        nb = self.n_rows * self.n_cols // 64
+        _expect_numel(self.codes, "codes", self.n_rows * self.n_cols // 2, torch.uint8)
+        _expect_numel(self.absmax_e4m3, "absmax_e4m3", nb, torch.uint8)
+        _expect_numel(self.dq_scale, "dq_scale", (nb + 255) // 256, torch.float32)
+        _expect_numel(self.dq_mean, "dq_mean", 1, torch.float32)
         return qlora_nf4_t(self.n_rows, self.n_cols, _ptr(self.codes, "codes"),
                            _ptr(self.absmax_e4m3, "absmax_e4m3"), _ptr(self.dq_scale, "dq_scale"),
                            _ptr(self.dq_mean, "dq_mean"))
@@ -216,9 +249,11 @@ def qlora_nf4_codebook() -> list:
 
 
 def qlora_nf4_quantize(W, out: Nf4Tensor, ws, stream=None) -> None:
+    torch = _torch()
     if W.dim() != 2:
         raise ValueError("W must be [N, K]")
     N, K = W.shape
+    _expect(W, "W", (out.n_rows, out.n_cols), (torch.float32, torch.bfloat16))
     st = out.c_struct()
     _check(lib.qlora_nf4_quantize(_ptr(W, "W"), _dtype(W, "W"), N, K, ctypes.byref(st),
                                   _ptr(ws, "ws"), ws.numel() * ws.element_size(),
@@ -226,6 +261,8 @@ def qlora_nf4_quantize(W, out: Nf4Tensor, ws, stream=None) -> None:
 
 
 def qlora_dequantize(q: Nf4Tensor, out, stream=None) -> None:
+    torch = _torch()
+    _expect(out, "out", (q.n_rows, q.n_cols), (torch.bfloat16, torch.float16))
     st = q.c_struct()
     _check(lib.qlora_dequantize(ctypes.byref(st), _ptr(out, "out"), _dtype(out, "out"),
                                 _stream(stream)))
@@ -237,14 +274,38 @@ def qlora_linear_fwd(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, ws,
     qlora_linear_fwd_ex(W, X, A, B, r, alpha, Y, T_save, ws, _dtype(X, "X"), stream)
 
 
+def _compute_torch_dtype(compute_dtype: int):
+    torch = _torch()
+    if compute_dtype == QLORA_BF16:
+        return torch.bfloat16
+    if compute_dtype == QLORA_F16:
+        return torch.float16
+    raise ValueError(f"compute_dtype {compute_dtype}: QLORA_BF16 or QLORA_F16")
+
+
+def _check_fwd(W: Nf4Tensor, X, A, B, r: int, Y, T_save, cdt):
+    torch = _torch()
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M = X.shape[0]
+    N, K = W.n_rows, W.n_cols
+    _expect(X, "X", (M, K), (cdt,))
+    _expect(A, "A", (r, K), (cdt,))
+    _expect(B, "B", (N, r), (cdt,))
+    _expect(Y, "Y", (M, N), (torch.float32, cdt))
+    if T_save is not None:
+        _expect(T_save, "T_save", (M, r), (torch.float32,))
+    return M
+
+
 def qlora_linear_fwd_ex(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, ws, compute_dtype: int,
                         stream=None) -> None:
-    M = X.shape[0]
+    M = _check_fwd(W, X, A, B, r, Y, T_save, _compute_torch_dtype(compute_dtype))
     st = W.c_struct()
     _check(lib.qlora_linear_fwd_ex(ctypes.byref(st), _ptr(X, "X"), M, _ptr(A, "A"), _ptr(B, "B"),
                                    r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
                                    _ptr(T_save, "T_save"), _ptr(ws, "ws"),
-                                   ws.numel() * ws.element_size(), compute_dtype, _stream(stream)))
+                                   _bytes(ws, "ws"), compute_dtype, _stream(stream)))
 
 
 def qlora_linear_bwd(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,
@@ -255,12 +316,26 @@ def qlora_linear_bwd(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, d
 
 def qlora_linear_bwd_ex(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,
                         compute_dtype: int, stream=None) -> None:
+    torch = _torch()
+    cdt = _compute_torch_dtype(compute_dtype)
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be [M, K]")
     M = X.shape[0]
+    N, K = W.n_rows, W.n_cols
+    _expect(X, "X", (M, K), (cdt,))
+    _expect(dY, "dY", (M, N), (cdt,))
+    _expect(A, "A", (r, K), (cdt,))
+    _expect(B, "B", (N, r), (cdt,))
+    if T_saved is not None:
+        _expect(T_saved, "T_saved", (M, r), (torch.float32,))
+    _expect(dX, "dX", (M, K), (torch.float32, cdt))
+    _expect(dA, "dA", (r, K), (torch.float32,))
+    _expect(dB, "dB", (N, r), (torch.float32,))
     st = W.c_struct()
     _check(lib.qlora_linear_bwd_ex(ctypes.byref(st), _ptr(X, "X"), _ptr(dY, "dY"), M, _ptr(A, "A"),
                                    _ptr(B, "B"), r, float(alpha), _ptr(T_saved, "T_saved"),
                                    _ptr(dX, "dX"), _dtype(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
-                                   _ptr(ws, "ws"), ws.numel() * ws.element_size(), compute_dtype,
+                                   _ptr(ws, "ws"), _bytes(ws, "ws"), compute_dtype,
                                    _stream(stream)))
 
 
@@ -281,8 +356,14 @@ def qlora_adamw_step(tensors, lr: float, beta1: float, beta2: float, eps: float,
     tensors = list(tensors)
     arr = (qlora_adamw_tensor_t * max(1, len(tensors)))()
     dt = None
+    torch = _torch()
     for i, (p, g, m, v) in enumerate(tensors):
         d = _dtype(p, f"tensors[{i}].param")
+        if d not in (QLORA_BF16, QLORA_F32):
+            raise ValueError(f"tensors[{i}].param: bf16 or fp32")
+        for t_, nm in ((g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
+            if t_.dtype != torch.float32:
+                raise ValueError(f"tensors[{i}].{nm}: dtype {t_.dtype}, expected float32")
         if dt is not None and d != dt:
             raise ValueError("every param must have the same dtype")
         dt = d
@@ -298,6 +379,10 @@ def qlora_adamw_step(tensors, lr: float, beta1: float, beta2: float, eps: float,
 
 def qlora_merge_lora(W: Nf4Tensor, A, B, r: int, alpha: float, out, stream=None) -> None:
     """out [N, K] (bf16 or fp16) = Ŵ + (alpha / r)·B·A, rounded once."""
+    torch = _torch()
+    _expect(A, "A", (r, W.n_cols), (torch.bfloat16,))
+    _expect(B, "B", (W.n_rows, r), (torch.bfloat16,))
+    _expect(out, "out", (W.n_rows, W.n_cols), (torch.bfloat16, torch.float16))
     st = W.c_struct()
     _check(lib.qlora_merge_lora(ctypes.byref(st), _ptr(A, "A"), _ptr(B, "B"), r, float(alpha),
                                 _ptr(out, "out"), _dtype(out, "out"), _stream(stream)))
@@ -319,22 +404,37 @@ class QTensor:
                    torch.empty(n_rows * n_cols // 64, dtype=torch.float32, device=device))
 
     def c_struct(self) -> qlora_qtensor_t:
+        torch = _torch()
+        if self.fmt not in FORMATS:
+            raise ValueError(f"format {self.fmt!r}: one of {sorted(FORMATS)}")
+        nbytes = self.n_rows * self.n_cols * (2 if self.fmt == "int8" else 1) // 2
+        _expect_numel(self.codes, "codes", nbytes, torch.uint8)
+        _expect_numel(self.absmax, "absmax", self.n_rows * self.n_cols // 64, torch.float32)
         return qlora_qtensor_t(self.n_rows, self.n_cols, FORMATS[self.fmt], _ptr(self.codes, "codes"),
                                _ptr(self.absmax, "absmax"))
 
 
 def qlora_quantize_format(W, out: QTensor, stream=None) -> None:
+    torch = _torch()
+    _expect(W, "W", (out.n_rows, out.n_cols), (torch.float32, torch.bfloat16))
     N, K = W.shape
     st = out.c_struct()
     _check(lib.qlora_quantize_format(_ptr(W, "W"), _dtype(W, "W"), N, K, ctypes.byref(st), _stream(stream)))
 
 
 def qlora_dequantize_format(q: QTensor, out, stream=None) -> None:
+    torch = _torch()
+    _expect(out, "out", (q.n_rows, q.n_cols), (torch.bfloat16,))
     st = q.c_struct()
     _check(lib.qlora_dequantize_format(ctypes.byref(st), _ptr(out, "out"), _dtype(out, "out"), _stream(stream)))
 
 
 def qlora_gemv_format(q: QTensor, X, Y, stream=None) -> None:
+    torch = _torch()
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    _expect(X, "X", (X.shape[0], q.n_cols), (torch.bfloat16,))
+    _expect(Y, "Y", (X.shape[0], q.n_rows), (torch.float32, torch.bfloat16))
     st = q.c_struct()
     _check(lib.qlora_gemv_format(ctypes.byref(st), _ptr(X, "X"), X.shape[0], _ptr(Y, "Y"), _dtype(Y, "Y"),
                                  _stream(stream)))

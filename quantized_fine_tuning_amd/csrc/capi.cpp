@@ -78,6 +78,22 @@ qlora_status check_tensor(const char* fn, const qlora_nf4_t* q) {
   return QLORA_OK;
 }
 
+// Limits of one linear pass, from the 32-bit byte offsets of the kernels'
+// buffer loads (one buffer resource spans at most 2^31 - 1 bytes): the packed
+// codes of the weight, the activations and gradients of one call, and the
+// transposed hi/lo splits [2Rp, round_up(M, 64)] of the low-rank factors.
+qlora_status check_linear_limits(const char* fn, int64_t M, int64_t N, int64_t K, int32_t r) {
+  const int64_t lim = int64_t(1) << 31;
+  if (N * K / 2 >= lim) return fail(QLORA_ERR_INVALID_ARG, "%s: N*K/2 = %lld code bytes (limit 2^31)", fn, (long long)(N * K / 2));
+  const int64_t wide = N > K ? N : K;
+  if (M > 0 && M >= (lim / 2) / wide)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: M*max(N, K) = %lld elements (limit 2^30)", fn, (long long)(M * wide));
+  const int64_t Rp = (r + 31) / 32 * 32, Mp = (M + 63) / 64 * 64;
+  if (2 * Rp * Mp * 2 >= lim)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld too large for rank %d (2*Rp*Mp*2 >= 2^31)", fn, (long long)M, r);
+  return QLORA_OK;
+}
+
 qlora_status hip_status(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(QLORA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return ok();
@@ -111,8 +127,8 @@ qlora_status qlora_nf4_sizes(int64_t N, int64_t K, int64_t M_max, int32_t r, qlo
   out->scale_bytes = (size_t)(4 * ((nb + 255) / 256));
   out->mean_bytes = 4;
   out->quantize_ws_bytes = qnf4::quant_layout(N, K).total;
-  out->fwd_ws_bytes = qnf4::fwd_layout(M_max, N, K, r).total;
-  out->bwd_ws_bytes = qnf4::bwd_layout(M_max, N, K, r).total;
+  out->fwd_ws_bytes = qnf4::fwd_ws_bytes_max(M_max, N, K, r);
+  out->bwd_ws_bytes = qnf4::bwd_ws_bytes_max(M_max, N, K, r);
   return ok();
 }
 
@@ -158,17 +174,21 @@ qlora_status qlora_linear_fwd(const qlora_nf4_t* W, const void* X, int64_t M, co
   return qlora_linear_fwd_ex(W, X, M, A, B, r, alpha, Y, y_dtype, T_save, ws, ws_bytes, QLORA_BF16, stream);
 }
 
-qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
-                                 const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
-                                 float* T_save, void* ws, size_t ws_bytes, qlora_dtype compute_dtype,
-                                 void* stream) {
-  const char* fn = "qlora_linear_fwd";
+}  // extern "C"
+
+namespace {
+
+// Arguments of a forward pass, everything but the workspace.
+qlora_status check_fwd_args(const char* fn, const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
+                            const void* B, int32_t r, const void* Y, qlora_dtype y_dtype, const float* T_save,
+                            qlora_dtype compute_dtype) {
   qlora_status st = check_tensor(fn, W);
   if (st != QLORA_OK) return st;
   if (compute_dtype != QLORA_BF16 && compute_dtype != QLORA_F16)
     return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: compute_dtype=%d (BF16 or F16)", fn, compute_dtype);
   if ((st = check_rank(fn, r)) != QLORA_OK) return st;
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
+  if ((st = check_linear_limits(fn, M, W->n_rows, W->n_cols, r)) != QLORA_OK) return st;
   if (y_dtype != QLORA_F32 && y_dtype != compute_dtype)
     return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: y_dtype=%d (F32 or the compute dtype)", fn, y_dtype);
   CHECK_PTR(A);
@@ -178,6 +198,20 @@ qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M,
     CHECK_PTR(Y);
   }
   CHECK_OPT_PTR(T_save);
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
+                                 const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
+                                 float* T_save, void* ws, size_t ws_bytes, qlora_dtype compute_dtype,
+                                 void* stream) {
+  const char* fn = "qlora_linear_fwd";
+  qlora_status st = check_fwd_args(fn, W, X, M, A, B, r, Y, y_dtype, T_save, compute_dtype);
+  if (st != QLORA_OK) return st;
   const qnf4::FwdLayout L = qnf4::fwd_layout(M, W->n_rows, W->n_cols, r);
   if (ws_bytes < L.total)
     return fail(QLORA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
@@ -189,6 +223,7 @@ qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M,
                             alpha / (float)r, Y, y_dtype != QLORA_F32, T_save,
                             static_cast<char*>(ws), L, compute_dtype == QLORA_F16, static_cast<hipStream_t>(stream)));
 }
+
 
 qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* dY, int64_t M,
                               const void* A, const void* B, int32_t r, float alpha,
@@ -210,6 +245,7 @@ qlora_status qlora_linear_bwd_ex(const qlora_nf4_t* W, const void* X, const void
     return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: compute_dtype=%d (BF16 or F16)", fn, compute_dtype);
   if ((st = check_rank(fn, r)) != QLORA_OK) return st;
   if (M < 0) return fail(QLORA_ERR_INVALID_ARG, "%s: M=%lld < 0", fn, (long long)M);
+  if ((st = check_linear_limits(fn, M, W->n_rows, W->n_cols, r)) != QLORA_OK) return st;
   if (dx_dtype != QLORA_F32 && dx_dtype != compute_dtype)
     return fail(QLORA_ERR_UNSUPPORTED_DTYPE, "%s: dx_dtype=%d (F32 or the compute dtype)", fn, dx_dtype);
   CHECK_PTR(A);

@@ -118,6 +118,8 @@ struct FwdLayout {
   SkPlan pT;
 };
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+// The largest fwd_layout(M, ...).total over M in [0, M_max].
+size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r);
 
 hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
                           const uint16_t* B, int32_t r, float scale, void* Y, bool y16,
@@ -132,6 +134,8 @@ struct BwdLayout {
   SkPlan pT, pU, pA, pB;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+// The largest bwd_layout(M, ...).total over M in [0, M_max].
+size_t bwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r);
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,

@@ -75,6 +75,49 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   return L;
 }
 
+// Workspace bytes that cover every M in [0, M_max].  The split reductions'
+// partial-sum areas (tiles x cmax slots) are not monotone in M: cmax, the
+// most workgroups that share one tile, depends on how the tiles fall on the
+// workgroups.  Every plan depends on M only through ceil(M / 64), so the
+// maximum is taken over those values; where a plan has at least as many
+// tiles as workgroups, each workgroup's run covers a whole tile's units and
+// cmax <= 2, so tiles x 2 slots bound it (monotone in M) and the exact plan
+// is not needed there.
+namespace {
+size_t rowred_bytes_bound(int64_t M, int64_t Kred, int64_t Rp) {
+  const int64_t tiles = ((M + 63) / 64) * ((Rp + 63) / 64);
+  if (tiles >= (int64_t)kSkWorkgroups) return round_up(tiles * 2 * 64 * 64 * 4, 256);
+  return round_up(rowred_partial_bytes(rowred_plan(M, Kred, Rp)), 256);
+}
+size_t colred_bytes_bound(int64_t M, int64_t Pn, int64_t Rp) {
+  const int64_t tiles = ((Pn + 127) / 128) * ((Rp + 63) / 64);
+  if (tiles >= (int64_t)kSkWorkgroups) return round_up(tiles * 2 * 128 * 64 * 4, 256);
+  return round_up(colred_partial_bytes(colred_plan(M, Pn, Rp)), 256);
+}
+}  // namespace
+
+size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
+  const FwdLayout L = fwd_layout(M_max, N, K, r);
+  if (M_max <= 16) return L.total;
+  const int64_t Rp = lora_rp(r);
+  size_t p = 0;
+  for (int64_t M = 64; M < M_max + 64; M += 64) p = std::max(p, rowred_bytes_bound(std::min(M, M_max), K, Rp));
+  return L.off_P + p;
+}
+
+size_t bwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
+  const BwdLayout L = bwd_layout(M_max, N, K, r);
+  if (M_max <= 0) return L.total;
+  const int64_t Rp = lora_rp(r);
+  size_t p = 0;
+  for (int64_t M = 64; M < M_max + 64; M += 64) {
+    const int64_t m = std::min(M, M_max);
+    p = std::max({p, rowred_bytes_bound(m, K, Rp), rowred_bytes_bound(m, N, Rp), colred_bytes_bound(m, K, Rp),
+                  colred_bytes_bound(m, N, Rp)});
+  }
+  return L.off_P + p;
+}
+
 hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
                           const uint16_t* B, int32_t r, float scale, void* Y, bool y16,
                           float* T, char* ws, const FwdLayout& L, bool f16, hipStream_t st) {
