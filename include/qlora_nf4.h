@@ -174,6 +174,28 @@ qlora_status qlora_linear_bwd_ex(const qlora_nf4_t* W, const void* X,
                                  void* ws, size_t ws_bytes,
                                  qlora_dtype compute_dtype, void* stream);
 
+/* qlora_linear_fwd for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * forward pass (bf16 compute) without a workspace argument: its scratch
+ * memory (T, the hi/lo split of s·T, the [B | B] operand and the partial sums
+ * of the split reductions) lives in a static 32 MiB device array of the
+ * library, one per GPU, held until the process ends.  The library allocates
+ * and frees nothing.
+ *   Arguments as qlora_linear_fwd; the calling thread's current device must
+ *   be the device of `stream`.
+ *   A call that needs more than 32 MiB of scratch (the fwd_ws_bytes that
+ *   qlora_nf4_sizes reports for its M) returns QLORA_ERR_WORKSPACE_TOO_SMALL
+ *   before any HIP call; every linear of the 7B and 65B shapes fits up to
+ *   8192 tokens at rank 64.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ *   call's contents (nothing relies on them): calls that overlap on one GPU
+ *   (other streams or host threads, unordered) race and give wrong results;
+ *   the caller orders them. */
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_t* W, const void* X, int64_t M,
+                                      const void* A, const void* B, int32_t r,
+                                      float alpha, void* Y, qlora_dtype y_dtype,
+                                      float* T_save, void* stream);
+
 /* One tensor of LoRA parameters for qlora_adamw_step (all device memory,
  * 16-byte aligned when n > 0):
  *   param       n elements, bf16 or fp32 (the call's param_dtype), updated in

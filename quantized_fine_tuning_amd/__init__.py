@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     qlora_linear_bwd,
     qlora_linear_fwd,
     qlora_linear_fwd_ex,
+    qlora_linear_fwd_noalloc,
     qlora_linear_bwd_ex,
     qlora_merge_lora,
     qlora_quantize_format,

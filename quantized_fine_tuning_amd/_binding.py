@@ -29,7 +29,7 @@ EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_l
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
            "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora",
            "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format",
-           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex")
+           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qlora_linear_fwd_noalloc")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -116,6 +116,8 @@ def _load():
     lib.qlora_linear_bwd_ex.argtypes = [P(qlora_nf4_t), vp, vp, i64, vp, vp, i32, f32, vp, vp, i32,
                                         vp, vp, vp, sz, i32, vp]
     lib.qlora_linear_fwd_ex.restype = i32
+    lib.qlora_linear_fwd_noalloc.argtypes = [P(qlora_nf4_t), vp, i64, vp, vp, i32, f32, vp, i32, vp, vp]
+    lib.qlora_linear_fwd_noalloc.restype = i32
     lib.qlora_linear_bwd_ex.restype = i32
     lib.qlora_quantize_format.argtypes = [vp, i32, i64, i64, P(qlora_qtensor_t), vp]
     lib.qlora_dequantize_format.argtypes = [P(qlora_qtensor_t), vp, i32, vp]
@@ -306,6 +308,18 @@ def qlora_linear_fwd_ex(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save, 
                                    r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
                                    _ptr(T_save, "T_save"), _ptr(ws, "ws"),
                                    _bytes(ws, "ws"), compute_dtype, _stream(stream)))
+
+
+def qlora_linear_fwd_noalloc(W: Nf4Tensor, X, A, B, r: int, alpha: float, Y, T_save=None,
+                             stream=None) -> None:
+    """The bf16 forward with the library's static scratch instead of a
+    workspace (for callers that cannot allocate).  Calls that overlap on one
+    GPU race: order them."""
+    M = _check_fwd(W, X, A, B, r, Y, T_save, _torch().bfloat16)
+    st = W.c_struct()
+    _check(lib.qlora_linear_fwd_noalloc(ctypes.byref(st), _ptr(X, "X"), M, _ptr(A, "A"), _ptr(B, "B"),
+                                        r, float(alpha), _ptr(Y, "Y"), _dtype(Y, "Y"),
+                                        _ptr(T_save, "T_save"), _stream(stream)))
 
 
 def qlora_linear_bwd(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved, dX, dA, dB, ws,

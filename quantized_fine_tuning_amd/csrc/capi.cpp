@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "host.h"
@@ -201,6 +202,39 @@ qlora_status check_fwd_args(const char* fn, const qlora_nf4_t* W, const void* X,
   return QLORA_OK;
 }
 
+// The static scratch of qlora_linear_fwd_noalloc: one copy per GPU, held
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it passes the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,6 +258,27 @@ qlora_status qlora_linear_fwd_ex(const qlora_nf4_t* W, const void* X, int64_t M,
                             static_cast<char*>(ws), L, compute_dtype == QLORA_F16, static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_t* W, const void* X, int64_t M, const void* A,
+                                      const void* B, int32_t r, float alpha, void* Y, qlora_dtype y_dtype,
+                                      float* T_save, void* stream) {
+  const char* fn = "qlora_linear_fwd_noalloc";
+  qlora_status st = check_fwd_args(fn, W, X, M, A, B, r, Y, y_dtype, T_save, QLORA_BF16);
+  if (st != QLORA_OK) return st;
+  const qnf4::FwdLayout L = qnf4::fwd_layout(M, W->n_rows, W->n_cols, r);
+  if (L.total > kStaticScratchBytes)
+    return fail(QLORA_ERR_WORKSPACE_TOO_SMALL,
+                "%s: this call needs %zu bytes of scratch; the static scratch holds %zu (use qlora_linear_fwd "
+                "with a workspace)",
+                fn, L.total, kStaticScratchBytes);
+  if (M == 0) return ok();
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(fn, e);
+  return hip_status(fn, qnf4::launch_forward(view(W), static_cast<const uint16_t*>(X), M,
+                                             static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), r,
+                                             alpha / (float)r, Y, y_dtype != QLORA_F32, T_save,
+                                             static_cast<char*>(ws), L, false, static_cast<hipStream_t>(stream)));
+}
 
 qlora_status qlora_linear_bwd(const qlora_nf4_t* W, const void* X, const void* dY, int64_t M,
                               const void* A, const void* B, int32_t r, float alpha,

@@ -1,6 +1,7 @@
 """Host-side contracts of the C ABI and the binding, checked without a GPU:
 workspace sizes that cover every smaller token count, the per-call limits of
-the kernels' 32-bit buffer offsets, and the binding's shape and dtype checks (a mis-shaped tensor must raise
+the kernels' 32-bit buffer offsets, the static-scratch forward's size bound,
+and the binding's shape and dtype checks (a mis-shaped tensor must raise
 before any pointer reaches the library)."""
 
 import ctypes
@@ -90,6 +91,27 @@ def test_workload_shapes_are_within_the_limits():
         assert st == q.QLORA_ERR_WORKSPACE_TOO_SMALL  # passed the limits, stopped at the workspace
 
 
+def test_noalloc_forward_rejects_calls_beyond_its_scratch():
+    f = q.lib.qlora_linear_fwd_noalloc
+    # 65B gate at 48000 tokens needs more than the 32 MiB static scratch
+    d = desc(22016, 8192)
+    assert fwd_need(22016, 8192, 48000, 64) > 32 << 20
+    st = f(ctypes.byref(d), FAKE, 48000, FAKE, FAKE, 64, 16.0, FAKE, q.QLORA_BF16, None, None)
+    assert st == q.QLORA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch holds 33554432" in q.lib.qlora_last_error().decode()
+    # argument errors come first, as in qlora_linear_fwd
+    assert f(ctypes.byref(d), FAKE, 32, FAKE, FAKE, 0, 16.0, FAKE, q.QLORA_BF16, None, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, q.QLORA_F16, None, None) == \
+        q.QLORA_ERR_UNSUPPORTED_DTYPE
+    assert f(ctypes.byref(d), None, 32, FAKE, FAKE, 8, 16.0, FAKE, q.QLORA_BF16, None, None) == \
+        q.QLORA_ERR_INVALID_ARG
+    # every workload linear fits at its token count
+    for N, K, M in ((11008, 4096, 8192), (4096, 11008, 8192), (22016, 8192, 2048), (8192, 22016, 2048),
+                    (8192, 8192, 8192), (22016, 8192, 8192)):
+        assert q.qlora_nf4_sizes(N, K, M, 64)["fwd_ws_bytes"] <= 32 << 20, (N, K, M)
+
+
 # ---------------------------------------------------------------- binding
 
 
@@ -127,6 +149,8 @@ def test_binding_forward_checks_shapes_and_dtypes():
         a[key] = val
         with pytest.raises(ValueError, match=msg):
             q.qlora_linear_fwd(W, a["X"], a["A"], a["B"], 8, 16.0, a["Y"], a["T"], ws)
+        with pytest.raises(ValueError, match=msg):
+            q.qlora_linear_fwd_noalloc(W, a["X"], a["A"], a["B"], 8, 16.0, a["Y"], a["T"])
     # correct shapes reach the device check
     with pytest.raises(ValueError, match="GPU tensor"):
         q.qlora_linear_fwd(W, good["X"], good["A"], good["B"], 8, 16.0, good["Y"], good["T"], ws)
