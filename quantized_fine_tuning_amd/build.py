@@ -43,15 +43,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, csrc: Path = CSRC, out: Path = LIB) -> Path:
-    """Compiles every source to an object (in parallel), then links."""
+def build(verbose: bool = False, csrc: Path = CSRC, out: Path = LIB, extra_flags=()) -> Path:
+    """Compiles every source to an object (in parallel), then links.
+    extra_flags go on every compile and the link line (a sanitizer build of
+    the host code passes ``-Xarch_host -fsanitize=...`` here)."""
     objdir = out.parent / "_build"
     objdir.mkdir(exist_ok=True)
     cc = hipcc()
 
     def compile_one(name: str) -> Path:
         obj = objdir / (name + ".o")
-        cmd = [cc, *[f for f in FLAGS if f != "-shared"], "-c", "-I", str(csrc), "-I", str(INCLUDE), "-x", "hip",
+        cmd = [cc, *[f for f in FLAGS if f != "-shared"], *extra_flags, "-c", "-I", str(csrc), "-I", str(INCLUDE), "-x", "hip",
                str(csrc / name), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -65,7 +67,7 @@ def build(verbose: bool = False, csrc: Path = CSRC, out: Path = LIB) -> Path:
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = out.with_suffix(".so.tmp")
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc", "-o", str(tmp),
+    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc", *extra_flags, "-o", str(tmp),
            *map(str, objs)]
     if verbose:
         print(" ".join(cmd), flush=True)

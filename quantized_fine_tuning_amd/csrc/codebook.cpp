@@ -13,6 +13,10 @@
 // precision; each level is then rounded to the nearest fp32.
 #include <cfloat>
 #include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "host.h"
@@ -55,12 +59,38 @@ Codebook build() {
   return cb;
 }
 
+// The quantize kernels find a code through a table of cells: |x| in
+// [2^-5, 1] is cut into cells by its exponent and top 3 mantissa bits (bits
+// 20..30 of the fp32 pattern), and each cell may hold at most one threshold
+// (code = thresholds below the cell + (x > the one inside)); |x| < 2^-5 must
+// hold none.  Returns false if the thresholds break that.
+bool cells_hold_one_threshold(const Codebook& cb) {
+  int count[2][512] = {};
+  for (int j = 0; j < 15; ++j) {
+    const float t = cb.t[j];
+    if (!(std::fabs(t) > 0x1p-5f) || !(std::fabs(t) < 1.0f)) return false;
+    uint32_t u;
+    std::memcpy(&u, &t, 4);
+    // cells are [lo, hi) for x >= 0 and (-hi, -lo] for x < 0: either way
+    // the cell of t is given by the bits of |t|
+    const uint32_t cell = (u & 0x7fffffffu) >> 20;
+    if (++count[u >> 31][cell & 511] > 1) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 const Codebook& codebook() {
   static Codebook cb;
   static std::once_flag once;
-  std::call_once(once, [] { cb = build(); });
+  std::call_once(once, [] {
+    cb = build();
+    if (!cells_hold_one_threshold(cb)) {
+      std::fprintf(stderr, "qlora_nf4: NF4 thresholds break the quantizer's one-threshold-per-cell table\n");
+      std::abort();
+    }
+  });
   return cb;
 }
 

@@ -52,8 +52,8 @@ struct QTraits<uint16_t> {
 // thresholds t_0 < ... < t_14; every |t_j| > 2^-5, so |x| < 2^-5 has the zero
 // code 7.  For 2^-5 <= |x| <= 1, cut each binade [2^e, 2^(e+1)) of |x| into
 // 8 cells by the top 3 mantissa bits (bits 20..30 of |x| index the cell):
-// 41 cells per sign, and no cell holds more than one threshold (checked
-// where the codebook is built).  Cell c of a sign stores base = the count of
+// 41 cells per sign, and no cell holds more than one threshold (codebook()
+// checks this when it builds the thresholds and stops the process if not).  Cell c of a sign stores base = the count of
 // thresholds below the whole cell and t* = the threshold inside it (or +inf):
 // code(x) = base + (x > t*).  Cell 0 of each sign covers |x| < 2^-5 (base
 // 7, t* = +inf).  Table: 42 cells for x >= 0, then 42 for x < 0.
