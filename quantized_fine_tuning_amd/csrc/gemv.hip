@@ -4,101 +4,150 @@
 // 16 bit on the fly for every product; with few tokens the product is bound by
 // streaming the packed codes from HBM, so this path reads each code exactly
 // once, keeps as many bytes in flight as possible and everything else small.
+// Two launches:
 //
-//   lora_down_small_kernel  T = X·Aᵀ (M x r, fp32) for one 16-wide slice of r
-//                           per workgroup: 16 waves split K, all loads issued
-//                           first, MFMA products, fixed-order combination of
-//                           the 16 partial tiles.
-//   gemv_kernel             one workgroup of 16 waves per 16 weight rows.  Lane
-//                           (row l % 16, q = l / 16) owns whole NF4 blocks (64
-//                           codes, one decoded constant c'); a "block group" is
-//                           4 consecutive blocks of the 16 rows, q taking one
-//                           each, and feeds 8 v_mfma_f32_16x16x32_bf16: MFMA t
-//                           takes codes 8t..8t+7 of every lane's block (the
-//                           A operand, X padded to 16 rows, uses the same
-//                           k slots).  Wave w takes block groups w, w+16, ...;
-//                           the codes, constants and X fragments of its next
-//                           group are loaded before the current one is
-//                           dequantized.  Each value is RNE_bf16(fl32(q_c * c'))
-//                           with q_c read from a 16-entry LDS codebook (one
-//                           address per code: no bank conflicts).  The LoRA
-//                           term s·T·Bᵀ is 2 MFMAs per 32 ranks in wave 0 (A
-//                           operand the bf16 hi/lo split of s·T), and the 16
-//                           partial tiles are combined in a fixed order, one
-//                           thread per output.
+//   lora_down_split_kernel  partial products of T = X·Aᵀ: one workgroup of 4
+//                           waves per 256-wide slice of K and 16 ranks, MFMA
+//                           products, the 4 waves' tiles summed in a fixed
+//                           order; a tiny grid (K/256 x r/16 workgroups).
+//   gemv_kernel             one workgroup of 16 waves per 16 weight rows.
+//                           Lane (row l % 16, q = l / 16) owns whole NF4 blocks
+//                           (64 codes, one decoded constant c'); a "block
+//                           group" is 4 consecutive blocks of the 16 rows, q
+//                           taking one each, and feeds 8
+//                           v_mfma_f32_16x16x32_bf16: MFMA t takes codes
+//                           8t..8t+7 of every lane's block (the A operand, X
+//                           padded to 16 rows and staged in LDS when small,
+//                           uses the same k slots).  Each value is
+//                           RNE_bf16(fl32(q_c * c')) with q_c read from a
+//                           16-entry LDS codebook (one address per code: no
+//                           bank conflicts).  The waves' partial tiles are
+//                           combined in a fixed order, one thread per output,
+//                           which also adds s·Σ_j T[m][j]·B[n][j] in fp32, T
+//                           summed from the split kernel's partial tiles in
+//                           slice order (requested at the kernel's start).
+//
+// Measured on the 4096x4096 q_proj weight (M = 1): computing T inside every
+// workgroup (each reading all of A) delayed the data by ~3.4 us; summing the
+// partial tiles with loads issued one after the other in the epilogue cost
+// ~3.7 us; the X fragments loaded by every wave from global memory ~1.6 us.
 #include "host.h"
 
 namespace qnf4 {
 namespace {
 
-constexpr int kWaves = 16, kThreads = 64 * kWaves;
-constexpr int kDownSteps = 8;  // 32-wide K steps per wave and pass
+constexpr int GEMV_ROWS = 16;
+constexpr int kTSlice = 256;  // reduction elements per T partial tile
 
-// T = X·Aᵀ (M x r, fp32) for one 16-wide slice of r per workgroup of 16
-// waves.  Wave w takes the 32-wide K steps w, w + 16, ...; each pass issues
-// the loads of 8 steps before their MFMAs (for K = 4096 one pass: every load
-// of the kernel is in flight at once).  The 16 partial tiles are combined in
-// a fixed order.
+// Partial tiles of T = X·Aᵀ: workgroup (s, jt) sums k in [256s, 256s + 256)
+// for ranks [16jt, +16) and all 16 token rows (rows past M and ranks past r
+// read as zero), 4 waves of 64 k each, and writes the 16 x 16 tile
+// P[(s * JT + jt) * 256 + 16m + j] (fp32).
 template <bool F16>
-__global__ __launch_bounds__(kThreads) void lora_down_small_kernel(const uint16_t* __restrict__ X,
-                                                                   int M, int64_t K,
-                                                                   const uint16_t* __restrict__ A,
-                                                                   int r, float* __restrict__ T) {
-  __shared__ f32x4_t s_acc[kWaves][64];
+__global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
+                                                              const uint16_t* __restrict__ A, int r,
+                                                              float* __restrict__ P) {
+  __shared__ f32x4_t s_acc[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
-  const int j0 = 16 * blockIdx.x;
-  // A operand: X rows (tokens), B operand: rows of A (rank index); rows past
-  // M or r read as zero
+  const int64_t slice = blockIdx.x, jt = blockIdx.y, JT = gridDim.y;
   const rsrc_t rx = make_rsrc(X, (int64_t)M * K * 2);
-  const rsrc_t ra = make_rsrc(A + (int64_t)j0 * K, (int64_t)(r - j0) * K * 2);
-  const uint32_t vx = (uint32_t)((lr * K + 8 * kq) * 2);
+  const int64_t j0 = 16 * jt;
+  const rsrc_t ra = make_rsrc(A + j0 * K, ((int64_t)r - j0) * K * 2);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // lane slot kq of step st holds k = 32st + 8kq .. +7
-  const int64_t nst = K / 32;
-  for (int64_t st0 = wave; st0 < nst; st0 += (int64_t)kWaves * kDownSteps) {
-    u32x4_t xa[kDownSteps], ab[kDownSteps];
+  u32x4_t xa[2], ab[2];
 #pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) {
-      const int64_t st = st0 + (int64_t)kWaves * u;
-      const uint32_t off = st < nst ? (uint32_t)(st * 64) : 0x7fffffffu;  // past the end: zero
-      xa[u] = buf_load16(rx, vx, off);
-      ab[u] = buf_load16(ra, vx, off);
-    }
-#pragma unroll
-    for (int u = 0; u < kDownSteps; ++u) acc = mfma16<F16>(xa[u], ab[u], acc);
+  for (int u = 0; u < 2; ++u) {
+    const int64_t k = slice * kTSlice + 64 * wave + 32 * u + 8 * kq;
+    const uint32_t off = k < K ? (uint32_t)((lr * K + k) * 2) : 0x7fffffffu;
+    xa[u] = buf_load16(rx, off, 0u);
+    ab[u] = buf_load16(ra, off, 0u);
   }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) acc = mfma16<F16>(xa[u], ab[u], acc);
   s_acc[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    // lane holds D rows (tokens) 4*(lane/16)+v of column (rank index) lane%16
-    f32x4_t t = s_acc[0][lane];
+  // thread (m, j): lane 16(m/4) + j holds token m in component m%4
+  const int m = tid >> 4, j = tid & 15;
+  const int sl = 16 * (m >> 2) + j, v = m & 3;
+  float t = s_acc[0][sl][v];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      const f32x4_t a = s_acc[w][lane];
+  for (int w = 1; w < 4; ++w) t = __fadd_rn(t, s_acc[w][sl][v]);
+  P[(slice * JT + jt) * 256 + 16 * m + j] = t;
+}
+
+// The adapter term of the GEMV.  gemv_t_reduce: T[m][j] = Σ_s P[s][m][j] in
+// slice order into t_fin (stride 257 floats per token row), written to
+// T_out by workgroup 0; the thread's first (m, j) has its first 16 slices
+// already in `pre` (requested at the start of the kernel), other slices are
+// loaded 16 at a time, all independent.  gemv_lora: lora[m][c] =
+// fl32(s · Σ_j T[m][j]·B[n0 + c][j]) in fp32, the B rows staged in s_b
+// [16][r].  Both run before the main loop, while the codes stream in.
+constexpr int kPre = 16;
+__device__ __forceinline__ void gemv_t_reduce(int nthreads, int M, int r, const float* __restrict__ P, int S,
+                                              int JT, const float* pre, float* t_fin, float* __restrict__ T_out) {
+  const int tid = threadIdx.x;
+  const int64_t sstride = (int64_t)JT * 256;
+  for (int idx = tid; idx < M * r; idx += nthreads) {
+    const int m = idx / r, j = idx % r;
+    const float* p = P + (int64_t)(j >> 4) * 256 + 16 * m + (j & 15);
+    float t = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += kPre) {
+      float v[kPre];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) t[v] = __fadd_rn(t[v], a[v]);
+      for (int i = 0; i < kPre; ++i)
+        v[i] = (idx == tid && s0 == 0) ? pre[i] : (s0 + i < S ? p[(int64_t)(s0 + i) * sstride] : 0.0f);
+#pragma unroll
+      for (int i = 0; i < kPre; ++i)
+        if (s0 + i < S) t = (s0 + i == 0) ? v[i] : __fadd_rn(t, v[i]);
     }
-    const int j = j0 + (lane & 15);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = 4 * (lane >> 4) + v;
-      if (m < M && j < r) T[(int64_t)m * r + j] = t[v];
+    t_fin[m * 257 + j] = t;
+    if (T_out && blockIdx.x == 0) T_out[(int64_t)m * r + j] = t;
+  }
+}
+__device__ __forceinline__ void gemv_lora(int nthreads, int M, int r, const float* t_fin, const float* s_b,
+                                          float scale, float* s_lora) {
+  for (int idx = threadIdx.x; idx < 16 * GEMV_ROWS; idx += nthreads) {
+    const int m = idx >> 4, c = idx & 15;
+    if (m < M) {
+      float dot = 0.0f;
+      for (int j = 0; j < r; ++j) dot = __fadd_rn(dot, __fmul_rn(t_fin[m * 257 + j], s_b[c * r + j]));
+      s_lora[idx] = __fmul_rn(scale, dot);
     }
   }
 }
 
-constexpr int GEMV_ROWS = 16;
-constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
-
+// B rows [n0, n0 + 16) of the adapter, widened to fp32 into s_b [16][r]
+// (rows past N read as zero).
 template <bool F16>
+__device__ __forceinline__ void stage_b_rows(const uint16_t* __restrict__ B, int64_t N, int64_t n0, int r,
+                                             float* s_b, int nthreads) {
+  const rsrc_t rb = make_rsrc(B + n0 * r, (N - n0) * r * 2);
+  for (int idx = threadIdx.x; idx < GEMV_ROWS * r; idx += nthreads)
+    s_b[idx] = widen16<F16>(buf_load2(rb, (uint32_t)(idx * 2), 0u));
+}
+
+constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvXLdsBytes = 32 * 1024;  // X staged in LDS up to this size
+
+// 16 waves per 16 weight rows; each wave's next block group is requested
+// before the current one is dequantized.  XL: X (M x K bf16) is staged in LDS
+// once per workgroup (when it fits) and the MFMA fragments are read from
+// there; otherwise every wave loads its fragments from global memory (the
+// same few bytes requested by every wave of every workgroup at once cost
+// ~1.6 us at M = 1 on the q_proj weight, measured).
+template <bool F16, bool XL>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
-                                                            int M, const float* __restrict__ T,
+                                                            int M, const float* __restrict__ P, int S, int JT,
                                                             const uint16_t* __restrict__ B, int r,
                                                             float scale, void* __restrict__ Y,
-                                                            int y_bf16, Codebook cb) {
-  __shared__ float sq[16];
+                                                            int y_bf16, float* __restrict__ T_out, Codebook cb) {
+  extern __shared__ __attribute__((aligned(16))) char sx[];  // X [M][K] bf16 (XL)
+  __shared__ __attribute__((aligned(256))) float sq[16];  // low address byte free for 4·code
+  __shared__ float s_lora[16 * GEMV_ROWS];
   __shared__ f32x4_t s_acc[kGemvWaves][64];
+  __shared__ float t_fin[16 * 257];
+  __shared__ float s_b[16 * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t K = W.K, N = W.N;
@@ -133,78 +182,63 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     // only the M token rows load X (the other lanes' A rows are zero)
 #pragma unroll
     for (int t = 0; t < 8; ++t) g.x[t] = u32x4_t{0u, 0u, 0u, 0u};
-    if (x_row) {
+    if (!XL && x_row) {
       const uint32_t xo = ok ? (uint32_t)((lr * K + b * kBlock) * 2) : 0x7fffffffu;
 #pragma unroll
       for (int t = 0; t < 8; ++t) g.x[t] = buf_load16(rx, xo, 16u * t);
     }
   };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](const Group& g) __attribute__((always_inline)) {
+  auto consume = [&](const Group& g, int64_t grp) __attribute__((always_inline)) {
     const float cp = decode_constant(g.e, g.s, mu);
+    const int64_t b = 4 * grp + kq;
+    const bool use_x = x_row && grp < ngroups && b < nb;
+    const char* xrow = sx + (size_t)(lr * K + (use_x ? b : 0) * kBlock) * 2;
+    // level of a code: one read of the fp32 codebook at sq + 4·code, the
+    // address formed four codes at a time (byte j of we / wo is 4·code of
+    // the even / odd code of byte j of w) and put in place by a byte permute
+    const uint32_t sqb = lds_offset(sq);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t w = g.c[t >> 2][t & 3];  // codes 8t .. 8t+7
+      const uint32_t we = (w << 2) & 0x3C3C3C3Cu, wo = (w >> 2) & 0x3C3C3C3Cu;
       u32x4_t bfrag;
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        bfrag[p] = pack16<F16>(__fmul_rn(sq[(w >> (8 * p)) & 15u], cp),
-                               __fmul_rn(sq[(w >> (8 * p + 4)) & 15u], cp));
-      acc = mfma16<F16>(g.x[t], bfrag, acc);
+      for (int p = 0; p < 4; ++p) {
+        const float qe = *(const __attribute__((address_space(3))) float*)(uintptr_t)__builtin_amdgcn_perm(
+            sqb, we, 0x07060500u | (uint32_t)p);
+        const float qo = *(const __attribute__((address_space(3))) float*)(uintptr_t)__builtin_amdgcn_perm(
+            sqb, wo, 0x07060500u | (uint32_t)p);
+        bfrag[p] = pack16<F16>(__fmul_rn(qe, cp), __fmul_rn(qo, cp));
+      }
+      u32x4_t xa = g.x[t];
+      if constexpr (XL) xa = use_x ? *reinterpret_cast<const u32x4_t*>(xrow + 16 * t) : u32x4_t{0u, 0u, 0u, 0u};
+      acc = mfma16<F16>(xa, bfrag, acc);
     }
   };
 
-  // The LoRA term s·T·Bᵀ enters wave 0's accumulator as extra MFMAs over
-  // the rank in steps of 32: A operand the bf16 hi/lo split of s·T (token
-  // row lr), B operand the workgroup's B rows (weight row lr); ranks past r
-  // and tokens past M read as zero.
-  const rsrc_t rt = make_rsrc(T, (int64_t)M * r * 4);
-  const rsrc_t rb = make_rsrc(B + n0 * r, (N - n0) * r * 2);
-  struct Lora {
-    float t[8];
-    uint32_t b[8];
-  };
-  auto lora_load = [&](Lora& l, int js) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = 32 * js + 8 * kq + e;
-      l.t[e] = __uint_as_float(buf_load4(rt, (x_row && j < r) ? (uint32_t)((lr * r + j) * 4) : 0x7fffffffu, 0u));
-      l.b[e] = buf_load2(rb, j < r ? (uint32_t)((lr * r + j) * 2) : 0x7fffffffu, 0u);
-    }
-  };
-  auto lora_mfma = [&](const Lora& l) __attribute__((always_inline)) {
-    u32x4_t hi, lo, bf;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint16_t h0, l0, h1, l1;
-      split_hilo16<F16>(__fmul_rn(scale, l.t[2 * p]), h0, l0);
-      split_hilo16<F16>(__fmul_rn(scale, l.t[2 * p + 1]), h1, l1);
-      hi[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lo[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      bf[p] = (l.b[2 * p] & 0xffffu) | (l.b[2 * p + 1] << 16);
-    }
-    acc = mfma16<F16>(hi, bf, acc);
-    acc = mfma16<F16>(lo, bf, acc);
-  };
-  const int rsteps = (r + 31) / 32;
-
-  // Everything this workgroup reads from memory is requested up front: the
-  // first block group of every wave and, in wave 0, the LoRA operands, whose
-  // MFMAs wave 0 issues before its main loop (their registers are free again
-  // by then).
   Group ga, gb;
   load(ga, wave);
-  if (wave == 0) {
-    for (int js = 0; js < rsteps; js += 2) {
-      Lora la[2];
-      lora_load(la[0], js);
-      if (js + 1 < rsteps) lora_load(la[1], js + 1);
-      lora_mfma(la[0]);
-      if (js + 1 < rsteps) lora_mfma(la[1]);
-    }
+  // this thread's first T entry (token tid / r, rank tid % r): its partial
+  // tiles from the split kernel (finished before this launch) requested now
+  float pre[kPre];
+  {
+    const int tm = tid / r, tj = tid % r;
+    const bool has = tid < M * r;
+    const float* pb = P + (int64_t)(tj >> 4) * 256 + 16 * tm + (tj & 15);
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) pre[i] = (has && i < S) ? pb[(int64_t)i * JT * 256] : 0.0f;
   }
+  if constexpr (XL) {
+    const int nvec = (M * (int)K * 2) / 16;
+    for (int v = tid; v < nvec; v += kGemvThreads)
+      *reinterpret_cast<u32x4_t*>(sx + 16 * v) = buf_load16(rx, (uint32_t)(16 * v), 0u);
+  }
+  stage_b_rows<F16>(B, N, n0, r, s_b, kGemvThreads);
   if (tid < 16) sq[tid] = cb.q[tid];
-  __syncthreads();  // codebook
+  gemv_t_reduce(kGemvThreads, M, r, P, S, JT, pre, t_fin, T_out);
+  __syncthreads();  // codebook, B rows, X, T
+  gemv_lora(kGemvThreads, M, r, t_fin, s_b, scale, s_lora);
 
   // two groups per iteration, alternating buffers: the loads of the next
   // group are issued (and kept above the barrier to the scheduler) before
@@ -212,24 +246,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
   for (int64_t grp = wave; grp < ngroups; grp += 2 * kGemvWaves) {
     load(gb, grp + kGemvWaves);
     __builtin_amdgcn_sched_barrier(0);
-    consume(ga);
+    consume(ga, grp);
     if (grp + kGemvWaves >= ngroups) break;
     load(ga, grp + 2 * kGemvWaves);
     __builtin_amdgcn_sched_barrier(0);
-    consume(gb);
+    consume(gb, grp + kGemvWaves);
   }
   s_acc[wave][lane] = acc;
   __syncthreads();
-  // one thread per output (token m, weight row n0 + c): the 16 partial tiles
-  // in a fixed order
+  // one thread per output (token m, weight row n0 + c): the 16 partial
+  // tiles in a fixed order, then the adapter term
   if (tid < 16 * GEMV_ROWS) {
     const int m = tid >> 4, c = tid & 15;
     const int64_t nn = n0 + c;
     if (m < M && nn < N) {
-      // partial tile of wave w: lane 16(m/4) + c holds token m in component m%4
       float y = s_acc[0][16 * (m >> 2) + c][m & 3];
 #pragma unroll
       for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
+      y = __fadd_rn(y, s_lora[tid]);
       if (y_bf16)
         static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack16<F16>(y, 0.0f) & 0xffffu);
       else
@@ -240,19 +274,32 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
 
 }  // namespace
 
-hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                       const uint16_t* B, int32_t r, float scale, void* Y, bool y16, float* T,
-                       bool f16, hipStream_t st) {
-  const unsigned gd = (unsigned)((r + 15) / 16);
+size_t gemv_partial_bytes(int64_t K, int32_t r) {
+  return (size_t)((K + kTSlice - 1) / kTSlice) * (size_t)((r + 15) / 16) * 256 * 4;
+}
+
+hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                       int32_t r, float scale, void* Y, bool y16, float* T, float* P, bool f16, hipStream_t st) {
+  const int S = (int)((W.K + kTSlice - 1) / kTSlice), JT = (r + 15) / 16;
+  const dim3 tg((unsigned)S, (unsigned)JT);
   if (f16)
-    lora_down_small_kernel<true><<<gd, kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
+    lora_down_split_kernel<true><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);
   else
-    lora_down_small_kernel<false><<<gd, kThreads, 0, st>>>(X, (int)M, W.K, A, r, T);
+    lora_down_split_kernel<false><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((W.N + GEMV_ROWS - 1) / GEMV_ROWS);
-  return f16 ? timed_launch(kKernGemv, gemv_kernel<true>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
-                            (const float*)T, B, r, scale, Y, y16 ? 1 : 0, codebook())
-             : timed_launch(kKernGemv, gemv_kernel<false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
-                            (const float*)T, B, r, scale, Y, y16 ? 1 : 0, codebook());
+  const int yb = y16 ? 1 : 0;
+  const size_t xb = (size_t)M * W.K * 2;
+  if (xb <= (size_t)kGemvXLdsBytes)
+    return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, true>, dim3(grid), dim3(kGemvThreads), xb, st, W, X,
+                                  (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
+               : timed_launch_shm(kKernGemv, gemv_kernel<false, true>, dim3(grid), dim3(kGemvThreads), xb, st, W, X,
+                                  (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook());
+  return f16 ? timed_launch(kKernGemv, gemv_kernel<true, false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
+                            (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
+             : timed_launch(kKernGemv, gemv_kernel<false, false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
+                            (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook());
 }
 
 }  // namespace qnf4

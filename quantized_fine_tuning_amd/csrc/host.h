@@ -26,15 +26,19 @@ TimingHook& timing_hook();
 // the runtime records around the dispatch itself (tighter than recording the
 // events on the stream before and after), and the request is cleared.
 template <typename F, typename... Args>
-hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+hipError_t timed_launch_shm(int kernel_id, F k, dim3 grid, dim3 block, size_t shm, hipStream_t st, Args... args) {
   TimingHook& h = timing_hook();
   if (h.kernel == kernel_id) {
     h.kernel = 0;
-    hipExtLaunchKernelGGL(k, grid, block, 0, st, h.start, h.stop, 0, args...);
+    hipExtLaunchKernelGGL(k, grid, block, shm, st, h.start, h.stop, 0, args...);
   } else {
-    hipLaunchKernelGGL(k, grid, block, 0, st, args...);
+    hipLaunchKernelGGL(k, grid, block, shm, st, args...);
   }
   return hipGetLastError();
+}
+template <typename F, typename... Args>
+hipError_t timed_launch(int kernel_id, F k, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  return timed_launch_shm(kernel_id, k, grid, block, 0, st, args...);
 }
 enum { kKernFwdGemm = 1, kKernDxGemm = 2, kKernGemv = 3, kKernQuantize = 4, kKernAdamw = 5, kKernMerge = 6, kKernFormatGemv = 7 };
 
@@ -109,6 +113,9 @@ hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, flo
                            uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
                            int64_t K, uint16_t* AT2, bool f16, hipStream_t st);
 hipError_t launch_zero(float* a, int64_t n, hipStream_t st);
+
+// Dequant-GEMV (M <= 16): bytes of the partial tiles of T = X·Aᵀ.
+size_t gemv_partial_bytes(int64_t K, int32_t r);
 
 // Forward ------------------------------------------------------------------
 struct FwdLayout {

@@ -16,9 +16,8 @@ hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const
                           const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B2, int64_t Rp, void* Y, bool y16, bool f16, hipStream_t st);
-hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A,
-                       const uint16_t* B, int32_t r, float scale, void* Y, bool y16, float* T,
-                       bool f16, hipStream_t st);
+hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                       int32_t r, float scale, void* Y, bool y16, float* T, float* P, bool f16, hipStream_t st);
 
 FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdLayout L{};
@@ -34,6 +33,8 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M > 16) {
     L.pT = rowred_plan(M, K, Rp);
     off += round_up(rowred_partial_bytes(L.pT), 256);
+  } else if (M > 0) {
+    off += round_up(gemv_partial_bytes(K, r), 256);  // partial tiles of T
   }
   L.total = off;
   return L;
@@ -97,12 +98,14 @@ size_t colred_bytes_bound(int64_t M, int64_t Pn, int64_t Rp) {
 }  // namespace
 
 size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
+  // M <= 16 (the GEMV path) grows with M; M > 16 is the GEMM path
+  const size_t small = fwd_layout(std::min<int64_t>(M_max, 16), N, K, r).total;
+  if (M_max <= 16) return small;
   const FwdLayout L = fwd_layout(M_max, N, K, r);
-  if (M_max <= 16) return L.total;
   const int64_t Rp = lora_rp(r);
   size_t p = 0;
   for (int64_t M = 64; M < M_max + 64; M += 64) p = std::max(p, rowred_bytes_bound(std::min(M, M_max), K, Rp));
-  return L.off_P + p;
+  return std::max(small, L.off_P + p);
 }
 
 size_t bwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
@@ -122,10 +125,8 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
                           const uint16_t* B, int32_t r, float scale, void* Y, bool y16,
                           float* T, char* ws, const FwdLayout& L, bool f16, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  if (M <= 16) {
-    float* Tw = T ? T : reinterpret_cast<float*>(ws + L.off_T);
-    return launch_gemv(W, X, M, A, B, r, scale, Y, y16, Tw, f16, st);
-  }
+  if (M <= 16)
+    return launch_gemv(W, X, M, A, B, r, scale, Y, y16, T, reinterpret_cast<float*>(ws + L.off_P), f16, st);
   const int64_t Rp = lora_rp(r);
   uint16_t* sT = reinterpret_cast<uint16_t*>(ws + L.off_sT);
   float* P = reinterpret_cast<float*>(ws + L.off_P);

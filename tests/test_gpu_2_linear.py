@@ -107,7 +107,7 @@ def test_identity_input_gives_weight_bit_exact():
 
 def test_qproj_gemv_m1_m16():
     w = Inputs(2)
-    for M in (1, 16):
+    for M in (1, 3, 4, 5, 16):  # the 4-wave kernel takes M <= 4, the 16-wave one the rest
         print(f"q_proj 4096x4096 M={M} r=16", flush=True)
         L = Layer.from_workload(2, 0, M)
         run_fwd(L, w.w.rank, w.w.alpha)
@@ -119,6 +119,9 @@ def test_qproj_gemv_m1_m16():
     (5, 136, 320, 3),      # GEMV with ragged N
     (300, 520, 640, 256),  # maximum rank
     (64, 64, 64, 1),
+    (3, 136, 320, 3),      # small-M GEMV, 5 blocks per row (a ragged block group)
+    (1, 200, 192, 5),
+    (4, 24, 64, 1),
 ])
 def test_ragged_shapes(M, N, K, r):
     print(f"ragged M={M} N={N} K={K} r={r}", flush=True)
