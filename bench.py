@@ -3,53 +3,58 @@
 
 One step = the whole path over one batch of the Llama-7B-shaped MLP workload
 (gate and up 4096->11008, down 11008->4096; M = 4096 tokens = batch 4 x seq
-1024; LoRA rank 64, alpha 16; weights fp32 N(0, 0.02^2)): for each of the three
-linears, NF4 quantization with double quantization of the fp32 weight, the
-fused dequant-GEMM forward (saving T) and the backward (dX, dA, dB).  Inputs are
-seeded synthetic data resident in HBM before the timed region.
+1024; LoRA rank 64, alpha 16; weights fp32 N(0, 0.02^2), NF4 + double
+quantization): for each of the three linears, the fused dequant-GEMM forward
+(saving T) and the backward (dX, dA, dB).  The frozen weights are quantized
+once, before the timed region (a training step does not re-quantize them);
+the step with the three quantizations included is reported beside it.
+Inputs are seeded synthetic data resident in HBM before the timed region.
 
-value = fwd+bwd algorithmic FLOP per step / step time (quantization time is in
-the denominator).  Algorithmic FLOP per linear: 4*M*N*K + 6*M*r*(K+N).
+value = fwd+bwd algorithmic FLOP per step / step time.  Algorithmic FLOP per
+linear: 4*M*N*K + 6*M*r*(K+N).
 
 Extra objects on the JSON line:
-  roofline      the dominant kernel (by total time) measured live with HIP
-                events recorded around its launches inside the timed steps;
-  gemv          the dequant-GEMV forward of the 4096x4096 q_proj at M = 1 and
-                M = 16, cycling through 64 quantized copies (about 0.55 GB, more
-                than twice the 256 MB last-level cache) so every launch streams
-                from HBM; also the whole forward (LoRA-down + GEMV kernels) per
-                call when the 64 forwards are captured in one graph and
-                replayed;
-  adamw         the AdamW step on bf16 LoRA parameters with fp32 moments (one
-                launch per step): the six LoRA matrices of the 7B MLP at r = 64,
-                and 8 tensors of 16 M parameters; kernel time and GB/s against
-                24 bytes per parameter;
-  merge         the LoRA adapter merged into the dequantized weight (bf16
-                out) for the three 7B MLP weights at r = 64: kernel time and
-                GB/s; and on the gate weight, the error of re-quantizing the
-                merged weight, relative to it and to the adapter's change;
-  formats       the comparison formats (NF4 without double quantization,
-                absmax INT4 and INT8) on the q_proj weight: reconstruction
-                error against the fp32 weight, and dequant-GEMV time and GB/s
-                at M = 1 and 16;
-  f16_step      the same MLP step in the fp16 compute format (5 timed steps):
-                ms per step, TFLOP/s and the two GEMMs' average times;
-  measured_peaks  in-run reference points beside the spec peaks: a 1 GiB
-                device copy (GB/s) and torch's bf16 matmul on the 4096 x 11008
-                x 4096 product (TFLOP/s); roofline.frac_of_measured_matmul is
-                the dominant GEMM against the latter;
-  cpu_baseline  the oracle (numpy, fp64) on a bounded sample: one whole step
-                of the same workload (quantize + dequantize + forward +
-                backward of the three linears at M = 4096).
+  roofline       the dominant kernel (by time per step), measured live with
+                 HIP events attached to its launches in the last timed step;
+                 frac against the 2.5 PFLOP/s dense bf16 spec, and beside it
+                 against the in-run MFMA loop (measured_peaks);
+  measured_peaks a register-only v_mfma_f32_16x16x32_bf16 loop on every SIMD
+                 (the MFMA rate the chip sustains) and a streaming copy of
+                 1 GiB (the HBM rate of a plain read + write), both from the
+                 library; torch's bf16 matmul on the 7B MLP shape as context;
+  workloads      the same fwd+bwd step on the 7B decoder block (seven
+                 linears, M = 8192) and the 65B layer (seven linears, M =
+                 2048), each with its dominant kernel's roofline;
+  m_sweep        the gate linear (11008x4096, r = 64) at M = 1, 16, 17, 64,
+                 128, 512 (one 8-way data-parallel shard of the 4096-token
+                 batch) and 4096: forward and forward+backward time;
+  gemv           the q_proj forward (4096x4096, r = 16) at M = 1 and 16: the
+                 whole forward (T partials + dequant-GEMV) per call when 64
+                 forwards over 64 quantized copies (~0.55 GB, more than twice
+                 the 256 MB last-level cache) are captured in one graph and
+                 replayed, against the forward's algorithmic bytes (codes,
+                 constants, X, A, B, Y); the GEMV kernel's own event-timed
+                 median beside it;
+  bulk_quantize  NF4 + double quantization throughput over streamed bf16
+                 weights (the 7B-block and 65B-layer tensor lists: 6.7B and
+                 65B parameters); only the quantize kernels are timed;
+  adamw, merge, formats, f16_step   the next rows (AdamW step, LoRA merge,
+                 comparison formats, fp16 compute);
+  cpu_baseline   the oracle (numpy, fp64) on a bounded sample: one whole step
+                 of the 7B MLP workload; breadth: quantize params/s on
+                 several shapes and fp64 fwd+bwd of one linear of each
+                 workload.
 
 roofline.traffic is the HBM traffic (bytes per launch) of the dominant kernel
 as rocprofv3's FETCH_SIZE and WRITE_SIZE counters read it, scaled by what the
-same counters read for a plain copy of known size (--copy-calibration).  It
-is taken from the summary under profiles/ and reported only while the
-kernel's sources are byte-identical to the ones profiled; otherwise null.
+same counters read for the library's streaming copy of known size
+(--copy-calibration).  It is taken from the summary under profiles/ and
+reported only while the kernel's sources are byte-identical to the ones
+profiled; otherwise null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-gemv] [--no-adamw] [--no-merge] [--no-formats] [--no-f16]
+                       [--no-workloads] [--no-sweep] [--no-bulk] [--bulk-sample]
 """
 
 import argparse
@@ -125,12 +130,13 @@ def linear_flops(M, N, K, r):
     return 4 * M * N * K + 6 * M * r * (K + N)
 
 
-def gemv_kernel_bytes(M, N, K, r):
-    """Bytes the GEMV kernel must move: packed codes, e4m3 constants, group
-    scales, mean, X, B, T (fp32) in; Y (bf16) out."""
+def gemv_forward_bytes(M, N, K, r):
+    """Bytes the whole M <= 16 forward must move (the algorithmic count):
+    packed codes, e4m3 constants, group scales, mean, X, A and B in; Y (bf16)
+    out.  8,933,380 bytes for the q_proj weight at M = 1, r = 16."""
     nb = N * K // 64
     ng = (nb + 255) // 256
-    return N * K // 2 + nb + 4 * ng + 4 + 2 * M * K + 2 * N * r + 4 * M * r + 2 * M * N
+    return N * K // 2 + nb + 4 * ng + 4 + 2 * M * K + 2 * r * (K + N) + 2 * M * N
 
 
 def dev_bf16(torch, bits):
@@ -150,38 +156,58 @@ def timed_events(torch, n):
     return evs
 
 
-def run_mlp(torch, q, args, f16=False, steps=None, warmup=None):
-    """The timed MLP step.  f16: the same step in the fp16 compute format
-    (the workloads' bf16 inputs converted to fp16 on the device)."""
-    from workloads import Inputs
+def make_layers(torch, q, widx, M, f16=False, device_inputs=False):
+    """Inputs of one workload on the device, weights quantized once."""
+    from workloads import Inputs, device_normal
 
-    steps = args.steps if steps is None else steps
-    warmup = args.warmup if warmup is None else warmup
     cvt = (lambda x: x.to(torch.float16)) if f16 else (lambda x: x)  # noqa: E731
-
-    w = Inputs(3)
-    M, r, alpha = w.w.tokens[0], w.w.rank, w.w.alpha
+    w = Inputs(widx)
+    r = w.w.rank
     layers = []
     for li, (name, N, K) in enumerate(w.w.layers):
         t0 = time.time()
         L = {"name": name, "N": N, "K": K}
-        L["W"] = torch.from_numpy(w.weight(li)).cuda()
-        L["X"] = cvt(dev_bf16(torch, w.X(li, M)))
-        L["dY"] = cvt(dev_bf16(torch, w.dY(li, M)))
-        L["A"] = cvt(dev_bf16(torch, w.lora_A(li)))
-        L["B"] = cvt(dev_bf16(torch, w.lora_B(li)))
+        seed = 1000 * widx + 10 * li
+        if device_inputs:
+            Wd = device_normal(torch, (N, K), seed, 0.02)
+            L["X"] = cvt(device_normal(torch, (M, K), seed + 1))
+            L["dY"] = cvt(device_normal(torch, (M, N), seed + 2))
+            L["A"] = cvt(device_normal(torch, (r, K), seed + 3, 0.02))
+            L["B"] = cvt(device_normal(torch, (N, r), seed + 4, 0.01))
+        else:
+            Wd = torch.from_numpy(w.weight(li)).cuda()
+            L["X"] = cvt(dev_bf16(torch, w.X(li, M)))
+            L["dY"] = cvt(dev_bf16(torch, w.dY(li, M)))
+            L["A"] = cvt(dev_bf16(torch, w.lora_A(li)))
+            L["B"] = cvt(dev_bf16(torch, w.lora_B(li)))
         sz = q.qlora_nf4_sizes(N, K, M, r)
+        L["W"] = Wd
         L["qt"] = q.Nf4Tensor.empty(N, K)
         L["wsq"] = q.workspace(sz["quantize_ws_bytes"])
+        q.qlora_nf4_quantize(Wd, L["qt"], L["wsq"])
         L["wsf"] = q.workspace(sz["fwd_ws_bytes"])
         L["wsb"] = q.workspace(sz["bwd_ws_bytes"])
-        L["Y"] = torch.empty(M, N, dtype=torch.float16 if f16 else torch.bfloat16, device="cuda")
+        dt16 = torch.float16 if f16 else torch.bfloat16
+        L["Y"] = torch.empty(M, N, dtype=dt16, device="cuda")
         L["T"] = torch.empty(M, r, dtype=torch.float32, device="cuda")
-        L["dX"] = torch.empty(M, K, dtype=torch.float16 if f16 else torch.bfloat16, device="cuda")
+        L["dX"] = torch.empty(M, K, dtype=dt16, device="cuda")
         L["dA"] = torch.empty(r, K, dtype=torch.float32, device="cuda")
         L["dB"] = torch.empty(N, r, dtype=torch.float32, device="cuda")
         layers.append(L)
-        log(f"[bench] inputs of {name} {N}x{K} ready ({time.time() - t0:.1f}s)")
+        log(f"[bench] inputs of workload {widx} {name} {N}x{K} M={M} ready ({time.time() - t0:.1f}s)")
+    return w, layers
+
+
+def run_step(torch, q, args, widx=3, M=None, f16=False, steps=None, warmup=None, device_inputs=False,
+             with_quantize=True):
+    """The timed fwd+bwd step of one workload; then the same step with the
+    quantization of every weight included."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    from workloads import Inputs
+    M = Inputs(widx).w.tokens[0] if M is None else M
+    w, layers = make_layers(torch, q, widx, M, f16, device_inputs)
+    r, alpha = w.w.rank, w.w.alpha
 
     kinds = ("quantize", "fwd_gemm", "dx_gemm")
     kid = {"quantize": q.QLORA_KERNEL_QUANTIZE, "fwd_gemm": q.QLORA_KERNEL_FWD_GEMM,
@@ -190,12 +216,13 @@ def run_mlp(torch, q, args, f16=False, steps=None, warmup=None):
     # around it, so only the launches of the last timed step carry events.
     events = {k: timed_events(torch, len(layers)) for k in kinds}
 
-    def step(i=None):
+    def step(i=None, quantize=False, last=None):
         for li, L in enumerate(layers):
-            j = li if i == steps - 1 else None
-            if j is not None:
-                q.qlora_time_next_launch(kid["quantize"], *events["quantize"][j])
-            q.qlora_nf4_quantize(L["W"], L["qt"], L["wsq"])
+            j = li if i == last else None
+            if quantize:
+                if j is not None:
+                    q.qlora_time_next_launch(kid["quantize"], *events["quantize"][j])
+                q.qlora_nf4_quantize(L["W"], L["qt"], L["wsq"])
             if j is not None:
                 q.qlora_time_next_launch(kid["fwd_gemm"], *events["fwd_gemm"][j])
             q.qlora_linear_fwd(L["qt"], L["X"], L["A"], L["B"], r, alpha, L["Y"], L["T"], L["wsf"])
@@ -204,46 +231,130 @@ def run_mlp(torch, q, args, f16=False, steps=None, warmup=None):
             q.qlora_linear_bwd(L["qt"], L["X"], L["dY"], L["A"], L["B"], r, alpha, L["T"],
                                L["dX"], L["dA"], L["dB"], L["wsb"])
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] {warmup} warmup steps done")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / steps
-    log(f"[bench] {steps} timed steps: {ms_per_step:.3f} ms/step")
+    def timed(quantize, n, nw):
+        for _ in range(nw):
+            step(quantize=quantize)
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record()
+        for i in range(n):
+            step(i, quantize, last=n - 1)
+        t_end.record()
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / n
 
-    flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
+    ms_per_step = timed(False, steps, warmup)
+    log(f"[bench] workload {widx}: {steps} timed fwd+bwd steps: {ms_per_step:.3f} ms/step")
     per_kernel = {}
-    for k in kinds:
+    for k in ("fwd_gemm", "dx_gemm"):
         durs = [a.elapsed_time(b) for a, b in events[k]]
         per_kernel[k] = {"avg_ms": statistics.mean(durs), "total_ms_per_step": sum(durs),
                          "launches_per_step": len(layers)}
+    ms_q = None
+    if with_quantize:
+        ms_q = timed(True, max(2, steps // 4), 1)
+        durs = [a.elapsed_time(b) for a, b in events["quantize"]]
+        per_kernel["quantize"] = {"avg_ms": statistics.mean(durs), "total_ms_per_step": sum(durs),
+                                  "launches_per_step": len(layers)}
+        q_bytes = statistics.mean(L["N"] * L["K"] * ((4 if L["W"].dtype == torch.float32 else 2) + 0.5 + 1 / 64)
+                                  + 4 * (L["N"] * L["K"] // 16384) + 4 for L in layers)
+        per_kernel["quantize"]["gbs"] = q_bytes / (per_kernel["quantize"]["avg_ms"] * 1e-3) / 1e9
+        log(f"[bench] workload {widx}: step with the quantization of every weight: {ms_q:.3f} ms")
+
+    flops = sum(linear_flops(M, L["N"], L["K"], r) for L in layers)
     # algorithmic work per launch, averaged over the step's launches of each kernel
     fwd_flop = statistics.mean(2 * M * L["N"] * L["K"] + 2 * M * L["N"] * r for L in layers)
     dx_flop = statistics.mean(2 * M * L["N"] * L["K"] + 2 * M * L["K"] * r for L in layers)
-    q_bytes = statistics.mean(L["N"] * L["K"] * (4 + 0.5 + 1 / 64) + 4 * (L["N"] * L["K"] // 16384) + 4
-                              for L in layers)
     per_kernel["fwd_gemm"]["tflops"] = fwd_flop / (per_kernel["fwd_gemm"]["avg_ms"] * 1e-3) / 1e12
     per_kernel["dx_gemm"]["tflops"] = dx_flop / (per_kernel["dx_gemm"]["avg_ms"] * 1e-3) / 1e12
-    per_kernel["quantize"]["gbs"] = q_bytes / (per_kernel["quantize"]["avg_ms"] * 1e-3) / 1e9
     dom = max(("fwd_gemm", "dx_gemm"), key=lambda k: per_kernel[k]["total_ms_per_step"])
     ach = per_kernel[dom]["tflops"]
     kname = {"fwd_gemm": "fwd_gemm_kernel", "dx_gemm": "dx_gemm_kernel"}[dom]
     roofline = {"bound": "mfma", "kernel": kname,
                 "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(kname),
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": profiled_traffic(kname) if widx == 3 and not f16 else None,
                 "avg_launch_ms": round(per_kernel[dom]["avg_ms"], 4),
                 "flop_per_launch": int(fwd_flop if dom == "fwd_gemm" else dx_flop)}
-    return {"ms_per_step": ms_per_step, "flops": flops, "M": M, "r": r, "alpha": alpha,
-            "layers": [[L["name"], L["N"], L["K"]] for L in layers], "per_kernel": per_kernel,
+    del layers
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms_per_step, "ms_per_step_with_quantize": ms_q, "flops": flops, "M": M, "r": r,
+            "alpha": alpha, "layers": [list(x) for x in w.w.layers], "per_kernel": per_kernel,
             "roofline": roofline}
+
+
+def run_workloads(torch, q, args, peaks):
+    """fwd+bwd of the 7B decoder block (M = 8192) and the 65B layer (M = 2048)."""
+    out = {}
+    for widx, name in ((4, "llama-7b decoder block, 7 linears"), (5, "65b-shaped layer, 7 linears")):
+        res = run_step(torch, q, args, widx, steps=max(3, args.steps // 2), warmup=2, device_inputs=True,
+                       with_quantize=False)
+        tf = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
+        rl = res["roofline"]
+        rl["frac_of_measured_mfma"] = round(rl["achieved"] / peaks["mfma_loop_TFLOP/s"], 4)
+        out[f"workload{widx}"] = {"workload": name, "tokens": res["M"], "lora_rank": res["r"],
+                                  "flop_per_step": res["flops"], "ms_per_step": round(res["ms_per_step"], 4),
+                                  "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "roofline": rl,
+                                  "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                                                  for kk, vv in v.items()} for k, v in res["per_kernel"].items()}}
+        log(f"[bench] workload {widx}: {tf:.1f} TFLOP/s fwd+bwd")
+    return out
+
+
+def run_m_sweep(torch, q, args):
+    """The gate linear (11008x4096, r = 64) at several token counts."""
+    from workloads import device_normal
+
+    N, K, r, alpha = 11008, 4096, 64, 16.0
+    Wd = device_normal(torch, (N, K), 77, 0.02, bf16=False)
+    qt = q.Nf4Tensor.empty(N, K)
+    q.qlora_nf4_quantize(Wd, qt, q.workspace(q.qlora_nf4_sizes(N, K, 0, r)["quantize_ws_bytes"]))
+    del Wd
+    A = device_normal(torch, (r, K), 78, 0.02)
+    B = device_normal(torch, (N, r), 79, 0.01)
+    out = {}
+    for M in (1, 16, 17, 64, 128, 512, 4096):
+        X = device_normal(torch, (M, K), 80 + M)
+        dY = device_normal(torch, (M, N), 81 + M)
+        sz = q.qlora_nf4_sizes(N, K, M, r)
+        wsf, wsb = q.workspace(sz["fwd_ws_bytes"]), q.workspace(sz["bwd_ws_bytes"])
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        T = torch.empty(M, r, dtype=torch.float32, device="cuda")
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        dA = torch.empty(r, K, dtype=torch.float32, device="cuda")
+        dB = torch.empty(N, r, dtype=torch.float32, device="cuda")
+
+        def fwd():
+            q.qlora_linear_fwd(qt, X, A, B, r, alpha, Y, T, wsf)
+
+        def bwd():
+            q.qlora_linear_bwd(qt, X, dY, A, B, r, alpha, T, dX, dA, dB, wsb)
+
+        n = 20
+        for _ in range(3):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(n):
+            fwd()
+        e[1].record()
+        for _ in range(n):
+            fwd()
+            bwd()
+        e[2].record()
+        torch.cuda.synchronize()
+        f_ms = e[0].elapsed_time(e[1]) / n
+        fb_ms = e[1].elapsed_time(e[2]) / n
+        fl = linear_flops(M, N, K, r)
+        out[f"M{M}"] = {"fwd_ms": round(f_ms, 4), "fwd_bwd_ms": round(fb_ms, 4),
+                        "fwd_bwd_TFLOP/s": round(fl / (fb_ms * 1e-3) / 1e12, 2),
+                        "path": "dequant-GEMV" if M <= 16 else "dequant-in-tile GEMM"}
+        log(f"[bench] gate M={M}: fwd {f_ms * 1e3:.1f} us, fwd+bwd {fb_ms * 1e3:.1f} us")
+    return out
 
 
 def run_gemv(torch, q, args):
@@ -284,14 +395,12 @@ def run_gemv(torch, q, args):
         torch.cuda.synchronize()
         durs = sorted(a.elapsed_time(b) for a, b in evs)
         med = statistics.median(durs)
-        nbytes = gemv_kernel_bytes(M, N, K, r)
-        gbs = nbytes / (med * 1e-3) / 1e9
-        out[f"M{M}"] = {"kernel_us_median": round(med * 1e3, 3),
-                        "kernel_us_p10": round(durs[n // 10] * 1e3, 3),
-                        "kernel_us_p90": round(durs[(9 * n) // 10] * 1e3, 3),
-                        "call_us_mean": round(c0.elapsed_time(c1) / n * 1e3, 3),
-                        "bytes": nbytes, "GB/s": round(gbs, 1),
-                        "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        nbytes = gemv_forward_bytes(M, N, K, r)
+        out[f"M{M}"] = {"gemv_kernel_us_median": round(med * 1e3, 3),
+                        "gemv_kernel_us_p10": round(durs[n // 10] * 1e3, 3),
+                        "gemv_kernel_us_p90": round(durs[(9 * n) // 10] * 1e3, 3),
+                        "eager_call_us_mean": round(c0.elapsed_time(c1) / n * 1e3, 3),
+                        "forward_bytes": nbytes}
         # the same forwards captured in one graph (one per quantized copy) and
         # replayed: the launch-bound decode loop without per-call host work
         s = torch.cuda.Stream()
@@ -316,11 +425,13 @@ def run_gemv(torch, q, args):
         g1.record()
         torch.cuda.synchronize()
         per = g0.elapsed_time(g1) / (reps * len(copies)) * 1e3
-        out[f"M{M}"]["graph_us_per_forward"] = round(per, 3)
-        out[f"M{M}"]["graph_GB/s"] = round(nbytes / (per * 1e-6) / 1e9, 1)
+        gbs = nbytes / (per * 1e-6) / 1e9
+        out[f"M{M}"]["forward_us"] = round(per, 3)
+        out[f"M{M}"]["GB/s"] = round(gbs, 1)
+        out[f"M{M}"]["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
         del g
-        log(f"[bench] GEMV M={M}: {med * 1e3:.2f} us median, {gbs:.0f} GB/s; "
-            f"graph-replayed forward {per:.2f} us")
+        log(f"[bench] GEMV M={M}: whole forward (graph-replayed) {per:.2f} us, {gbs:.0f} GB/s; "
+            f"GEMV kernel {med * 1e3:.2f} us median (events)")
     return out
 
 
@@ -487,6 +598,43 @@ def run_formats(torch, q, args):
     return out
 
 
+def run_cpu_breadth():
+    """Oracle timings beyond the main step (numpy quantize runs on one core):
+    quantize params/s on the tiny and q_proj shapes and on a 1024-row slice of
+    a 65B-layer 8192-wide weight; fp64 forward + backward of one linear of the
+    tiny workload (M = 32) and of the 7B-block and 65B-layer q_proj shapes at
+    M = 512, whose weight is the unquantized draw (only the rate is kept)."""
+    import numpy as np
+    from oracle import linalg, nf4
+    from workloads import Inputs, bf16_bits_to_f32
+
+    out = {"quantize_params_per_s": {}, "fwd_bwd_TFLOP/s": {}}
+    rng = np.random.default_rng(3)
+    for label, (N, K) in (("tiny 256x256", (256, 256)), ("q_proj 4096x4096", (4096, 4096)),
+                          ("65B q_proj rows 1024x8192", (1024, 8192))):
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        t0 = time.perf_counter()
+        nf4.quantize(W)
+        dt = time.perf_counter() - t0
+        out["quantize_params_per_s"][label] = round(N * K / dt, 1)
+    f64 = linalg.bf16_to_f64
+    for widx, M in ((1, 32), (4, 512), (5, 512)):
+        w = Inputs(widx)
+        name, N, K = w.w.layers[0]
+        r, alpha = w.w.rank, w.w.alpha
+        Wb = w.weight(0)
+        wh = (Wb if w.w.weight_dtype == "f32" else bf16_bits_to_f32(Wb)).astype(np.float64)
+        X, dY = f64(w.X(0, M)), f64(w.dY(0, M))
+        A, B = f64(w.lora_A(0)), f64(w.lora_B(0))
+        t0 = time.perf_counter()
+        linalg.linear_fwd(X, wh, A, B, alpha, r)
+        linalg.linear_bwd(X, dY, wh, A, B, alpha, r)
+        dt = time.perf_counter() - t0
+        out["fwd_bwd_TFLOP/s"][f"workload {widx} {name} {N}x{K} M={M}"] = round(linear_flops(M, N, K, r) / dt / 1e12, 6)
+        log(f"[bench] cpu oracle breadth: workload {widx} {name} ({dt:.1f}s)")
+    return out
+
+
 def run_cpu_baseline():
     """The oracle as it stands, timed on the host over one whole step of the
     same workload: for each of the three linears, quantize + dequantize + fp64
@@ -529,23 +677,25 @@ def run_cpu_baseline():
                       "not timed"}
 
 
-def copy_calibration(torch, mib):
-    """A plain device copy of known size, three times, for scaling the HBM
-    byte counters of a profiled run (the copy reads and writes `mib` MiB)."""
+def copy_calibration(torch, q, mib):
+    """The library's streaming copy of known size, three times, for scaling
+    the HBM byte counters of a profiled run (each reads and writes `mib`
+    MiB)."""
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        q.qlora_bench_copy(src, dst)
     torch.cuda.synchronize()
     log(f"[bench] copy calibration: 3 copies of {mib} MiB")
     del src, dst
 
 
-def measured_peaks(torch):
-    """In-run reference points beside the spec peaks: a streaming device copy
-    of 1 GiB (read + write bytes / time) and torch's bf16 matmul (hipBLASLt)
-    on the 7B MLP's largest product shape, each the median of 10 runs."""
+def measured_peaks(torch, q):
+    """In-run reference points beside the spec peaks: the library's
+    register-only MFMA loop on every SIMD and its streaming copy of 1 GiB;
+    torch's bf16 matmul (hipBLASLt) on the 7B MLP's largest product as
+    context."""
     def med_ms(fn, n=10):
         for _ in range(3):
             fn()
@@ -557,20 +707,73 @@ def measured_peaks(torch):
         torch.cuda.synchronize()
         return statistics.median(a.elapsed_time(b) for a, b in evs)
 
+    sink = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    flop = {}
+
+    def mfma():
+        flop["n"] = q.qlora_bench_mfma_peak(20000, sink)
+
+    mfma_ms = med_ms(mfma)
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    copy_ms = med_ms(lambda: dst.copy_(src))
+    copy_ms = med_ms(lambda: q.qlora_bench_copy(src, dst))
     del src, dst
     M, N, K = 4096, 11008, 4096
     a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
     b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
     mm_ms = med_ms(lambda: torch.matmul(a, b))
     del a, b
-    out = {"copy_GB/s": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
-           "bf16_matmul_TFLOP/s": round(2 * M * N * K / (mm_ms * 1e-3) / 1e12, 1),
-           "bf16_matmul_shape": [M, N, K]}
+    out = {"mfma_loop_TFLOP/s": round(flop["n"] / (mfma_ms * 1e-3) / 1e12, 1),
+           "copy_GB/s": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+           "context_torch_bf16_matmul_TFLOP/s": round(2 * M * N * K / (mm_ms * 1e-3) / 1e12, 1),
+           "context_torch_bf16_matmul_shape": [M, N, K]}
     log(f"[bench] measured peaks: {out}")
+    return out
+
+
+def run_bulk(torch, q, args):
+    """NF4 + double quantization of streamed bf16 weights: each tensor of the
+    list is drawn on the GPU (not timed), then quantized (timed with events
+    attached to the quantize kernel).  The whole 6.7B and 65B lists; with
+    --bulk-sample only the first block / layer of each plus the two padding
+    matrices."""
+    from workloads import bulk_tensors, device_normal
+
+    out = {}
+    for widx, label in ((4, "6.7B (7B block list)"), (5, "65B (65B layer list)")):
+        tl = bulk_tensors(widx)
+        if args.bulk_sample:
+            tl = tl[:7] + tl[-2:]
+        total_params, total_ms, nbytes = 0, 0.0, 0
+        outs = {}
+        for i, (name, N, K) in enumerate(tl):
+            Wd = device_normal(torch, (N, K), 5000 + 7 * widx + (i % 9), 0.02)
+            if (N, K) not in outs:
+                outs[(N, K)] = (q.Nf4Tensor.empty(N, K), q.workspace(q.qlora_nf4_sizes(N, K, 0, 1)["quantize_ws_bytes"]))
+            qt, ws = outs[(N, K)]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            q.qlora_time_next_launch(q.QLORA_KERNEL_QUANTIZE, a, b)
+            q.qlora_nf4_quantize(Wd, qt, ws)
+            torch.cuda.synchronize()
+            # the quantize call is one main kernel plus the small double
+            # quantization encode; the event pair brackets the main kernel
+            total_ms += a.elapsed_time(b)
+            total_params += N * K
+            nbytes += int(N * K * (2 + 0.5 + 1 / 64)) + 4 * ((N * K // 64 + 255) // 256) + 4
+            del Wd
+        gbs = nbytes / (total_ms * 1e-3) / 1e9
+        out[f"workload{widx}"] = {"list": label, "tensors": len(tl), "params": total_params,
+                                  "quantize_kernel_ms": round(total_ms, 3), "bytes": nbytes,
+                                  "params_per_s": round(total_params / (total_ms * 1e-3), 1),
+                                  "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                                  "sample": "first block/layer + 2 padding matrices" if args.bulk_sample else "whole list"}
+        log(f"[bench] bulk quantize workload {widx}: {total_params / 1e9:.2f}e9 params in {total_ms:.1f} ms, "
+            f"{gbs:.0f} GB/s")
+        del outs
+        torch.cuda.empty_cache()
     return out
 
 
@@ -585,6 +788,10 @@ def main():
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-formats", action="store_true")
     ap.add_argument("--no-f16", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-bulk", action="store_true")
+    ap.add_argument("--bulk-sample", action="store_true", help="quantize one block / layer of the bulk lists only")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -600,23 +807,29 @@ def main():
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
-        copy_calibration(torch, args.copy_calibration)
-    mlp = run_mlp(torch, q, args)
+        copy_calibration(torch, q, args.copy_calibration)
+    peaks = measured_peaks(torch, q)
+    mlp = run_step(torch, q, args)
+    mlp["roofline"]["frac_of_measured_mfma"] = round(mlp["roofline"]["achieved"] / peaks["mfma_loop_TFLOP/s"], 4)
+    workloads = None if args.no_workloads else run_workloads(torch, q, args, peaks)
+    sweep = None if args.no_sweep else run_m_sweep(torch, q, args)
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
+    bulk = None if args.no_bulk else run_bulk(torch, q, args)
     adamw = None if args.no_adamw else run_adamw(torch, q, args)
     merge = None if args.no_merge else run_merge(torch, q, args)
     formats = None if args.no_formats else run_formats(torch, q, args)
     f16_step = None
     if not args.no_f16:
-        m16 = run_mlp(torch, q, args, f16=True, steps=5, warmup=2)
+        m16 = run_step(torch, q, args, f16=True, steps=5, warmup=2, with_quantize=False)
         f16_step = {"ms_per_step": round(m16["ms_per_step"], 4),
                     "TFLOP/s": round(m16["flops"] / (m16["ms_per_step"] * 1e-3) / 1e12, 2),
                     "fwd_gemm_ms": round(m16["per_kernel"]["fwd_gemm"]["avg_ms"], 4),
                     "dx_gemm_ms": round(m16["per_kernel"]["dx_gemm"]["avg_ms"], 4)}
         log(f"[bench] fp16 compute step: {f16_step}")
-    peaks = measured_peaks(torch)
-    mlp["roofline"]["frac_of_measured_matmul"] = round(mlp["roofline"]["achieved"] / peaks["bf16_matmul_TFLOP/s"], 4)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline()
+        cpu["breadth"] = run_cpu_breadth()
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -632,14 +845,19 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": "llama-7b MLP linears (gate, up 4096->11008; down 11008->4096), "
-                               "step = NF4+DQ quantize + fwd + bwd per linear",
+                               "step = fwd + bwd per linear of NF4+DQ weights quantized once",
                    "global_batch": 4, "seq_len": 1024, "tokens": mlp["M"], "lora_rank": mlp["r"],
                    "lora_alpha": mlp["alpha"], "layers": mlp["layers"],
                    "flop_per_step": mlp["flops"], "parallelism": "single GPU"},
         "roofline": mlp["roofline"],
+        "step_with_quantize": {"ms": round(mlp["ms_per_step_with_quantize"], 4),
+                               "TFLOP/s": round(mlp["flops"] / (mlp["ms_per_step_with_quantize"] * 1e-3) / 1e12, 2)},
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "gemv": gemv,
+        "workloads": workloads,
+        "m_sweep": sweep,
+        "bulk_quantize": bulk,
         "adamw": adamw,
         "merge": merge,
         "formats": formats,

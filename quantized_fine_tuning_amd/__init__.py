@@ -36,6 +36,8 @@ from ._binding import (  # noqa: F401
     qlora_linear_fwd,
     qlora_linear_fwd_ex,
     qlora_linear_fwd_noalloc,
+    qlora_bench_mfma_peak,
+    qlora_bench_copy,
     qlora_linear_bwd_ex,
     qlora_merge_lora,
     qlora_quantize_format,

@@ -29,7 +29,8 @@ EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_l
            "qlora_linear_bwd", "qlora_nf4_codebook", "qlora_status_string", "qlora_last_error",
            "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora",
            "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format",
-           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qlora_linear_fwd_noalloc")
+           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qlora_linear_fwd_noalloc",
+           "qlora_bench_mfma_peak", "qlora_bench_copy")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -118,6 +119,10 @@ def _load():
     lib.qlora_linear_fwd_ex.restype = i32
     lib.qlora_linear_fwd_noalloc.argtypes = [P(qlora_nf4_t), vp, i64, vp, vp, i32, f32, vp, i32, vp, vp]
     lib.qlora_linear_fwd_noalloc.restype = i32
+    lib.qlora_bench_mfma_peak.argtypes = [i64, vp, P(i64), vp]
+    lib.qlora_bench_mfma_peak.restype = i32
+    lib.qlora_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.qlora_bench_copy.restype = i32
     lib.qlora_linear_bwd_ex.restype = i32
     lib.qlora_quantize_format.argtypes = [vp, i32, i64, i64, P(qlora_qtensor_t), vp]
     lib.qlora_dequantize_format.argtypes = [P(qlora_qtensor_t), vp, i32, vp]
@@ -351,6 +356,22 @@ def qlora_linear_bwd_ex(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved
                                    _ptr(dX, "dX"), _dtype(dX, "dX"), _ptr(dA, "dA"), _ptr(dB, "dB"),
                                    _ptr(ws, "ws"), _bytes(ws, "ws"), compute_dtype,
                                    _stream(stream)))
+
+
+def qlora_bench_mfma_peak(iters: int, sink, stream=None) -> int:
+    """Launches the MFMA reference loop; returns its FLOP count."""
+    torch = _torch()
+    _expect_numel(sink, "sink", 2048, torch.float32)
+    flop = ctypes.c_int64(0)
+    _check(lib.qlora_bench_mfma_peak(int(iters), _ptr(sink, "sink"), ctypes.byref(flop), _stream(stream)))
+    return int(flop.value)
+
+
+def qlora_bench_copy(src, dst, stream=None) -> None:
+    """Streaming copy of src into dst (same number of bytes)."""
+    if _bytes(src, "src") != _bytes(dst, "dst"):
+        raise ValueError("src and dst sizes differ")
+    _check(lib.qlora_bench_copy(_ptr(src, "src"), _ptr(dst, "dst"), _bytes(src, "src"), _stream(stream)))
 
 
 def qlora_time_next_launch(kernel_id: int, start_event=None, stop_event=None) -> None:

@@ -465,6 +465,24 @@ qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* 
   return ok();
 }
 
+qlora_status qlora_bench_mfma_peak(int64_t iters, float* sink, int64_t* flop, void* stream) {
+  const char* fn = "qlora_bench_mfma_peak";
+  if (iters < 1 || iters > (int64_t(1) << 30)) return fail(QLORA_ERR_INVALID_ARG, "%s: iters=%lld", fn, (long long)iters);
+  CHECK_PTR(sink);
+  if (flop == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: flop is NULL", fn);
+  *flop = qnf4::mfma_peak_flop(iters);
+  return hip_status(fn, qnf4::launch_mfma_peak(iters, sink, static_cast<hipStream_t>(stream)));
+}
+
+qlora_status qlora_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  const char* fn = "qlora_bench_copy";
+  CHECK_PTR(src);
+  CHECK_PTR(dst);
+  if (bytes <= 0 || bytes % 16 != 0)
+    return fail(QLORA_ERR_INVALID_ARG, "%s: bytes=%lld must be a positive multiple of 16", fn, (long long)bytes);
+  return hip_status(fn, qnf4::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 void qlora_nf4_codebook(float* out16) {
   if (out16 == nullptr) return;
   std::memcpy(out16, qnf4::codebook().q, 16 * sizeof(float));

@@ -180,4 +180,10 @@ hipError_t launch_format_dequantize(const uint8_t* codes, const float* absmax, i
 hipError_t launch_format_gemv(const uint8_t* codes, const float* absmax, int fmt, int64_t N, int64_t K,
                               const uint16_t* X, int64_t M, void* Y, bool y_bf16, hipStream_t st);
 
+// Benchmark instrumentation -------------------------------------------------
+constexpr int kPeakWorkgroups = 2048;  // 8 waves per compute unit of an MI355X
+int64_t mfma_peak_flop(int64_t iters);
+hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+
 }  // namespace qnf4

@@ -1,0 +1,59 @@
+// Benchmark instrumentation: the two in-run reference points the roofline
+// fractions are also reported against.
+//
+//   mfma_peak_kernel   v_mfma_f32_16x16x32_bf16 issued back to back from
+//                      registers (8 independent accumulators per wave, so the
+//                      matrix pipe never waits on a result), on every SIMD
+//                      of every compute unit: the bf16 dense MFMA rate the
+//                      chip sustains at the clock it runs at under that load.
+//   stream_copy_kernel a plain copy, 16 bytes per lane and access: the HBM
+//                      rate of a streaming read + write of known size, also
+//                      the calibration for the HBM byte counters.
+#include "host.h"
+
+namespace qnf4 {
+namespace {
+
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int64_t iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  u32x4_t a = {0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  u32x4_t b = {0x3c003c00u, 0x3c003c00u ^ (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
+  f32x4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = mfma_16x16x32(a, b, acc[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  if (s == 1234.5f) sink[blockIdx.x] = s;  // never in practice: keeps the MFMAs
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+}  // namespace
+
+int64_t mfma_peak_flop(int64_t iters) {
+  return (int64_t)kPeakWorkgroups * 4 * iters * 8 * (16 * 16 * 32 * 2);
+}
+
+hipError_t launch_mfma_peak(int64_t iters, float* sink, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(kPeakWorkgroups), dim3(256), 0, st, iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(2048), dim3(256), 0, st, static_cast<const u32x4_t*>(src),
+                     static_cast<u32x4_t*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace qnf4

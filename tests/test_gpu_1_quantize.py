@@ -134,6 +134,31 @@ def test_large_tensor_tree_levels():
     assert np.array_equal(G.host(qt.dq_scale).view(np.uint32), o.s.view(np.uint32))
 
 
+@pytest.mark.parametrize("n,k,seed", [(32000, 4096, 5061), (22016, 8192, 5037), (32000, 8192, 5042)])
+def test_bulk_shapes_device_drawn(n, k, seed):
+    # the bulk quantization shapes, drawn on the GPU as the bulk measurement
+    # draws them (bf16 N(0, 0.02^2)); mean, all E4M3 constants and group
+    # scales exact; codes and dequantized weights exact on 32 sampled rows
+    from workloads import device_normal
+
+    t = G.torch()
+    print(f"bulk shape {n}x{k} bf16 seed {seed}", flush=True)
+    Wd = device_normal(t, (n, k), seed, 0.02)
+    qt = G.gpu_quantize(Wd)
+    W = bf16_bits_to_f32(G.host(Wd.view(t.int16)).view(np.uint16))
+    del Wd
+    o = G.SampledOracle(W)
+    assert G.host(qt.dq_mean).view(np.uint32)[0] == np.float32(o.mu).view(np.uint32)
+    assert np.array_equal(G.host(qt.absmax_e4m3), o.e)
+    assert np.array_equal(G.host(qt.dq_scale).view(np.uint32), o.s.view(np.uint32))
+    rows = np.sort(np.random.default_rng(seed).choice(n, 32, replace=False))
+    codes_gpu = G.host(qt.codes).reshape(n, -1)[rows]
+    codes_ref, _ = nf4.quantize_codes(W[rows])
+    assert np.array_equal(codes_gpu.reshape(-1), nf4.pack_nibbles(codes_ref))
+    w_hat = G.host_bf16(G.gpu_dequantize(qt)).reshape(n, k)[rows]
+    assert np.array_equal(w_hat, o._blocks(rows, 0, k // 64))
+
+
 def test_deterministic():
     W = random_f32((1024, 1024), seed=9, scale=0.02)
     Wd = G.dev_f32(W)

@@ -136,3 +136,29 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
 def random_f32(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
     return (g.standard_normal(shape) * scale).astype(np.float32)
+
+
+def device_normal(torch, shape, seed: int, scale: float = 1.0, bf16: bool = True):
+    """Seeded N(0, scale^2) drawn on the GPU with torch's counter-based Philox
+    generator (fp32 draws, scaled, then rounded to bf16 unless bf16=False):
+    the large inputs of the 7B-block and 65B-layer workloads and of the bulk
+    quantization, where host generation would dominate the run.  The same
+    (shape, seed) gives the same tensor on every call."""
+    g = torch.Generator(device="cuda").manual_seed(int(seed))
+    t = torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).mul_(scale)
+    return t.to(torch.bfloat16) if bf16 else t
+
+
+# Bulk quantization tensor lists (the totals the 7B-block and 65B workloads
+# name; the two 32000-row embedding-shaped matrices only pad the totals):
+# 32 x the seven 7B-block linears + 2 x 32000x4096 = 6.738e9 parameters;
+# 80 x the seven 65B-layer linears + 2 x 32000x8192 = 65.29e9 parameters.
+def bulk_tensors(index: int):
+    w = WORKLOADS[index]
+    reps, emb = (32, (32000, 4096)) if index == 4 else (80, (32000, 8192))
+    out = []
+    for rep in range(reps):
+        for name, n, k in w.layers:
+            out.append((f"layer{rep}.{name}", n, k))
+    out += [("embed", emb[0], emb[1]), ("lm_head", emb[0], emb[1])]
+    return out
