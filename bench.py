@@ -9,6 +9,10 @@ quantization): for each of the three linears, the fused dequant-GEMM forward
 once, before the timed region (a training step does not re-quantize them);
 the step with the three quantizations included is reported beside it.
 Inputs are seeded synthetic data resident in HBM before the timed region.
+Before the W warmup steps, steps run untimed for --settle seconds (0.5): the
+GPU idles while the host draws the inputs, and its clocks take tens of
+milliseconds to come back up.  The JSON line carries the min / median / max
+of the K timed steps (events at every step boundary).
 
 value = fwd+bwd algorithmic FLOP per step / step time.  Algorithmic FLOP per
 linear: 4*M*N*K + 6*M*r*(K+N).
@@ -52,7 +56,7 @@ same counters read for the library's streaming copy of known size
 reported only while the kernel's sources are byte-identical to the ones
 profiled; otherwise null.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle S] [--no-cpu-baseline]
                        [--no-gemv] [--no-adamw] [--no-merge] [--no-formats] [--no-f16]
                        [--no-workloads] [--no-sweep] [--no-bulk] [--bulk-sample]
 """
@@ -231,21 +235,34 @@ def run_step(torch, q, args, widx=3, M=None, f16=False, steps=None, warmup=None,
             q.qlora_linear_bwd(L["qt"], L["X"], L["dY"], L["A"], L["B"], r, alpha, L["T"],
                                L["dX"], L["dA"], L["dB"], L["wsb"])
 
+    step_ms = []
+
     def timed(quantize, n, nw):
+        # The clocks ramp up over tens of milliseconds once the GPU is busy
+        # again (it idles while the host draws the inputs): steps are run
+        # for args.settle seconds first, then the warmup steps, then the
+        # timed ones, with an event at every step boundary.
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle:
+            step(quantize=quantize)
+            torch.cuda.synchronize()
         for _ in range(nw):
             step(quantize=quantize)
         torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
         for i in range(n):
             step(i, quantize, last=n - 1)
-        t_end.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / n
+        step_ms[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        return ev[0].elapsed_time(ev[n]) / n
 
     ms_per_step = timed(False, steps, warmup)
-    log(f"[bench] workload {widx}: {steps} timed fwd+bwd steps: {ms_per_step:.3f} ms/step")
+    step_stats = {"min": round(min(step_ms), 4), "median": round(statistics.median(step_ms), 4),
+                  "max": round(max(step_ms), 4)}
+    log(f"[bench] workload {widx}: {steps} timed fwd+bwd steps: {ms_per_step:.3f} ms/step "
+        f"(per step {step_stats})")
     per_kernel = {}
     for k in ("fwd_gemm", "dx_gemm"):
         durs = [a.elapsed_time(b) for a, b in events[k]]
@@ -279,12 +296,13 @@ def run_step(torch, q, args, widx=3, M=None, f16=False, steps=None, warmup=None,
                 "flop_per_launch": int(fwd_flop if dom == "fwd_gemm" else dx_flop)}
     del layers
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms_per_step, "ms_per_step_with_quantize": ms_q, "flops": flops, "M": M, "r": r,
+    return {"ms_per_step": ms_per_step, "step_ms": step_stats, "ms_per_step_with_quantize": ms_q,
+            "flops": flops, "M": M, "r": r,
             "alpha": alpha, "layers": [list(x) for x in w.w.layers], "per_kernel": per_kernel,
             "roofline": roofline}
 
 
-def run_workloads(torch, q, args, peaks):
+def run_workloads(torch, q, args):
     """fwd+bwd of the 7B decoder block (M = 8192) and the 65B layer (M = 2048)."""
     out = {}
     for widx, name in ((4, "llama-7b decoder block, 7 linears"), (5, "65b-shaped layer, 7 linears")):
@@ -292,9 +310,9 @@ def run_workloads(torch, q, args, peaks):
                        with_quantize=False)
         tf = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
         rl = res["roofline"]
-        rl["frac_of_measured_mfma"] = round(rl["achieved"] / peaks["mfma_loop_TFLOP/s"], 4)
         out[f"workload{widx}"] = {"workload": name, "tokens": res["M"], "lora_rank": res["r"],
                                   "flop_per_step": res["flops"], "ms_per_step": round(res["ms_per_step"], 4),
+                                  "step_ms": res["step_ms"],
                                   "TFLOP/s": round(tf, 2), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                   "roofline": rl,
                                   "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
@@ -792,6 +810,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-bulk", action="store_true")
     ap.add_argument("--bulk-sample", action="store_true", help="quantize one block / layer of the bulk lists only")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup (clock ramp-up)")
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -808,10 +828,8 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(torch, q, args.copy_calibration)
-    peaks = measured_peaks(torch, q)
     mlp = run_step(torch, q, args)
-    mlp["roofline"]["frac_of_measured_mfma"] = round(mlp["roofline"]["achieved"] / peaks["mfma_loop_TFLOP/s"], 4)
-    workloads = None if args.no_workloads else run_workloads(torch, q, args, peaks)
+    workloads = None if args.no_workloads else run_workloads(torch, q, args)
     sweep = None if args.no_sweep else run_m_sweep(torch, q, args)
     gemv = None if args.no_gemv else run_gemv(torch, q, args)
     bulk = None if args.no_bulk else run_bulk(torch, q, args)
@@ -826,6 +844,11 @@ def main():
                     "fwd_gemm_ms": round(m16["per_kernel"]["fwd_gemm"]["avg_ms"], 4),
                     "dx_gemm_ms": round(m16["per_kernel"]["dx_gemm"]["avg_ms"], 4)}
         log(f"[bench] fp16 compute step: {f16_step}")
+    # last: the register-only MFMA loop runs the chip at its power limit,
+    # and the clocks take a while to recover after it
+    peaks = measured_peaks(torch, q)
+    for res in [mlp["roofline"]] + [v["roofline"] for v in (workloads or {}).values()]:
+        res["frac_of_measured_mfma"] = round(res["achieved"] / peaks["mfma_loop_TFLOP/s"], 4)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline()
@@ -839,6 +862,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(mlp["ms_per_step"], 4),
+        "step_ms": mlp["step_ms"],
+        "settle_s": args.settle,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

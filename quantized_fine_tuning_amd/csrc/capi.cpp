@@ -264,7 +264,8 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_t* W, const void* X, int64
   const char* fn = "qlora_linear_fwd_noalloc";
   qlora_status st = check_fwd_args(fn, W, X, M, A, B, r, Y, y_dtype, T_save, QLORA_BF16);
   if (st != QLORA_OK) return st;
-  const qnf4::FwdLayout L = qnf4::fwd_layout(M, W->n_rows, W->n_cols, r);
+  // (splits of the GEMM's reduction are limited to what fits the array)
+  const qnf4::FwdLayout L = qnf4::fwd_layout(M, W->n_rows, W->n_cols, r, kStaticScratchBytes);
   if (L.total > kStaticScratchBytes)
     return fail(QLORA_ERR_WORKSPACE_TOO_SMALL,
                 "%s: this call needs %zu bytes of scratch; the static scratch holds %zu (use qlora_linear_fwd "

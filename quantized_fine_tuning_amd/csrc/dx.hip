@@ -32,6 +32,10 @@
 //   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
 //     AT2[k][j] = A[j mod Rp][k] (a transposed, padded copy of A), both
 //     copied straight into LDS.
+//   * With few tokens the tiles alone leave most compute units idle; then
+//     the n steps are split over `splits` workgroups per tile (the last
+//     split also takes the LoRA steps), each writing its fp32 partial tile
+//     to P[split][M][K], summed in split order by splitk_reduce_kernel.
 #include <type_traits>
 
 #include "host.h"
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
                                                               const uint16_t* __restrict__ AT2,
                                                               int64_t Rp, void* __restrict__ dX,
                                                               int dx_bf16, int tiles_m, int tiles_k,
+                                                              int splits, float* __restrict__ P,
                                                               Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sa0[TM * 128], sa1[TM * 128];  // A tiles: dY, then sU
   __shared__ __attribute__((aligned(16))) char sw[2][TK * 128];  // B tiles: Ŵᵀ, then AT2
@@ -79,14 +84,19 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // of 16-byte slot 8rg + (cg ^ rg))
   __shared__ __attribute__((aligned(256))) char stab[2][4][64 * 32];
   __shared__ __attribute__((aligned(16))) char scode[2][8][64 * 16];
-  int tmi, tki;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_k, tmi, tki)) return;
+  int tmi, tki, sp;
+  if (!tile_of(blockIdx.x, tiles_m, tiles_k, splits, tmi, tki, sp)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rg = lane >> 3, cg = lane & 7;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, k0 = (int64_t)tki * TK;
-  const int nsteps = (int)((N + NSTEP - 1) / NSTEP);
+  // this workgroup's n steps [nfirst, nfirst + nsteps) (step indices below
+  // are relative to nfirst) and its LoRA steps
+  const int nall = (int)((N + NSTEP - 1) / NSTEP);
+  const int nfirst = split_first(sp, splits, nall);
+  const int nsteps = split_first(sp + 1, splits, nall) - nfirst;
+  const int lsteps = sp == splits - 1 ? LSTEPS : 0;
   auto sab = [&](int i) { return i ? sa1 : sa0; };
 
   // Slice sigma (columns [32 sigma, +32)) of step t into Ŵᵀ(t): lane (rg, cg)
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       __syncthreads();
     }
 #pragma unroll 1
-    for (int s = nsteps - 1; s < nsteps + LSTEPS; ++s) {
+    for (int s = nsteps - 1; s < nsteps + lsteps; ++s) {
       mfma_step(sab(s & 1), sw[s & 1]);
       __syncthreads();
     }
@@ -248,7 +258,18 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     int row0 = 128 * wm + 4 * kq, col0 = 64 * wk + lr;
     asm volatile("" : "+v"(row0), "+v"(col0));
     const bool full = (m0 + TM <= M) && (k0 + TK <= K);
-    if (dx_bf16) {
+    if (splits > 1) {
+      float* Pp = P + ((int64_t)sp * M + m0 + row0) * K + k0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, k = k0 + col0 + 16 * j;
+            if (full || (m < M && k < K)) Pp[(16 * i + v) * K + 16 * j] = acc[i][j][v];
+          }
+    } else if (dx_bf16) {
       uint16_t* D = static_cast<uint16_t*>(dX) + (m0 + row0) * K + k0 + col0;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -298,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   const uint32_t y_gstride = (uint32_t)(8 * N * 2);
   const i32x4_t ryw = rsrc_words(dY + m0 * N, (M - m0) * N * 2);
   auto copy_y_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
-    dma_lds16(ryw, t + (64 * p + 8 * c) * 128, vy + c * y_gstride, (uint32_t)s * 128u);
+    dma_lds16(ryw, t + (64 * p + 8 * c) * 128, vy + c * y_gstride, (uint32_t)(nfirst + s) * 128u);
   };
   auto copy_y = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -329,8 +350,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     u32x4_t c0, c1;
   };
   auto load_codes = [&](Codes& r, int t) __attribute__((always_inline)) {
-    r.c0 = buf_load16(rc, vcode, (uint32_t)t * code_sstride);
-    r.c1 = buf_load16(rc, vcode + 16u, (uint32_t)t * code_sstride);
+    r.c0 = buf_load16(rc, vcode, (uint32_t)(nfirst + t) * code_sstride);
+    r.c1 = buf_load16(rc, vcode + 16u, (uint32_t)(nfirst + t) * code_sstride);
   };
   const uint32_t code_wbase = (uint32_t)((lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7));
   auto store_codes = [&](int t, const Codes& r) __attribute__((always_inline)) {
@@ -355,12 +376,12 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     uint32_t e, s;
   };
   auto load_consts = [&](Consts& r, int t) __attribute__((always_inline)) {
-    const uint32_t blk = ((uint32_t)t * NSTEP + (uint32_t)tb_row) * kpr + kb;
+    const uint32_t blk = ((uint32_t)(nfirst + t) * NSTEP + (uint32_t)tb_row) * kpr + kb;
     r.e = buf_load1(re, blk, 0u);
     r.s = buf_load4(rs, (blk / kDqBlock) * 4u, 0u);
   };
   auto build_table = [&](int t, const Consts& r) __attribute__((always_inline)) {
-    const bool row_ok = cols_ok && ((int64_t)t * NSTEP + tb_row < N);
+    const bool row_ok = cols_ok && ((int64_t)(nfirst + t) * NSTEP + tb_row < N);
     const float cp = decode_constant(r.e, __uint_as_float(r.s), mu);
     u32x4_t t0, t1;
 #pragma unroll
@@ -418,14 +439,16 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   }
   // last reduction step: copy LoRA step 0 (sU and AT2 tiles) into the other
   // buffers; then the LoRA steps
-  copy_su(sab(nsteps & 1), 0);
-  copy_at(sw[nsteps & 1], 0);
+  if (lsteps > 0) {
+    copy_su(sab(nsteps & 1), 0);
+    copy_at(sw[nsteps & 1], 0);
+  }
   wait_vmem();
   __syncthreads();
 #pragma unroll 1
-  for (int l = 0; l < LSTEPS; ++l) {
+  for (int l = 0; l < lsteps; ++l) {
     const int s = nsteps + l;
-    if (l + 1 < LSTEPS) {
+    if (l + 1 < lsteps) {
       copy_su(sab((s + 1) & 1), l + 1);
       copy_at(sw[(s + 1) & 1], l + 1);
     }
@@ -436,18 +459,24 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
 
 }  // namespace
 
+int dx_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap) {
+  const int64_t tiles = ((M + TM - 1) / TM) * ((K + TK - 1) / TK);
+  return gemm_splits(tiles, (N + NSTEP - 1) / NSTEP, M, K, cap);
+}
+
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st) {
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, int splits, float* P, bool f16,
+                          hipStream_t st) {
   const int tm = (int)((M + TM - 1) / TM), tk = (int)((W.K + TK - 1) / TK);
-  const unsigned grid = tile_grid(tm, tk);
+  const unsigned grid = tile_grid(tm, tk, splits);
   const int db = dx16 ? 1 : 0;
   switch (2 * Rp / NSTEP) {
 #define QNF4_DX_CASE(LS)                                                                      \
   case LS:                                                                                    \
     return f16 ? timed_launch(kKernDxGemm, dx_gemm_kernel<LS, true>, dim3(grid), dim3(kThreads), st, W, dY, M, \
-                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook()) \
+                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, splits, P, codebook()) \
                : timed_launch(kKernDxGemm, dx_gemm_kernel<LS, false>, dim3(grid), dim3(kThreads), st, W, dY, M, \
-                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, codebook());
+                              (const uint16_t*)sU, (const uint16_t*)AT2, Rp, dX, db, tm, tk, splits, P, codebook());
     QNF4_DX_CASE(1)
     QNF4_DX_CASE(2)
     QNF4_DX_CASE(3)

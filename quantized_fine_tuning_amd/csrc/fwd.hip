@@ -37,6 +37,10 @@
 //   * Workgroups are mapped to tiles so that each XCD (workgroup id mod 8)
 //     walks a contiguous run of a grouped tile order (4 M-tiles per group):
 //     the ~32 workgroups resident on one XCD share X and code rows in its L2.
+//   * With few tokens the tiles alone leave most compute units idle; then
+//     the K steps are split over `splits` workgroups per tile (the last
+//     split also takes the LoRA steps), each writing its fp32 partial tile
+//     to P[split][M][N], summed in split order by splitk_reduce_kernel.
 #include <type_traits>
 
 #include "host.h"
@@ -67,19 +71,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                const uint16_t* __restrict__ B2,
                                                                int64_t Rp, void* __restrict__ Y,
                                                                int y_bf16, int tiles_m, int tiles_n,
+                                                               int splits, float* __restrict__ P,
                                                                Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
   // tables of the tile's weight rows (row r at 32(r % 8) + 256(r / 8)),
   // double-buffered by step
   __shared__ __attribute__((aligned(256))) char stab[2][TN * 32];
-  int tmi, tni;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni)) return;
+  int tmi, tni, sp;
+  if (!tile_of(blockIdx.x, tiles_m, tiles_n, splits, tmi, tni, sp)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, n0 = (int64_t)tni * TN;
-  const int ksteps = (int)(K / KSTEP);
+  // this workgroup's K steps [kfirst, kfirst + ksteps) (step indices below
+  // are relative to kfirst) and its LoRA steps
+  const int kall = (int)(K / KSTEP);
+  const int kfirst = split_first(sp, splits, kall);
+  const int ksteps = split_first(sp + 1, splits, kall) - kfirst;
+  const int lsteps = sp == splits - 1 ? LSTEPS : 0;
   auto sxb = [&](int i) { return i ? sx1 : sx0; };
 
   // Resources start at this tile's first row and end at the tensor's last
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const int dr = lane >> 3, dc = lane & 7;
   const uint32_t dr32x4 = (uint32_t)dr * 0x20202020u;
   auto load_code = [&](int R, int t) __attribute__((always_inline)) {
-    return buf_load4(rc, (uint32_t)(R + dr) * (uint32_t)(K / 2) + 4u * (uint32_t)dc, (uint32_t)t * 32u);
+    return buf_load4(rc, (uint32_t)(R + dr) * (uint32_t)(K / 2) + 4u * (uint32_t)dc, (uint32_t)(kfirst + t) * 32u);
   };
   auto lookup_group = [&](uint32_t w, const char* tabs, int R, uint32_t* v) __attribute__((always_inline)) {
     const uint32_t tab = lds_offset(tabs) + 256u * (uint32_t)(R >> 3) + 32u * (uint32_t)dr;
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       __syncthreads();
     }
 #pragma unroll 1
-    for (int s = ksteps - 1; s < ksteps + LSTEPS; ++s) {
+    for (int s = ksteps - 1; s < ksteps + lsteps; ++s) {
       mfma_step(sxb(s & 1), sw[s & 1]);
       __syncthreads();
     }
@@ -213,7 +223,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     int row0 = 128 * wm + 4 * kq, col0 = 64 * wn + lr;
     asm volatile("" : "+v"(row0), "+v"(col0));
     const bool full = (m0 + TM <= M) && (n0 + TN <= N);
-    if (y_bf16) {
+    if (splits > 1) {
+      float* Pp = P + ((int64_t)sp * M + m0 + row0) * N + n0 + col0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t m = m0 + row0 + 16 * i + v, n = n0 + col0 + 16 * j;
+            if (full || (m < M && n < N)) Pp[(16 * i + v) * N + 16 * j] = acc[i][j][v];
+          }
+    } else if (y_bf16) {
       uint16_t* Yb = static_cast<uint16_t*>(Y) + (m0 + row0) * N + n0 + col0;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const uint32_t x_gstride = (uint32_t)(8 * K * 2);
   const i32x4_t rxw = rsrc_words(X + m0 * K, (M - m0) * K * 2);
   auto copy_x_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
-    dma_lds16(rxw, t + (64 * p + 8 * c) * 128, vx + c * x_gstride, (uint32_t)s * 128u);
+    dma_lds16(rxw, t + (64 * p + 8 * c) * 128, vx + c * x_gstride, (uint32_t)(kfirst + s) * 128u);
   };
   auto copy_x = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
@@ -289,12 +310,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     uint32_t e, s;
   };
   auto load_consts = [&](Consts& r, int t) __attribute__((always_inline)) {
-    r.e = buf_load4(re, (ve_me + (uint32_t)t) & ~3u, 0u);
-    r.s = buf_load4(rs, ((blk_me + (uint32_t)t) / kDqBlock) * 4u, 0u);
+    r.e = buf_load4(re, (ve_me + (uint32_t)(kfirst + t)) & ~3u, 0u);
+    r.s = buf_load4(rs, ((blk_me + (uint32_t)(kfirst + t)) / kDqBlock) * 4u, 0u);
   };
   const int tb_off = 32 * (lane & 7) + 256 * (8 * p + (lane >> 3));
   auto build_table = [&](int t, const Consts& r) __attribute__((always_inline)) {
-    const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)t) & 3u))) & 0xffu;
+    const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)(kfirst + t)) & 3u))) & 0xffu;
     const float cp = decode_constant(e, __uint_as_float(r.s), mu);
     u32x4_t t0, t1;
 #pragma unroll
@@ -355,14 +376,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   }
   // last weight step: copy LoRA step 0 (sT and B2 tiles) into the other
   // buffers; then the LoRA steps
-  copy_lora(rt, sxb(ksteps & 1), 0);
-  copy_lora(rb, sw[ksteps & 1], 0);
+  if (lsteps > 0) {
+    copy_lora(rt, sxb(ksteps & 1), 0);
+    copy_lora(rb, sw[ksteps & 1], 0);
+  }
   wait_vmem();
   __syncthreads();
 #pragma unroll 1
-  for (int l = 0; l < LSTEPS; ++l) {
+  for (int l = 0; l < lsteps; ++l) {
     const int s = ksteps + l;
-    if (l + 1 < LSTEPS) {
+    if (l + 1 < lsteps) {
       copy_lora(rt, sxb((s + 1) & 1), l + 1);
       copy_lora(rb, sw[(s + 1) & 1], l + 1);
     }
@@ -373,18 +396,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
 
 }  // namespace
 
+int fwd_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap) {
+  const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+  return gemm_splits(tiles, K / KSTEP, M, N, cap);
+}
+
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
-                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, bool f16, hipStream_t st) {
+                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, int splits, float* P, bool f16,
+                           hipStream_t st) {
   const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
-  const unsigned grid = tile_grid(tm, tn);
+  const unsigned grid = tile_grid(tm, tn, splits);
   const int yb = y16 ? 1 : 0;
   switch (2 * Rp / KSTEP) {
 #define QNF4_FWD_CASE(LS)                                                                   \
   case LS:                                                                                  \
     return f16 ? timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, true>, dim3(grid), dim3(kThreads), st, W, X, M, \
-                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook()) \
+                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, splits, P, codebook()) \
                : timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, false>, dim3(grid), dim3(kThreads), st, W, X, M, \
-                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, codebook());
+                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, splits, P, codebook());
     QNF4_FWD_CASE(1)
     QNF4_FWD_CASE(2)
     QNF4_FWD_CASE(3)

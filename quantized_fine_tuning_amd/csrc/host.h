@@ -120,11 +120,16 @@ size_t gemv_partial_bytes(int64_t K, int32_t r);
 // Forward ------------------------------------------------------------------
 struct FwdLayout {
   // fp32 T [M, r] (if not saved by the caller), bf16 sT [M, 2Rp], bf16 B2
-  // [N, 2Rp], fp32 partial sums of T over the reduction slices
+  // [N, 2Rp], one fp32 partial-sum area: first the partial sums of T over
+  // the reduction slices, then (splits > 1) the GEMM's split partials
+  // [splits, M, N]
   size_t off_T, off_sT, off_B2, off_P, total;
   SkPlan pT;
+  int splits;
 };
-FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
+// cap: the most bytes the layout may take; the GEMM's reduction splits are
+// reduced until it fits (the layout may still exceed cap without splits).
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, size_t cap = SIZE_MAX);
 // The largest fwd_layout(M, ...).total over M in [0, M_max].
 size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r);
 
@@ -136,9 +141,11 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
 struct BwdLayout {
   // bf16 sT, sU [M, 2Rp] and their transposes sTT, sUT [2Rp, Mp]; bf16 BT
   // [Rp, round_up(N, 64)]; bf16 AT2 [K, 2Rp]; one fp32 partial-sum area
-  // reused by the T, U, dA and dB reductions
+  // reused by the T, U, dA and dB reductions and (splits > 1) the dX GEMM's
+  // split partials [splits, M, K]
   size_t off_sT, off_sTT, off_sU, off_sUT, off_BT, off_AT2, off_P, total;
   SkPlan pT, pU, pA, pB;
+  int splits;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 // The largest bwd_layout(M, ...).total over M in [0, M_max].

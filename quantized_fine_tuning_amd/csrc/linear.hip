@@ -13,14 +13,21 @@
 namespace qnf4 {
 
 hipError_t launch_dx_gemm(const Nf4View& W, const uint16_t* dY, int64_t M, const uint16_t* sU,
-                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, bool f16, hipStream_t st);
+                          const uint16_t* AT2, int64_t Rp, void* dX, bool dx16, int splits, float* P, bool f16,
+                          hipStream_t st);
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
-                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, bool f16, hipStream_t st);
+                           const uint16_t* B2, int64_t Rp, void* Y, bool y16, int splits, float* P, bool f16,
+                           hipStream_t st);
+hipError_t launch_splitk_reduce(const float* P, int splits, int64_t n, void* out, bool out16, bool f16,
+                                hipStream_t st);
+int fwd_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap);
+int dx_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap);
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
                        int32_t r, float scale, void* Y, bool y16, float* T, float* P, bool f16, hipStream_t st);
 
-FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, size_t cap) {
   FwdLayout L{};
+  L.splits = 1;
   const int64_t Rp = lora_rp(r);
   size_t off = 0;
   L.off_T = off;
@@ -32,7 +39,9 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   L.off_P = off;
   if (M > 16) {
     L.pT = rowred_plan(M, K, Rp);
-    off += round_up(rowred_partial_bytes(L.pT), 256);
+    const size_t p = round_up(rowred_partial_bytes(L.pT), 256);
+    L.splits = fwd_gemm_splits(M, N, K, cap > off ? cap - off : 0);
+    off += L.splits > 1 ? std::max<size_t>(p, round_up((size_t)L.splits * M * N * 4, 256)) : p;
   } else if (M > 0) {
     off += round_up(gemv_partial_bytes(K, r), 256);  // partial tiles of T
   }
@@ -65,11 +74,14 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   // one partial-sum area reused by the successive reductions
   L.off_P = off;
   size_t p = 0;
+  L.splits = 1;
   if (M > 0) {
     p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pT), 256));
     p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pU), 256));
     p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pA), 256));
     p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pB), 256));
+    L.splits = dx_gemm_splits(M, N, K, SIZE_MAX);
+    if (L.splits > 1) p = std::max<size_t>(p, round_up((size_t)L.splits * M * K * 4, 256));
   }
   off += p;
   L.total = off;
@@ -95,6 +107,22 @@ size_t colred_bytes_bound(int64_t M, int64_t Pn, int64_t Rp) {
   if (tiles >= (int64_t)kSkWorkgroups) return round_up(tiles * 2 * 128 * 64 * 4, 256);
   return round_up(colred_partial_bytes(colred_plan(M, Pn, Rp)), 256);
 }
+// The GEMMs' split partials over M in [1, M_max] (the forward GEMM runs
+// from 17 tokens on, the dX GEMM from 1): the split count depends on M only
+// through the number of 256-row tiles, and within one such band the bytes
+// grow with M, so each band's largest M is taken.
+size_t splitk_bytes_max(int64_t M_max, int64_t N, int64_t K, bool fwd) {
+  size_t p = 0;
+  for (int64_t top = 256;; top += 256) {
+    const int64_t M = std::min(top, M_max);
+    if (M > (fwd ? 16 : 0)) {
+      const int s = fwd ? fwd_gemm_splits(M, N, K, SIZE_MAX) : dx_gemm_splits(M, N, K, SIZE_MAX);
+      if (s > 1) p = std::max<size_t>(p, round_up((size_t)s * M * (fwd ? N : K) * 4, 256));
+    }
+    if (top >= M_max) break;
+  }
+  return p;
+}
 }  // namespace
 
 size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
@@ -103,7 +131,7 @@ size_t fwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
   if (M_max <= 16) return small;
   const FwdLayout L = fwd_layout(M_max, N, K, r);
   const int64_t Rp = lora_rp(r);
-  size_t p = 0;
+  size_t p = splitk_bytes_max(M_max, N, K, true);
   for (int64_t M = 64; M < M_max + 64; M += 64) p = std::max(p, rowred_bytes_bound(std::min(M, M_max), K, Rp));
   return std::max(small, L.off_P + p);
 }
@@ -112,7 +140,7 @@ size_t bwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
   const BwdLayout L = bwd_layout(M_max, N, K, r);
   if (M_max <= 0) return L.total;
   const int64_t Rp = lora_rp(r);
-  size_t p = 0;
+  size_t p = splitk_bytes_max(M_max, N, K, false);
   for (int64_t M = 64; M < M_max + 64; M += 64) {
     const int64_t m = std::min(M, M_max);
     p = std::max({p, rowred_bytes_bound(m, K, Rp), rowred_bytes_bound(m, N, Rp), colred_bytes_bound(m, K, Rp),
@@ -135,7 +163,10 @@ hipError_t launch_forward(const Nf4View& W, const uint16_t* X, int64_t M, const 
   uint16_t* B2 = reinterpret_cast<uint16_t*>(ws + L.off_B2);
   e = launch_rowred_finish(P, L.pT, M, r, Rp, scale, T, sT, nullptr, B, W.N, B2, f16, st);
   if (e != hipSuccess) return e;
-  return launch_fwd_gemm(W, X, M, sT, B2, Rp, Y, y16, f16, st);
+  // (the partial sums of T have been consumed: P now takes the split partials)
+  e = launch_fwd_gemm(W, X, M, sT, B2, Rp, Y, y16, L.splits, P, f16, st);
+  if (e != hipSuccess || L.splits == 1) return e;
+  return launch_splitk_reduce(P, L.splits, M * W.N, Y, y16, f16, st);
 }
 
 hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* dY, int64_t M,
@@ -171,7 +202,8 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   if (e == hipSuccess) e = launch_rowred_finish(P, L.pU, M, r, Rp, scale, nullptr, sU, sUT, nullptr, 0, nullptr, f16, st);
   if (e != hipSuccess) return e;
   // dX = [dY | sU_hi | sU_lo] · [Ŵ ; A ; A]
-  e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx16, f16, st);
+  e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx16, L.splits, P, f16, st);
+  if (e == hipSuccess && L.splits > 1) e = launch_splitk_reduce(P, L.splits, M * K, dX, dx16, f16, st);
   if (e != hipSuccess) return e;
   // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
   e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, f16, st);

@@ -5,6 +5,11 @@
 // grouped tile order, so the ~32 workgroups resident on one XCD at a time
 // cover a compact block of tiles (4 M-tiles by ~8 N-tiles) and share their
 // operand rows in that XCD's L2.
+//
+// When the output has too few tiles to occupy the chip (few tokens), the
+// reduction is split: unit u = (split, tile), split-major, each unit one
+// workgroup that reduces over its own range of steps and writes an fp32
+// partial tile; a second kernel sums the partials in split order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,17 +19,41 @@ namespace qnf4 {
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-inline unsigned tile_grid(int tiles_m, int tiles_n) {
-  const int T = tiles_m * tiles_n;
+constexpr int kGemmCus = 256;  // one GEMM workgroup per compute unit
+
+inline unsigned tile_grid(int tiles_m, int tiles_n, int splits = 1) {
+  const int T = tiles_m * tiles_n * splits;
   return (unsigned)(kXcds * ((T + kXcds - 1) / kXcds));
 }
 
-// Returns false for the padding workgroups beyond the last tile.
-__device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+// Number of reduction splits for a GEMM of `tiles` output tiles and `steps`
+// reduction steps: 1 while the tiles fill at least 3/4 of the compute units,
+// else as many as fit one round of workgroups, with at least 8 steps each,
+// fewer while the fp32 partials (splits x rows x cols x 4 bytes) exceed
+// `cap` bytes.
+inline int gemm_splits(int64_t tiles, int64_t steps, int64_t rows, int64_t cols, size_t cap) {
+  if (tiles <= 0 || 4 * tiles >= 3 * kGemmCus) return 1;
+  int64_t s = kGemmCus / tiles;
+  s = s < steps / 8 ? s : steps / 8;
+  while (s > 1 && (size_t)s * (size_t)rows * (size_t)cols * 4u > cap) --s;
+  return s > 1 ? (int)s : 1;
+}
+
+// Steps [first, last) of split `sp` out of `splits` over `steps` steps.
+__host__ __device__ inline int split_first(int sp, int splits, int steps) {
+  return (int)(((int64_t)sp * steps) / splits);
+}
+
+// Returns false for the padding workgroups beyond the last unit.
+__device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int splits, int& tm, int& tn,
+                                        int& sp) {
   const int T = tiles_m * tiles_n;
-  const int per = (T + kXcds - 1) / kXcds;
-  const int t = (bid % kXcds) * per + bid / kXcds;
-  if (t >= T) return false;
+  const int U = T * splits;
+  const int per = (U + kXcds - 1) / kXcds;
+  const int u = (bid % kXcds) * per + bid / kXcds;
+  if (u >= U) return false;
+  sp = u / T;
+  const int t = u - sp * T;
   const int group = t / (kGroupM * tiles_n);
   const int first = group * kGroupM;
   const int gm = min(kGroupM, tiles_m - first);

@@ -136,10 +136,15 @@ def check_elementwise(got, ref, scale, n, out16, what):
 def test_mlp_7b_full_size_every_element(layer):
     """Every element of Y, dX, dA and dB of one 7B MLP linear at M = 4096,
     r = 64, in the launch configuration the benchmark times."""
+    compare_every_element(layer, Inputs(3).w.tokens[0])
+
+
+def compare_every_element(layer, M):
+    """Every element of Y, dX, dA and dB of the 7B MLP linear `layer` at M
+    tokens (r = 64) against the oracle."""
     t = torch()
     w = Inputs(3)
     name, N, K = w.w.layers[layer]
-    M = w.w.tokens[0]
     r, alpha = w.w.rank, w.w.alpha
     s = alpha / r
     print(f"7b MLP {name} {N}x{K} M={M} r={r}: every element", flush=True)

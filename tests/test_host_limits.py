@@ -50,6 +50,16 @@ def test_sizes_cover_every_smaller_token_count(N, K, r, M_max):
         assert bwd_need(N, K, M, r) <= s["bwd_ws_bytes"], M
 
 
+@pytest.mark.parametrize("N,K,r", [(11008, 4096, 64), (4096, 11008, 64), (4096, 4096, 16)])
+def test_sizes_cover_each_small_token_count(N, K, r):
+    # sizes at M_max itself, for every M_max up to 300 (the GEMV forward, the
+    # split reductions of both GEMMs)
+    for M in range(1, 301):
+        s = q.qlora_nf4_sizes(N, K, M, r)
+        assert fwd_need(N, K, M, r) <= s["fwd_ws_bytes"], M
+        assert bwd_need(N, K, M, r) <= s["bwd_ws_bytes"], M
+
+
 def test_sizes_are_monotone_in_m_max():
     prev_f = prev_b = 0
     for M in range(0, 3000, 37):
@@ -109,7 +119,15 @@ def test_noalloc_forward_rejects_calls_beyond_its_scratch():
     # every workload linear fits at its token count
     for N, K, M in ((11008, 4096, 8192), (4096, 11008, 8192), (22016, 8192, 2048), (8192, 22016, 2048),
                     (8192, 8192, 8192), (22016, 8192, 8192)):
-        assert q.qlora_nf4_sizes(N, K, M, 64)["fwd_ws_bytes"] <= 32 << 20, (N, K, M)
+        assert fwd_need(N, K, M, 64) <= 32 << 20, (N, K, M)
+    # few tokens: the workspace forward splits the GEMM's reduction and needs
+    # more than the array for its partials; the no-alloc forward takes fewer
+    # splits and is not rejected (here it fails later, at the first HIP call,
+    # since this host has no GPU)
+    for N, K, M in ((22016, 8192, 256), (11008, 4096, 512), (22016, 8192, 17)):
+        st = f(ctypes.byref(desc(N, K)), FAKE, M, FAKE, FAKE, 64, 16.0, FAKE, q.QLORA_BF16, None, None)
+        assert st != q.QLORA_ERR_WORKSPACE_TOO_SMALL, (N, K, M)
+    assert fwd_need(11008, 4096, 512, 64) > 32 << 20 and fwd_need(22016, 8192, 256, 64) > 32 << 20
 
 
 # ---------------------------------------------------------------- binding
