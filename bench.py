@@ -725,13 +725,16 @@ def measured_peaks(torch, q):
         torch.cuda.synchronize()
         return statistics.median(a.elapsed_time(b) for a, b in evs)
 
-    sink = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(2056, dtype=torch.float32, device="cuda")
     flop = {}
 
     def mfma():
         flop["n"] = q.qlora_bench_mfma_peak(20000, sink)
 
     mfma_ms = med_ms(mfma)
+    # shader clock of the last loop: counter ticks / real-time seconds
+    clk = sink[2048:].view(torch.int64).cpu().tolist()
+    mfma_ghz = (clk[1] - clk[0]) / ((clk[3] - clk[2]) / (q.qlora_bench_wall_clock_khz() * 1e3)) / 1e9
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -743,6 +746,9 @@ def measured_peaks(torch, q):
     mm_ms = med_ms(lambda: torch.matmul(a, b))
     del a, b
     out = {"mfma_loop_TFLOP/s": round(flop["n"] / (mfma_ms * 1e-3) / 1e12, 1),
+           "mfma_loop_shader_clock_GHz": round(mfma_ghz, 3),
+           # the dense bf16 rate at 2.5 PFLOP/s per 2.4 GHz, scaled to that clock
+           "spec_peak_at_that_clock_TFLOP/s": round(PEAK_BF16_TFLOPS * mfma_ghz / 2.4, 1),
            "copy_GB/s": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
            "context_torch_bf16_matmul_TFLOP/s": round(2 * M * N * K / (mm_ms * 1e-3) / 1e12, 1),
            "context_torch_bf16_matmul_shape": [M, N, K]}

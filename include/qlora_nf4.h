@@ -311,15 +311,22 @@ qlora_status qlora_time_next_launch(int32_t kernel_id, void* start_event, void* 
 
 /* Benchmark reference points (not part of the method).
  * qlora_bench_mfma_peak: 2048 workgroups of 4 waves issue `iters` rounds of 8
- * independent v_mfma_f32_16x16x32_bf16 from registers (sink: device float
- * array of 2048, written only in a case that does not occur); *flop receives
- * the dense bf16 FLOP the launch performs, so FLOP / the launch's time is the
- * MFMA rate the chip sustains.  1 <= iters <= 2^30.
+ * independent v_mfma_f32_16x16x32_bf16 from registers; *flop receives the
+ * dense bf16 FLOP the launch performs, so FLOP / the launch's time is the
+ * MFMA rate the chip sustains.  sink: device array of 2056 floats, 8-byte
+ * aligned; its first 2048 are written only in a case that does not occur;
+ * the last 8 receive four uint64 values from the first lane of workgroup 0:
+ * the shader clock counter before and after its loop, then the real-time
+ * counter before and after (its rate: qlora_bench_wall_clock_khz).
+ * 1 <= iters <= 2^30.
+ * qlora_bench_wall_clock_khz: the current device's real-time counter rate
+ * in kHz (hipDeviceAttributeWallClockRate).
  * qlora_bench_copy: a streaming copy of `bytes` (a positive multiple of 16)
  * from src to dst (device, 16-byte aligned, not overlapping): the HBM rate of
  * a plain read + write, and the calibration of the HBM byte counters. */
 qlora_status qlora_bench_mfma_peak(int64_t iters, float* sink, int64_t* flop, void* stream);
 qlora_status qlora_bench_copy(const void* src, void* dst, int64_t bytes, void* stream);
+qlora_status qlora_bench_wall_clock_khz(int32_t* khz);
 
 /* The 16 fp32 NF4 levels as the library computes them (host memory, 16
  * floats), ascending, index 7 = 0.  (P4 §三: levels at standard-normal

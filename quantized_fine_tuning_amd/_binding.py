@@ -30,7 +30,7 @@ EXPORTS = ("qlora_nf4_sizes", "qlora_nf4_quantize", "qlora_dequantize", "qlora_l
            "qlora_time_next_launch", "qlora_adamw_step", "qlora_merge_lora",
            "qlora_quantize_format", "qlora_dequantize_format", "qlora_gemv_format",
            "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qlora_linear_fwd_noalloc",
-           "qlora_bench_mfma_peak", "qlora_bench_copy")
+           "qlora_bench_mfma_peak", "qlora_bench_copy", "qlora_bench_wall_clock_khz")
 
 QLORA_KERNEL_NONE = 0
 QLORA_KERNEL_FWD_GEMM = 1
@@ -123,6 +123,8 @@ def _load():
     lib.qlora_bench_mfma_peak.restype = i32
     lib.qlora_bench_copy.argtypes = [vp, vp, i64, vp]
     lib.qlora_bench_copy.restype = i32
+    lib.qlora_bench_wall_clock_khz.argtypes = [P(i32)]
+    lib.qlora_bench_wall_clock_khz.restype = i32
     lib.qlora_linear_bwd_ex.restype = i32
     lib.qlora_quantize_format.argtypes = [vp, i32, i64, i64, P(qlora_qtensor_t), vp]
     lib.qlora_dequantize_format.argtypes = [P(qlora_qtensor_t), vp, i32, vp]
@@ -359,12 +361,21 @@ def qlora_linear_bwd_ex(W: Nf4Tensor, X, dY, A, B, r: int, alpha: float, T_saved
 
 
 def qlora_bench_mfma_peak(iters: int, sink, stream=None) -> int:
-    """Launches the MFMA reference loop; returns its FLOP count."""
+    """Launches the MFMA reference loop; returns its FLOP count.  sink: 2056
+    float32 on the device; sink[2048:].view(int64) receives the shader and
+    real-time clock counters of workgroup 0 (start, end, start, end)."""
     torch = _torch()
-    _expect_numel(sink, "sink", 2048, torch.float32)
+    _expect_numel(sink, "sink", 2056, torch.float32)
     flop = ctypes.c_int64(0)
     _check(lib.qlora_bench_mfma_peak(int(iters), _ptr(sink, "sink"), ctypes.byref(flop), _stream(stream)))
     return int(flop.value)
+
+
+def qlora_bench_wall_clock_khz() -> int:
+    """Rate of the device's real-time counter, kHz."""
+    khz = ctypes.c_int32(0)
+    _check(lib.qlora_bench_wall_clock_khz(ctypes.byref(khz)))
+    return int(khz.value)
 
 
 def qlora_bench_copy(src, dst, stream=None) -> None:

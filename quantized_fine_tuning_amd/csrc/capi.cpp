@@ -475,6 +475,15 @@ qlora_status qlora_bench_mfma_peak(int64_t iters, float* sink, int64_t* flop, vo
   return hip_status(fn, qnf4::launch_mfma_peak(iters, sink, static_cast<hipStream_t>(stream)));
 }
 
+qlora_status qlora_bench_wall_clock_khz(int32_t* khz) {
+  const char* fn = "qlora_bench_wall_clock_khz";
+  if (khz == nullptr) return fail(QLORA_ERR_INVALID_ARG, "%s: khz is NULL", fn);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return hip_status(fn, e);
+}
+
 qlora_status qlora_bench_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   const char* fn = "qlora_bench_copy";
   CHECK_PTR(src);

@@ -345,6 +345,28 @@ __device__ __forceinline__ int sk_count(uint32_t t, uint32_t ut, uint32_t U, uin
   return (int)(sk_owner((t + 1) * ut - 1, U, G) - sk_owner(t * ut, U, G)) + 1;
 }
 
+// acc[e] = slot 0 + slot 1 + ... + slot cnt-1 of element threadIdx.x + 256e
+// (slots SLOT floats apart), added in slot order; the loads of four slots
+// are issued before their adds.
+template <int E, int SLOT>
+__device__ __forceinline__ void sum_slots(const float* __restrict__ pt, int cnt, float* acc) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < cnt; c += 4) {
+    float v[4][E];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        v[i][e] = c + i < cnt ? pt[(int64_t)(c + i) * SLOT + threadIdx.x + 256 * e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (c + i < cnt) acc[e] = __fadd_rn(acc[e], v[i][e]);
+  }
+}
+
 // rowred tiles (64 m x 64 j) → optional fp32 T [M, r]; hi/lo split of
 // scale·T into out [M, 2Rp] (hi in columns < Rp, lo from Rp; zeros for
 // j >= r) and, if outT is non-null, its transpose outT [2Rp, Mp] (zeros for
@@ -362,11 +384,23 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
   if (blockIdx.x >= pad_b0) {
     // blocks past the tiles' (only when B2 is given): the forward GEMM's
     // LoRA operand, in the same launch: B2[n][j] = B[n][j mod Rp] for
-    // (j mod Rp) < r, else 0 ([N, 2Rp])
-    const int64_t idx = (int64_t)(blockIdx.x - pad_b0) * 256 + threadIdx.x;
-    if (idx >= N * 2 * Rp) return;
-    const int64_t n = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
-    B2[idx] = j < r ? B[n * r + j] : (uint16_t)0;
+    // (j mod Rp) < r, else 0 ([N, 2Rp]); 8 consecutive j of one row per
+    // lane (2Rp is a multiple of 64), one 16-byte store
+    const uint32_t cpr = (uint32_t)(2 * Rp / 8);  // chunks per row
+    const uint32_t idx = (blockIdx.x - pad_b0) * 256u + threadIdx.x;
+    if (idx >= (uint32_t)N * cpr) return;
+    const uint32_t n = idx / cpr, jc = (idx - n * cpr) * 8u;
+    const uint16_t* br = B + (int64_t)n * r;
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t jj = jc + (uint32_t)e, j = jj >= (uint32_t)Rp ? jj - (uint32_t)Rp : jj;
+      w[e] = j < (uint32_t)r ? (uint32_t)br[j] : 0u;
+    }
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = w[2 * e] | (w[2 * e + 1] << 16);
+    *reinterpret_cast<u32x4_t*>(B2 + (int64_t)idx * 8) = o;
     return;
   }
   const uint32_t t = blockIdx.x >> 1, half = blockIdx.x & 1;
@@ -374,15 +408,7 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
   const int cnt = sk_count(t, ut, U, G);
   const float* pt = P + (int64_t)t * cmax * 4096 + 32 * half * 64;
   float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < cnt; ++c) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = pt[(int64_t)c * 4096 + threadIdx.x + 256 * e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], v[e]);
-  }
+  sum_slots<8, 4096>(pt, cnt, acc);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int idx = threadIdx.x + 256 * e, i = idx >> 6, jj = idx & 63;
@@ -424,15 +450,7 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
   const int cnt = sk_count(t, ut, U, G);
   const float* pt = P + (int64_t)t * cmax * 8192 + 32 * q * 64;
   float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int c = 0; c < cnt; ++c) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = pt[(int64_t)c * 8192 + threadIdx.x + 256 * e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __fadd_rn(acc[e], v[e]);
-  }
+  sum_slots<8, 8192>(pt, cnt, acc);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int idx = threadIdx.x + 256 * e, i = idx >> 6, jj = idx & 63;
@@ -453,42 +471,85 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restr
   }
 }
 
-// The backward pass's operand copies in one launch.  Blocks [0, b1): sT
-// [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r] (no
-// blocks when T is null); [b1, b2): BT [Rp, Np] = Bᵀ zero-padded; [b2, ...):
-// AT2 [K, 2Rp], AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r, else 0.
+// The backward pass's operand copies in one launch, each through 64 x 64
+// tiles transposed in LDS, so that every global load and store of a wave
+// covers whole rows of 64 consecutive 16-bit (or fp32) values.  Tile column
+// block jb0 of jb = ceil(Rp / 64) within each row block.  Blocks [0, b1):
+// sT [M, 2Rp] and its transpose sTT [2Rp, Mp] from a saved fp32 T [M, r]
+// (no blocks when T is null); [b1, b2): BT [Rp, Np] = Bᵀ zero-padded;
+// [b2, ...): AT2 [K, 2Rp], AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r,
+// else 0.  Lane l of the block handles column l & 63 of rows
+// 4i + (l >> 6), i = 0..15.
 template <bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ T, int64_t M, int64_t Mp,
                                                        int r, int64_t Rp, float scale, uint16_t* __restrict__ sT,
                                                        uint16_t* __restrict__ sTT, const uint16_t* __restrict__ B,
                                                        int64_t N, int64_t Np, uint16_t* __restrict__ BT,
                                                        const uint16_t* __restrict__ A, int64_t K,
-                                                       uint16_t* __restrict__ AT2, unsigned b1, unsigned b2) {
+                                                       uint16_t* __restrict__ AT2, unsigned b1, unsigned b2,
+                                                       unsigned jb) {
+  __shared__ uint32_t sh[64][65];  // sh[col][row] of the tile read in
   const unsigned b = blockIdx.x;
+  const int col = threadIdx.x & 63, row = threadIdx.x >> 6;
   if (b < b1) {
-    const int64_t idx = (int64_t)b * 256 + threadIdx.x;
-    if (idx >= Mp * Rp) return;
-    // m runs fastest inside blocks of 64 so that the transposed stores coalesce
-    const int64_t mblk = idx / (64 * Rp), rem = idx % (64 * Rp);
-    const int64_t j = rem / 64, m = mblk * 64 + rem % 64;
-    uint16_t hi = 0, lo = 0;
-    if (m < M) {
-      if (j < r) split_hilo16<F16>(__fmul_rn(scale, T[m * r + j]), hi, lo);
-      sT[m * 2 * Rp + j] = hi;
-      sT[m * 2 * Rp + Rp + j] = lo;
+    // rows m, columns j of T
+    const int64_t m0 = (int64_t)(b / jb) * 64, j = (int64_t)(b % jb) * 64 + col;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + 4 * i + row;
+      uint16_t hi = 0, lo = 0;
+      if (m < M && j < r) split_hilo16<F16>(__fmul_rn(scale, T[m * r + j]), hi, lo);
+      if (m < M && j < Rp) {
+        sT[m * 2 * Rp + j] = hi;
+        sT[m * 2 * Rp + Rp + j] = lo;
+      }
+      sh[col][4 * i + row] = (uint32_t)hi | ((uint32_t)lo << 16);
     }
-    sTT[j * Mp + m] = hi;
-    sTT[(Rp + j) * Mp + m] = lo;
+    __syncthreads();
+    const int64_t j0 = (int64_t)(b % jb) * 64, m = m0 + col;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t jj = j0 + 4 * i + row;
+      if (jj < Rp && m < Mp) {
+        const uint32_t v = sh[4 * i + row][col];
+        sTT[jj * Mp + m] = (uint16_t)(v & 0xffffu);
+        sTT[(Rp + jj) * Mp + m] = (uint16_t)(v >> 16);
+      }
+    }
   } else if (b < b2) {
-    const int64_t idx = (int64_t)(b - b1) * 256 + threadIdx.x;
-    if (idx >= Rp * Np) return;
-    const int64_t j = idx / Np, n = idx % Np;
-    BT[idx] = (j < r && n < N) ? B[n * r + j] : (uint16_t)0;
+    // rows n, columns j of B
+    const unsigned bb = b - b1;
+    const int64_t n0 = (int64_t)(bb / jb) * 64, j0 = (int64_t)(bb % jb) * 64;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t n = n0 + 4 * i + row, j = j0 + col;
+      sh[col][4 * i + row] = (n < N && j < r) ? (uint32_t)B[n * r + j] : 0u;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = j0 + 4 * i + row, n = n0 + col;
+      if (j < Rp && n < Np) BT[j * Np + n] = (uint16_t)sh[4 * i + row][col];
+    }
   } else {
-    const int64_t idx = (int64_t)(b - b2) * 256 + threadIdx.x;
-    if (idx >= K * 2 * Rp) return;
-    const int64_t k = idx / (2 * Rp), j = (idx % (2 * Rp)) % Rp;
-    AT2[idx] = j < r ? A[j * K + k] : (uint16_t)0;
+    // rows j, columns k of A
+    const unsigned bb = b - b2;
+    const int64_t k0 = (int64_t)(bb / jb) * 64, j0 = (int64_t)(bb % jb) * 64;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t j = j0 + 4 * i + row, k = k0 + col;
+      sh[col][4 * i + row] = (j < r && k < K) ? (uint32_t)A[j * K + k] : 0u;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t k = k0 + 4 * i + row, j = j0 + col;
+      if (k < K && j < Rp) {
+        const uint16_t v = (uint16_t)sh[4 * i + row][col];
+        AT2[k * 2 * Rp + j] = v;
+        AT2[k * 2 * Rp + Rp + j] = v;
+      }
+    }
   }
 }
 
@@ -545,7 +606,7 @@ hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int3
                                 float scale, float* T, uint16_t* out, uint16_t* outT, const uint16_t* B,
                                 int64_t N, uint16_t* B2, bool f16, hipStream_t st) {
   const uint32_t b0 = (uint32_t)(2 * p.tiles);
-  const unsigned grid = b0 + (B2 ? cdiv(N * 2 * Rp, 256) : 0u);
+  const unsigned grid = b0 + (B2 ? cdiv(N * 2 * Rp / 8, 256) : 0u);
   if (f16)
     rowred_finish_kernel<true><<<grid, 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, M, lora_mp(M), r, Rp, scale, T,
                                                      out, outT, B, N, B2, b0);
@@ -575,13 +636,14 @@ hipError_t launch_bwd_prep(const float* T, int64_t M, int32_t r, int64_t Rp, flo
                            uint16_t* sTT, const uint16_t* B, int64_t N, uint16_t* BT, const uint16_t* A,
                            int64_t K, uint16_t* AT2, bool f16, hipStream_t st) {
   const int64_t Mp = lora_mp(M), Np = round_up(N, 64);
-  const unsigned b1 = T ? cdiv(Mp * Rp, 256) : 0u;
-  const unsigned b2 = b1 + cdiv(Rp * Np, 256);
-  const unsigned b3 = b2 + cdiv(K * 2 * Rp, 256);
+  const unsigned jb = cdiv(Rp, 64);
+  const unsigned b1 = T ? cdiv(Mp, 64) * jb : 0u;
+  const unsigned b2 = b1 + cdiv(Np, 64) * jb;
+  const unsigned b3 = b2 + cdiv(K, 64) * jb;
   if (f16)
-    bwd_prep_kernel<true><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
+    bwd_prep_kernel<true><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2, jb);
   else
-    bwd_prep_kernel<false><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2);
+    bwd_prep_kernel<false><<<b3, 256, 0, st>>>(T, M, Mp, r, Rp, scale, sT, sTT, B, N, Np, BT, A, K, AT2, b1, b2, jb);
   return hipGetLastError();
 }
 

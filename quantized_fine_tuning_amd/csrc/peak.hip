@@ -6,6 +6,9 @@
 //                      matrix pipe never waits on a result), on every SIMD
 //                      of every compute unit: the bf16 dense MFMA rate the
 //                      chip sustains at the clock it runs at under that load.
+//                      The first lane of workgroup 0 reads the shader clock
+//                      counter and the constant-rate real-time counter before
+//                      and after its loop, which gives that clock.
 //   stream_copy_kernel a plain copy, 16 bytes per lane and access: the HBM
 //                      rate of a streaming read + write of known size, also
 //                      the calibration for the HBM byte counters.
@@ -16,11 +19,20 @@ namespace {
 
 __global__ __launch_bounds__(256) void mfma_peak_kernel(int64_t iters, float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
+  const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+  uint64_t c0 = 0, w0 = 0;
+  if (timer) {
+    c0 = clock64();
+    w0 = wall_clock64();
+  }
   u32x4_t a = {0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   u32x4_t b = {0x3c003c00u, 0x3c003c00u ^ (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
+  // distinct starting values: eight chains the compiler cannot merge (with
+  // equal operands and equal starts it treats them as one value and
+  // shuffles accumulator registers between the MFMAs)
   f32x4_t acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{(float)(lane + 64 * i), 0.f, 0.f, 0.f};
   for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = mfma_16x16x32(a, b, acc[i]);
@@ -29,6 +41,15 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int64_t iters, float* __
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
   if (s == 1234.5f) sink[blockIdx.x] = s;  // never in practice: keeps the MFMAs
+  if (timer) {
+    asm volatile("" : "+v"(s));  // the loop's results exist before the clocks are read
+    const uint64_t c1 = clock64(), w1 = wall_clock64();
+    uint64_t* const clk = reinterpret_cast<uint64_t*>(sink + kPeakWorkgroups);
+    clk[0] = c0;
+    clk[1] = c1;
+    clk[2] = w0;
+    clk[3] = w1;
+  }
 }
 
 // Four 16-byte loads in flight per lane before their stores.

@@ -18,12 +18,20 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const f32
   const int64_t stride = (int64_t)gridDim.x * kReduceThreads;
   for (int64_t i = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x; i < n4; i += stride) {
     f32x4_t a = __builtin_nontemporal_load(P + i);
-    for (int s = 1; s < splits; ++s) {
-      const f32x4_t b = __builtin_nontemporal_load(P + (int64_t)s * n4 + i);
-      a[0] = a[0] + b[0];
-      a[1] = a[1] + b[1];
-      a[2] = a[2] + b[2];
-      a[3] = a[3] + b[3];
+    // the loads of four partials are issued before their adds
+    for (int s = 1; s < splits; s += 4) {
+      f32x4_t b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (s + q < splits) b[q] = __builtin_nontemporal_load(P + (int64_t)(s + q) * n4 + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (s + q < splits) {
+          a[0] = a[0] + b[q][0];
+          a[1] = a[1] + b[q][1];
+          a[2] = a[2] + b[q][2];
+          a[3] = a[3] + b[q][3];
+        }
     }
     if (out16) {
       u32x2_t o;
