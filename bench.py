@@ -821,7 +821,7 @@ def main():
     ap.add_argument("--gemv-copies", type=int, default=64)
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="run a plain copy of MIB MiB first (for counter scaling)")
+                    help="run three plain copies of MIB MiB first and three last (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -859,6 +859,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline()
         cpu["breadth"] = run_cpu_breadth()
+    if args.copy_calibration:
+        copy_calibration(torch, q, args.copy_calibration)
     value = mlp["flops"] / (mlp["ms_per_step"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
