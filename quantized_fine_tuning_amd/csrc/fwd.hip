@@ -9,24 +9,28 @@
 //     [128wm, +128) and weight rows [64wn, +64) of the tile, 64
 //     v_mfma_f32_16x16x32_bf16 per 64-wide reduction step, operands read
 //     from LDS one MFMA group ahead.  Waves 8..11 (one per SIMD) produce the
-//     operands: each copies a quarter of the next step's X tile straight
-//     into LDS and dequantizes 64 of the tile's 256 weight rows of the next
-//     step into the shared bf16 tile Ŵ[n][k].  The producers' table
-//     arithmetic, lookups and copies overlap the MFMAs of the other two
-//     waves of their SIMD instead of interrupting a wave's own MFMA stream.
-//   * Dequantization goes through a per-row table: lane t writes the 16
-//     values RNE_bf16(fl32(q_j * c')) of its row t to LDS, and every code is
-//     one 2-byte table read (bit-identical to multiplying per element, since
-//     the value depends only on code and row).  For row group q lane l reads
-//     rows 8q + (l >> 3), k = 8(l & 7) + 0..7: the 8 lanes of one row hit its
-//     table, and the 4 rows of each half-wave (served in one LDS cycle) hit 4
-//     different groups of 8 of the 32 banks.  The lookups of one row group
-//     are in flight while the previous group's values are packed and stored.
+//     operands of the next step: each copies a quarter of the X tile
+//     straight into LDS and dequantizes 64 of the tile's 256 weight rows into
+//     the shared bf16 tile Ŵ[n][k].  Their arithmetic and copies overlap the
+//     MFMAs of the other two waves of their SIMD.
+//   * Dequantization in registers: lane l of producer p owns tile row
+//     64p + l.  Per step it builds that row's table of the 16 values
+//     RNE_bf16(fl32(q_j * c')) of the step's block (bit-identical to
+//     multiplying per element, since the value depends only on code and
+//     row), held as four byte planes (low bytes of values 0-3, 4-7, 8-11,
+//     12-15, likewise the high bytes), and decodes the row's 64 codes with
+//     byte permutes: four codes per permute pair, the code's low three bits
+//     selecting within 8 bytes and its top bit between the two halves; the
+//     low and high bytes are then interleaved into bf16 pairs and the row's
+//     eight 16-byte chunks stored.  No LDS lookups, no tables in LDS.
+//   * Each producer step first waits for the codes and constants it loaded a
+//     step earlier, then issues the X copy of the next step, then the loads
+//     of the step after (into the other of two register sets, so that no
+//     register a load in flight writes is copied), then decodes; at its end
+//     only the X copy must be complete.  (The X copy is the long-latency
+//     transfer; issued first it has the whole step to land.)
 //   * Tiles are stored with 16-byte chunks XOR-swizzled by row (xswz) so that
 //     MFMA operand reads of 8 rows cover the 32 LDS banks once.
-//   * The packed codes, e4m3 bytes and group scales of step s+2 are loaded
-//     while step s+1 is dequantized; codes go through LDS (each producer
-//     reads back only its own rows), constants stay in registers.
 //   * One barrier per step: after it the MFMA waves use X(s) and Ŵ(s) while
 //     the producers fill the other buffers with X(s+1) and Ŵ(s+1).
 //   * All operand reads are buffer loads whose resources end at the tensor's
@@ -75,9 +79,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                Codebook cb) {
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
-  // tables of the tile's weight rows (row r at 32(r % 8) + 256(r / 8)),
-  // double-buffered by step
-  __shared__ __attribute__((aligned(256))) char stab[2][TN * 32];
   int tmi, tni, sp;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, splits, tmi, tni, sp)) return;
 
@@ -99,57 +100,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // these buffers or return zeros; their results are never used.
   const rsrc_t rc = make_rsrc(W.codes + n0 * (K / 2), (N - n0) * (K / 2));
 
-  // Lookups of a row group (8 weight rows from tile row R, a multiple of 8):
-  // lane l = (dr, dc) = (l >> 3, l & 7) takes code dword dc of row R + dr
-  // (k = 8dc .. 8dc + 7 of the step) and looks each code up in its row's
-  // table, then stores the 8 bf16 as one 16-byte chunk.  The 8 lanes of a
-  // row hit its table, and the 4 rows of each half-wave (served in one LDS
-  // cycle) hit 4 different groups of 8 of the 32 banks.  The table of row
-  // R + dr starts at a 256-byte-aligned base + 256(R / 8) + 32dr, so a
-  // lookup address is that address with its low byte replaced by
-  // 32dr | 2*code; the low bytes of the 4 even (odd) codes of a dword are
-  // formed together, then each address is one byte permute.
-  const int dr = lane >> 3, dc = lane & 7;
-  const uint32_t dr32x4 = (uint32_t)dr * 0x20202020u;
-  auto load_code = [&](int R, int t) __attribute__((always_inline)) {
-    return buf_load4(rc, (uint32_t)(R + dr) * (uint32_t)(K / 2) + 4u * (uint32_t)dc, (uint32_t)(kfirst + t) * 32u);
-  };
-  auto lookup_group = [&](uint32_t w, const char* tabs, int R, uint32_t* v) __attribute__((always_inline)) {
-    const uint32_t tab = lds_offset(tabs) + 256u * (uint32_t)(R >> 3) + 32u * (uint32_t)dr;
-    const uint32_t we = ((w << 1) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j
-    const uint32_t wo = ((w >> 3) & 0x1E1E1E1Eu) | dr32x4;  // byte j: 2 * code 2j+1
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = lds_read_u16(__builtin_amdgcn_perm(tab, we, 0x07060500u | (uint32_t)j));
-      v[2 * j + 1] = lds_read_u16(__builtin_amdgcn_perm(tab, wo, 0x07060500u | (uint32_t)j));
-    }
-  };
-  // (the empty asm pins the wait for the lookups here: otherwise the values
-  // are packed, and so waited for, right after the lookups are issued)
-  auto store_group = [&](uint32_t* v, char* dst, int R) __attribute__((always_inline)) {
-    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
-                 "+v"(v[7]));
-    u32x4_t o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = v[2 * j] | (v[2 * j + 1] << 16);
-    *reinterpret_cast<u32x4_t*>(dst + xswz(R + dr, dc)) = o;
-  };
-  // NG row groups from R0 (8 rows apart), lookups of group q in flight while
-  // group q - 1 is packed and stored; issue(q) runs after group q's lookups.
-  auto dequant_rows = [&](auto NGc, int R0, const uint32_t* cw, int t, auto&& issue)
-      __attribute__((always_inline)) {
-    constexpr int NG = decltype(NGc)::value;
-    uint32_t lv[2][8];
-#pragma unroll
-    for (int q = 0; q <= NG; ++q) {
-      if (q < NG) {
-        lookup_group(cw[q], stab[t & 1], R0 + 8 * q, lv[q & 1]);
-        issue(q);
-        __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
-      }
-      if (q > 0) store_group(lv[(q - 1) & 1], sw[t & 1], R0 + 8 * (q - 1));
-    }
-  };
   auto no_issue = [](int) {};
 
   if (wave < kMfmaWaves) {
@@ -194,21 +144,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       }
     };
 
-    // This wave also dequantizes weight rows [16w, 16w + 16) of every step,
-    // after its MFMAs of the step before.
-    const int R0 = 16 * wave;
-    uint32_t cw[2];
-    cw[0] = load_code(R0, 0);
-    cw[1] = load_code(R0 + 8, 0);
-    __syncthreads();  // tables of steps 0 and 1 in place
-    dequant_rows(std::integral_constant<int, 2>(), R0, cw, 0, no_issue);
+    __syncthreads();  // (the producers' prologue)
     __syncthreads();  // step 0 in place
 #pragma unroll 1
     for (int s = 0; s + 1 < ksteps; ++s) {
-      cw[0] = load_code(R0, s + 1);
-      cw[1] = load_code(R0 + 8, s + 1);
       mfma_step(sxb(s & 1), sw[s & 1]);
-      dequant_rows(std::integral_constant<int, 2>(), R0, cw, s + 1, no_issue);
       __syncthreads();
     }
 #pragma unroll 1
@@ -262,8 +202,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   }
 
   // ------------------------------------------------------------ producers
-  // Producer p builds the tables of weight rows [64p, 64p + 64), dequantizes
-  // rows [128 + 32p, +32) and copies X rows [64p, +64) of every step.
+  // Producer p dequantizes weight rows [64p, 64p + 64) and copies X rows
+  // [64p, +64) of every step.
   const int p = wave - kMfmaWaves;
   const uint32_t kpr = (uint32_t)(K / kBlock);  // blocks per weight row
   const float mu = *W.mu;
@@ -299,10 +239,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
       buf_load_lds16(r, t + (64 * p + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
   };
 
-  // Table of row 64p + lane for step t: the dword holding its e4m3 byte and
-  // its group scale, loaded a step ahead; lane writes the 16 values
-  // RNE_bf16(fl32(q_j * c')) (bit-identical to multiplying per element,
-  // since the value depends only on code and row).
+  // Row trow = 64p + lane of the tile is this lane's: the dword holding its
+  // e4m3 byte and its group scale, its 32 bytes of codes per step.
   const int trow = 64 * p + lane;
   const uint32_t ve_me = (uint32_t)trow * kpr;
   const uint32_t blk_me = (uint32_t)(n0 + trow) * kpr;
@@ -313,66 +251,97 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     r.e = buf_load4(re, (ve_me + (uint32_t)(kfirst + t)) & ~3u, 0u);
     r.s = buf_load4(rs, ((blk_me + (uint32_t)(kfirst + t)) / kDqBlock) * 4u, 0u);
   };
-  const int tb_off = 32 * (lane & 7) + 256 * (8 * p + (lane >> 3));
-  auto build_table = [&](int t, const Consts& r) __attribute__((always_inline)) {
+  const uint32_t vrow = (uint32_t)trow * (uint32_t)(K / 2);
+  auto load_row = [&](u32x4_t* c, int t) __attribute__((always_inline)) {
+    c[0] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u);
+    c[1] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u + 16u);
+  };
+  auto row_table = [&](int t, const Consts& r, uint32_t* L, uint32_t* H) __attribute__((always_inline)) {
     const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)(kfirst + t)) & 3u))) & 0xffu;
     const float cp = decode_constant(e, __uint_as_float(r.s), mu);
-    u32x4_t t0, t1;
+    uint32_t d[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      t0[j] = pack16<F16>(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
-      t1[j] = pack16<F16>(__fmul_rn(cb.q[8 + 2 * j], cp), __fmul_rn(cb.q[9 + 2 * j], cp));
+    for (int j = 0; j < 8; ++j) d[j] = pack16<F16>(__fmul_rn(cb.q[2 * j], cp), __fmul_rn(cb.q[2 * j + 1], cp));
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      L[g] = __builtin_amdgcn_perm(d[2 * g + 1], d[2 * g], 0x06040200u);
+      H[g] = __builtin_amdgcn_perm(d[2 * g + 1], d[2 * g], 0x07050301u);
     }
-    char* const d = stab[t & 1] + tb_off;
-    *reinterpret_cast<u32x4_t*>(d) = t0;
-    *reinterpret_cast<u32x4_t*>(d + 16) = t1;
+  };
+  // T: a byte plane; the bytes of c are four codes (0..15)
+  auto look = [&](uint32_t c, const uint32_t* T) __attribute__((always_inline)) {
+    const uint32_t s7 = c & 0x07070707u;
+    const uint32_t sel = ((c >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(__builtin_amdgcn_perm(T[3], T[2], s7), __builtin_amdgcn_perm(T[1], T[0], s7), sel);
+  };
+  // eight codes (one dword: element 2b in the low nibble of byte b, 2b+1 in
+  // its high nibble) into four bf16 pairs in element order
+  auto decode8 = [&](uint32_t w, const uint32_t* L, const uint32_t* H, u32x4_t& o) __attribute__((always_inline)) {
+    const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t le = look(ev, L), he = look(ev, H), lo = look(od, L), ho = look(od, H);
+    const uint32_t E01 = __builtin_amdgcn_perm(he, le, 0x05010400u), E23 = __builtin_amdgcn_perm(he, le, 0x07030602u);
+    const uint32_t O01 = __builtin_amdgcn_perm(ho, lo, 0x05010400u), O23 = __builtin_amdgcn_perm(ho, lo, 0x07030602u);
+    o[0] = __builtin_amdgcn_perm(O01, E01, 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(O01, E01, 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(O23, E23, 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(O23, E23, 0x07060302u);
+  };
+  auto decode_row = [&](const u32x4_t* c, const uint32_t* L, const uint32_t* H, char* dst, auto&& issue)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4_t o;
+      decode8(c[j >> 2][j & 3], L, H, o);
+      *reinterpret_cast<u32x4_t*>(dst + xswz(trow, j)) = o;
+      issue(j);
+    }
   };
 
-  const int PR0 = 128 + 32 * p;
-  uint32_t cw[4], cwn[4];
+  u32x4_t cw[2], cwn[2];
   Consts cc, cn;
-  // prologue: X of step 0, tables of steps 0 and 1, lookups of step 0
+  // prologue: X of step 0, codes and constants of steps 0 and 1, step 0 decoded
   {
     Consts c0;
+    u32x4_t k0[2];
     copy_x(sx0, 0);
     load_consts(c0, 0);
-    load_consts(cn, 1);
-    load_consts(cc, 2);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      cw[q] = load_code(PR0 + 8 * q, 0);
-      cwn[q] = load_code(PR0 + 8 * q, 1);
-    }
-    build_table(0, c0);
-    build_table(1, cn);
+    load_consts(cc, 1);
+    load_row(k0, 0);
+    load_row(cw, 1);
+    uint32_t L[4], H[4];
+    row_table(0, c0, L, H);
+    decode_row(k0, L, H, sw[0], no_issue);
   }
-  __syncthreads();  // tables of steps 0 and 1 in place
-  dequant_rows(std::integral_constant<int, 4>(), PR0, cw, 0, no_issue);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) cw[q] = cwn[q];
+  __syncthreads();
   wait_vmem();
   __syncthreads();  // step 0 in place
 
-  // Weight steps 0 .. ksteps-2: load the codes of step s+2 and constants of
-  // step s+3, build the tables of step s+2 (that buffer was last read in the
-  // previous iteration), dequantize this wave's rows of step s+1 while
-  // copying X of step s+1 into the other X buffer.
-#pragma unroll 1
-  for (int s = 0; s + 1 < ksteps; ++s) {
-    char* const xn = sxb((s + 1) & 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cwn[q] = load_code(PR0 + 8 * q, s + 2);
-    load_consts(cn, s + 3);
-    build_table(s + 2, cc);
-    dequant_rows(std::integral_constant<int, 4>(), PR0, cw, s + 1, [&](int q) {
-      copy_x_part(xn, s + 1, 2 * q);
-      copy_x_part(xn, s + 1, 2 * q + 1);
-    });
-#pragma unroll
-    for (int q = 0; q < 4; ++q) cw[q] = cwn[q];
-    cc = cn;
-    wait_vmem();
+  // Weight steps 0 .. ksteps-2, one step: the table of step s+1 from constants loaded a step earlier
+  // (their first use, where the compiler waits for them), then the X copy of
+  // step s+1 and the loads of step s+2 (into the other register set: no
+  // copies of registers that loads in flight are writing), then the decode;
+  // at the end the X copy must be done while the 4 loads of step s+2 may
+  // still be in flight.
+  auto pstep = [&](int s, const u32x4_t* cur, u32x4_t* nxt, const Consts& ccur, Consts& cnxt)
+      __attribute__((always_inline)) {
+    uint32_t L[4], H[4];
+    row_table(s + 1, ccur, L, H);
+    // the table and this step's codes exist before the copies are issued
+    // (the compiler's waits for them would otherwise also wait for copies
+    // issued before them, which it does not track)
+    asm volatile("" : "+v"(L[0]), "+v"(L[1]), "+v"(L[2]), "+v"(L[3]), "+v"(H[0]), "+v"(H[1]), "+v"(H[2]),
+                 "+v"(H[3]) : "v"(cur[0]), "v"(cur[1]));
+    copy_x(sxb((s + 1) & 1), s + 1);
+    load_row(nxt, s + 2);
+    load_consts(cnxt, s + 2);
+    decode_row(cur, L, H, sw[(s + 1) & 1], no_issue);
+    wait_vmem_le<4>();
     __syncthreads();
+  };
+#pragma unroll 1
+  for (int s = 0; s + 1 < ksteps; s += 2) {
+    pstep(s, cw, cwn, cc, cn);
+    if (s + 2 < ksteps) pstep(s + 1, cwn, cw, cn, cc);
   }
   // last weight step: copy LoRA step 0 (sT and B2 tiles) into the other
   // buffers; then the LoRA steps

@@ -114,57 +114,56 @@ def test_fwd_x_copy_lands_on_the_swizzled_tile(p):
             assert (64 * p + 8 * c) * 128 + 16 * lane == xswz(row, logical)
 
 
-def fwd_table_base(row):
-    return 32 * (row % 8) + 256 * (row // 8)
+def fwd_row_table(vals):
+    """The producer lane's byte planes: L[g] = low bytes of values 4g..4g+3,
+    H[g] the high bytes, from the packed pairs d[j] = v[2j] | v[2j+1] << 16."""
+    d = [vals[2 * j] | (vals[2 * j + 1] << 16) for j in range(8)]
+    L = [perm(d[2 * g + 1], d[2 * g], 0x06040200) for g in range(4)]
+    H = [perm(d[2 * g + 1], d[2 * g], 0x07050301) for g in range(4)]
+    return L, H
 
 
-def test_fwd_tables_written_where_the_lookups_read_them():
-    written = {}
-    for p in range(4):
-        for lane in range(64):
-            off = 32 * (lane & 7) + 256 * (8 * p + (lane >> 3))
-            written[64 * p + lane] = off
-    assert sorted(written.values()) == list(range(0, 256 * 32, 32))
-    for R in range(0, 256, 8):
-        for dr in range(8):
-            assert 256 * (R >> 3) + 32 * dr == written[R + dr] == fwd_table_base(R + dr)
+def fwd_look(c, T):
+    s7 = c & 0x07070707
+    sel = ((c >> 1) & 0x04040404) | 0x03020100
+    return perm(perm(T[3], T[2], s7), perm(T[1], T[0], s7), sel)
 
 
-def test_fwd_lookup_address_by_byte_permute():
-    rnd = random.Random(7)
-    stab = 0x1A00  # any 256-byte-aligned LDS address
-    for _ in range(200):
-        w = rnd.getrandbits(32)
-        R = 8 * rnd.randrange(32)
-        for dr in range(8):
-            tab = stab + 256 * (R >> 3) + 32 * dr
-            dr32x4 = dr * 0x20202020
-            we = ((w << 1) & 0x1E1E1E1E) | dr32x4
-            wo = ((w >> 3) & 0x1E1E1E1E) | dr32x4
-            for j in range(4):
-                code_e = (w >> (8 * j)) & 15
-                code_o = (w >> (8 * j + 4)) & 15
-                assert perm(tab, we, 0x07060500 | j) == tab + 2 * code_e
-                assert perm(tab, wo, 0x07060500 | j) == tab + 2 * code_o
+def fwd_decode8(w, L, H):
+    ev, od = w & 0x0F0F0F0F, (w >> 4) & 0x0F0F0F0F
+    le, he, lo, ho = fwd_look(ev, L), fwd_look(ev, H), fwd_look(od, L), fwd_look(od, H)
+    e01, e23 = perm(he, le, 0x05010400), perm(he, le, 0x07030602)
+    o01, o23 = perm(ho, lo, 0x05010400), perm(ho, lo, 0x07030602)
+    return [perm(o01, e01, 0x05040100), perm(o01, e01, 0x07060302),
+            perm(o23, e23, 0x05040100), perm(o23, e23, 0x07060302)]
 
 
-def test_fwd_lookups_are_conflict_free_for_any_codes():
-    rnd = random.Random(3)
-    for _ in range(200):
-        R = 8 * rnd.randrange(32)
-        codes = [rnd.randrange(16) for _ in range(64)]
-        for half in range(2):
-            addrs = []
-            for lane in range(32 * half, 32 * half + 32):
-                dr = lane >> 3
-                addrs.append(fwd_table_base(R + dr) + 2 * codes[lane])
-            assert conflict_free_small(addrs)
+def check_decode(vals, w):
+    L, H = fwd_row_table(vals)
+    out = fwd_decode8(w, L, H)
+    codes = [(w >> (4 * k)) & 15 for k in range(8)]  # element 2b: low nibble of byte b
+    for i in range(4):
+        assert out[i] == vals[codes[2 * i]] | (vals[codes[2 * i + 1]] << 16), (hex(w), i)
 
 
-def test_fwd_w_tile_stores_cover_their_rows():
-    for R in range(0, 256, 8):
-        addrs = [xswz(R + (l >> 3), l & 7) for l in range(64)]
-        assert sorted(addrs) == list(range(R * 128, (R + 8) * 128, 16))
+def test_fwd_register_decode_gives_the_table_values():
+    # every code in every one of the 8 positions of a dword (the other seven
+    # random), distinct random 16-bit table values, and all-equal dwords
+    rnd = random.Random(11)
+    for _ in range(40):
+        vals = [rnd.getrandbits(16) for _ in range(16)]
+        for pos in range(8):
+            for code in range(16):
+                w = rnd.getrandbits(32) & ~(15 << (4 * pos)) | (code << (4 * pos))
+                check_decode(vals, w)
+        for code in range(16):
+            check_decode(vals, code * 0x11111111)
+
+
+def test_fwd_producer_stores_cover_the_w_tile():
+    # lane l of producer p stores the 8 chunks of tile row 64p + l
+    addrs = sorted(xswz(64 * p + lane, j) for p in range(4) for lane in range(64) for j in range(8))
+    assert addrs == list(range(0, 256 * 128, 16))
 
 
 # ------------------------------------------------------------------- dx.hip
