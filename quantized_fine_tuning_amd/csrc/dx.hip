@@ -416,22 +416,26 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   wait_vmem();
   __syncthreads();  // step 0 in place
 
-  // Reduction steps 0 .. nsteps-2: load the codes of step s+2 and the
-  // constants of step s+3, build the tables of step s+2 (that buffer was
-  // last read in the previous iteration), dequantize slice 2p + 1 of step
-  // s+1 while copying dY of step s+1, then store the codes of step s+2.
+  // Reduction steps 0 .. nsteps-2: build the tables of step s+2 (that
+  // buffer was last read in the previous iteration; the constants were
+  // loaded then), then issue the copy of dY of step s+1 (first, so that it
+  // has the whole step to land) and the loads of the codes of step s+2 and
+  // the constants of step s+3, dequantize slice 2p + 1 of step s+1, then
+  // store the codes of step s+2.  (The empty asm keeps the table's
+  // arithmetic, and the compiler's wait for its constants, ahead of the
+  // copies: the compiler does not track those, and a wait it places after
+  // them would also wait for them.)
   // Weight data past the last step may be loaded: its reads stay inside the
   // buffers or return zeros, and it is not used.
 #pragma unroll 1
   for (int s = 0; s + 1 < nsteps; ++s) {
     char* const yn = sab((s + 1) & 1);
+    build_table(s + 2, cc);
+    asm volatile("" ::: "memory");
+    copy_y(yn, s + 1);
     load_codes(cn, s + 2);
     load_consts(cnx, s + 3);
-    build_table(s + 2, cc);
-    dequant_slice(std::true_type(), s + 1, 2 * p + 1, read_codes(s + 1, 2 * p + 1), [&](int h) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) copy_y_part(yn, s + 1, 4 * h + c);
-    });
+    dequant_slice(std::true_type(), s + 1, 2 * p + 1, read_codes(s + 1, 2 * p + 1), no_issue);
     store_codes(s + 2, cn);
     cc = cnx;
     wait_vmem();
