@@ -85,8 +85,11 @@ struct SkPlan {
 };
 // T = X·Aᵀ, U = dY·B: reduction over Kred for M rows, 64x64 tiles
 SkPlan rowred_plan(int64_t M, int64_t Kred, int64_t Rp);
-// dA, dB: reduction over Mred for Pn columns, 128x64 tiles
-SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp);
+// dA, dB: reduction over Mred for Pn columns, 128x64 tiles, on at most
+// gmax workgroups.  The two run in one launch: dA on colred_split(K, N, Rp)
+// of the 256 workgroups, dB on the rest.
+SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp, uint32_t gmax);
+uint32_t colred_split(int64_t K, int64_t N, int64_t Rp);
 size_t rowred_partial_bytes(const SkPlan& p);
 size_t colred_partial_bytes(const SkPlan& p);
 // Columns of the transposed bf16 splits [2Rp, Mp]: M rounded up to 64.
@@ -101,11 +104,28 @@ hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int3
                                 float scale, float* T, uint16_t* out, uint16_t* outT, const uint16_t* B,
                                 int64_t N, uint16_t* B2, bool f16, hipStream_t st);
 // Partial tiles of Σ_m L[m][p]·(S[j][m] + S[Rp + j][m]).
-hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, bool f16, hipStream_t st);
+struct ColredJob {  // one adapter gradient's reduction (see lora.hip)
+  const uint16_t* L;
+  int64_t Mred, ldl;
+  const uint16_t* S;
+  int64_t lds, Rp;
+  int jt;
+  uint32_t ut, U, G;
+  int cmax;
+  float* P;
+};
+hipError_t launch_colred(const ColredJob& a, const ColredJob& b, bool f16, hipStream_t st);
 // Sums them → out [Pn, r], or out [r, Pn] when transposed.
-hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
-                                float* out, hipStream_t st);
+struct ColredFinishJob {
+  const float* P;
+  int jt;
+  uint32_t ut, U, G;
+  int cmax;
+  int64_t Pn, tiles;
+  int transpose;
+  float* out;
+};
+hipError_t launch_colred_finish(const ColredFinishJob& a, const ColredFinishJob& b, int32_t r, hipStream_t st);
 // The backward pass's operand copies, one launch: if T is non-null, sT
 // [M, 2Rp] and sTT [2Rp, Mp] from the saved T; BT [Rp, round_up(N, 64)] =
 // Bᵀ zero-padded; AT2 [K, 2Rp] = [Aᵀ | Aᵀ] zero-padded.

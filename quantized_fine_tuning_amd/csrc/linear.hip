@@ -55,8 +55,9 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M > 0) {
     L.pT = rowred_plan(M, K, Rp);
     L.pU = rowred_plan(M, N, Rp);
-    L.pA = colred_plan(M, K, Rp);
-    L.pB = colred_plan(M, N, Rp);
+    const uint32_t ga = colred_split(K, N, Rp);
+    L.pA = colred_plan(M, K, Rp, ga);
+    L.pB = colred_plan(M, N, Rp, kSkWorkgroups - ga);
   }
   size_t off = 0;
   L.off_sT = off;
@@ -78,8 +79,8 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M > 0) {
     p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pT), 256));
     p = std::max<size_t>(p, round_up(rowred_partial_bytes(L.pU), 256));
-    p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pA), 256));
-    p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pB), 256));
+    // dA's and dB's partial tiles side by side (one launch)
+    p = std::max<size_t>(p, round_up(colred_partial_bytes(L.pA), 256) + round_up(colred_partial_bytes(L.pB), 256));
     L.splits = dx_gemm_splits(M, N, K, SIZE_MAX);
     if (L.splits > 1) p = std::max<size_t>(p, round_up((size_t)L.splits * M * K * 4, 256));
   }
@@ -102,10 +103,10 @@ size_t rowred_bytes_bound(int64_t M, int64_t Kred, int64_t Rp) {
   if (tiles >= (int64_t)kSkWorkgroups) return round_up(tiles * 2 * 64 * 64 * 4, 256);
   return round_up(rowred_partial_bytes(rowred_plan(M, Kred, Rp)), 256);
 }
-size_t colred_bytes_bound(int64_t M, int64_t Pn, int64_t Rp) {
+size_t colred_bytes_bound(int64_t M, int64_t Pn, int64_t Rp, uint32_t gmax) {
   const int64_t tiles = ((Pn + 127) / 128) * ((Rp + 63) / 64);
-  if (tiles >= (int64_t)kSkWorkgroups) return round_up(tiles * 2 * 128 * 64 * 4, 256);
-  return round_up(colred_partial_bytes(colred_plan(M, Pn, Rp)), 256);
+  if (tiles >= (int64_t)gmax) return round_up(tiles * 2 * 128 * 64 * 4, 256);
+  return round_up(colred_partial_bytes(colred_plan(M, Pn, Rp, gmax)), 256);
 }
 // The GEMMs' split partials over M in [1, M_max] (the forward GEMM runs
 // from 17 tokens on, the dX GEMM from 1): the split count depends on M only
@@ -140,11 +141,12 @@ size_t bwd_ws_bytes_max(int64_t M_max, int64_t N, int64_t K, int32_t r) {
   const BwdLayout L = bwd_layout(M_max, N, K, r);
   if (M_max <= 0) return L.total;
   const int64_t Rp = lora_rp(r);
+  const uint32_t ga = colred_split(K, N, Rp);
   size_t p = splitk_bytes_max(M_max, N, K, false);
   for (int64_t M = 64; M < M_max + 64; M += 64) {
     const int64_t m = std::min(M, M_max);
-    p = std::max({p, rowred_bytes_bound(m, K, Rp), rowred_bytes_bound(m, N, Rp), colred_bytes_bound(m, K, Rp),
-                  colred_bytes_bound(m, N, Rp)});
+    p = std::max({p, rowred_bytes_bound(m, K, Rp), rowred_bytes_bound(m, N, Rp),
+                  colred_bytes_bound(m, K, Rp, ga) + colred_bytes_bound(m, N, Rp, kSkWorkgroups - ga)});
   }
   return L.off_P + p;
 }
@@ -205,14 +207,17 @@ hipError_t launch_backward(const Nf4View& W, const uint16_t* X, const uint16_t* 
   e = launch_dx_gemm(W, dY, M, sU, AT2, Rp, dX, dx16, L.splits, P, f16, st);
   if (e == hipSuccess && L.splits > 1) e = launch_splitk_reduce(P, L.splits, M * K, dX, dx16, f16, st);
   if (e != hipSuccess) return e;
-  // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU)
-  e = launch_colred(X, M, K, K, sUT, Mp, Rp, L.pA, P, f16, st);
-  if (e == hipSuccess) e = launch_colred_finish(P, L.pA, K, r, true, dA, st);
+  // dA[j][k] = Σ_m (sU_hi + sU_lo)[m][j] · X[m][k]   (s is inside sU) and
+  // dB[n][j] = Σ_m dY[m][n] · (sT_hi + sT_lo)[m][j], in one launch, their
+  // partial tiles side by side
+  float* PB = P + round_up(colred_partial_bytes(L.pA), 256) / 4;
+  const ColredJob ja{X, M, K, sUT, Mp, Rp, L.pA.jt, L.pA.ut, L.pA.U, L.pA.G, L.pA.cmax, P};
+  const ColredJob jb{dY, M, N, sTT, Mp, Rp, L.pB.jt, L.pB.ut, L.pB.U, L.pB.G, L.pB.cmax, PB};
+  e = launch_colred(ja, jb, f16, st);
   if (e != hipSuccess) return e;
-  // dB[n][j] = Σ_m dY[m][n] · (sT_hi + sT_lo)[m][j]
-  e = launch_colred(dY, M, N, N, sTT, Mp, Rp, L.pB, P, f16, st);
-  if (e == hipSuccess) e = launch_colred_finish(P, L.pB, N, r, false, dB, st);
-  return e;
+  const ColredFinishJob fa{P, L.pA.jt, L.pA.ut, L.pA.U, L.pA.G, L.pA.cmax, K, L.pA.tiles, 1, dA};
+  const ColredFinishJob fb{PB, L.pB.jt, L.pB.ut, L.pB.U, L.pB.G, L.pB.cmax, N, L.pB.tiles, 0, dB};
+  return launch_colred_finish(fa, fb, r, st);
 }
 
 }  // namespace qnf4

@@ -211,22 +211,28 @@ __device__ __forceinline__ int lswz(int row, int chunk) {
   return row * 256 + ((chunk ^ (((row >> 3) & 7) << 1)) << 4);
 }
 
+// Both adapter gradients run in one launch: workgroups [0, g1) take job j0
+// (dA), the rest job j1 (dB), each job with its own stream-K plan over its
+// own workgroups.
 template <bool F16>
-__global__ __launch_bounds__(256) void colred_kernel(const uint16_t* __restrict__ L, int64_t Mred,
-                                                     int64_t Pn, int64_t ldl,
-                                                     const uint16_t* __restrict__ S, int64_t lds,
-                                                     int64_t Rp, int jt, uint32_t ut, uint32_t U, int cmax,
-                                                     float* __restrict__ P) {
+__global__ __launch_bounds__(256) void colred_kernel(ColredJob j0, ColredJob j1, uint32_t g1) {
   constexpr int NS = kColRing;
+  const bool second = blockIdx.x >= g1;
+  const ColredJob J = second ? j1 : j0;
+  const uint16_t* __restrict__ L = J.L;
+  const uint16_t* __restrict__ S = J.S;
+  float* __restrict__ P = J.P;
+  const int64_t Mred = J.Mred, ldl = J.ldl, lds = J.lds, Rp = J.Rp;
+  const int jt = J.jt, cmax = J.cmax;
+  const uint32_t ut = J.ut, U = J.U;
   __shared__ __attribute__((aligned(1024))) char l0[16384], l1[16384], l2[16384], l3[16384], l4[16384];
   __shared__ __attribute__((aligned(1024))) char s0[16384], s1[16384], s2[16384], s3[16384], s4[16384];
   char* const ls[NS] = {l0, l1, l2, l3, l4};
   char* const ss[NS] = {s0, s1, s2, s3, s4};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
-  const uint32_t G = gridDim.x, g = blockIdx.x;
+  const uint32_t G = J.G, g = second ? blockIdx.x - g1 : blockIdx.x;
   const uint32_t u0 = sk_begin(g, U, G), u1 = sk_begin(g + 1, U, G);
-  (void)Pn;
 
   // L tile: wave w copies rows 16w + 4c + (lane >> 4), c = 0..3; lane i fills
   // physical chunk i & 15.  S tile: wave w copies rows 32w + 8c + (lane >> 3)
@@ -440,12 +446,19 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
 
 // colred tiles (128 p x 64 j) → out [Pn, r] (out[p][j], transpose == 0) or
 // out [r, Pn] (out[j][p], transpose == 1).  One workgroup of 256 per 32
-// rows p of a tile.
-__global__ __launch_bounds__(256) void colred_finish_kernel(const float* __restrict__ P, int jt, uint32_t ut,
-                                                            uint32_t U, uint32_t G, int cmax, int64_t Pn,
-                                                            int r, int transpose, float* __restrict__ out) {
+// rows p of a tile; workgroups [0, b1) finish job f0, the rest job f1.
+__global__ __launch_bounds__(256) void colred_finish_kernel(ColredFinishJob f0, ColredFinishJob f1, uint32_t b1,
+                                                            int r) {
   __shared__ float sh[64][33];
-  const uint32_t t = blockIdx.x >> 2, q = blockIdx.x & 3;
+  const bool second = blockIdx.x >= b1;
+  const ColredFinishJob F = second ? f1 : f0;
+  const float* __restrict__ P = F.P;
+  float* __restrict__ out = F.out;
+  const int jt = F.jt, cmax = F.cmax, transpose = F.transpose;
+  const uint32_t ut = F.ut, U = F.U, G = F.G;
+  const int64_t Pn = F.Pn;
+  const uint32_t bid = second ? blockIdx.x - b1 : blockIdx.x;
+  const uint32_t t = bid >> 2, q = bid & 3;
   const int64_t p0 = (int64_t)(t / jt) * 128 + 32 * q, j0 = (int64_t)(t % jt) * 64;
   const int cnt = sk_count(t, ut, U, G);
   const float* pt = P + (int64_t)t * cmax * 8192 + 32 * q * 64;
@@ -564,13 +577,13 @@ unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 }  // namespace
 
 // Stream-K plan of a product with `tiles` output tiles of `ns` stages each.
-SkPlan sk_plan(int64_t tiles, int64_t ns, int jt, int ring) {
+SkPlan sk_plan(int64_t tiles, int64_t ns, int jt, int ring, uint32_t gmax) {
   SkPlan p{};
   p.jt = jt;
   p.tiles = tiles;
   p.ut = (uint32_t)std::max<int64_t>(1, (ns + ring - 1) / ring);
   p.U = (uint32_t)(tiles * p.ut);
-  p.G = std::min<uint32_t>(p.U, kSkWorkgroups);
+  p.G = std::min<uint32_t>(p.U, gmax);
   p.cmax = 1;
   for (int64_t t = 0; t < tiles; ++t) {
     const int c = (int)(sk_owner((uint32_t)((t + 1) * p.ut - 1), p.U, p.G) -
@@ -582,11 +595,19 @@ SkPlan sk_plan(int64_t tiles, int64_t ns, int jt, int ring) {
 
 SkPlan rowred_plan(int64_t M, int64_t Kred, int64_t Rp) {
   const int jt = (int)cdiv(Rp, 64);
-  return sk_plan((int64_t)cdiv(M, 64) * jt, cdiv(Kred, ST), jt, kRowRing);
+  return sk_plan((int64_t)cdiv(M, 64) * jt, cdiv(Kred, ST), jt, kRowRing, kSkWorkgroups);
 }
-SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp) {
+int64_t colred_tiles(int64_t Pn, int64_t Rp) { return (int64_t)cdiv(Pn, 128) * cdiv(Rp, 64); }
+SkPlan colred_plan(int64_t Mred, int64_t Pn, int64_t Rp, uint32_t gmax) {
   const int jt = (int)cdiv(Rp, 64);
-  return sk_plan((int64_t)cdiv(Pn, 128) * jt, cdiv(Mred, ST), jt, kColRing);
+  return sk_plan(colred_tiles(Pn, Rp), cdiv(Mred, ST), jt, kColRing, gmax);
+}
+uint32_t colred_split(int64_t K, int64_t N, int64_t Rp) {
+  // both products reduce over the same tokens, so their units are in the
+  // ratio of their tiles, whatever M
+  const int64_t ta = colred_tiles(K, Rp), tb = colred_tiles(N, Rp);
+  const int64_t ga = (2 * (int64_t)kSkWorkgroups * ta + (ta + tb)) / (2 * (ta + tb));
+  return (uint32_t)std::min<int64_t>(kSkWorkgroups - 1, std::max<int64_t>(1, ga));
 }
 size_t rowred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 64 * 64 * 4; }
 size_t colred_partial_bytes(const SkPlan& p) { return (size_t)p.tiles * p.cmax * 128 * 64 * 4; }
@@ -616,19 +637,18 @@ hipError_t launch_rowred_finish(const float* P, const SkPlan& p, int64_t M, int3
   return hipGetLastError();
 }
 
-hipError_t launch_colred(const uint16_t* L, int64_t Mred, int64_t Pn, int64_t ldl, const uint16_t* S,
-                         int64_t lds, int64_t Rp, const SkPlan& p, float* P, bool f16, hipStream_t st) {
+hipError_t launch_colred(const ColredJob& a, const ColredJob& b, bool f16, hipStream_t st) {
+  const unsigned grid = a.G + b.G;
   if (f16)
-    colred_kernel<true><<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
+    colred_kernel<true><<<grid, 256, 0, st>>>(a, b, a.G);
   else
-    colred_kernel<false><<<p.G, 256, 0, st>>>(L, Mred, Pn, ldl, S, lds, Rp, p.jt, p.ut, p.U, p.cmax, P);
+    colred_kernel<false><<<grid, 256, 0, st>>>(a, b, a.G);
   return hipGetLastError();
 }
 
-hipError_t launch_colred_finish(const float* P, const SkPlan& p, int64_t Pn, int32_t r, bool transpose,
-                                float* out, hipStream_t st) {
-  colred_finish_kernel<<<(unsigned)(4 * p.tiles), 256, 0, st>>>(P, p.jt, p.ut, p.U, p.G, p.cmax, Pn, r,
-                                                          transpose ? 1 : 0, out);
+hipError_t launch_colred_finish(const ColredFinishJob& a, const ColredFinishJob& b, int32_t r, hipStream_t st) {
+  const unsigned b1 = (unsigned)(4 * a.tiles), grid = b1 + (unsigned)(4 * b.tiles);
+  colred_finish_kernel<<<grid, 256, 0, st>>>(a, b, b1, r);
   return hipGetLastError();
 }
 
