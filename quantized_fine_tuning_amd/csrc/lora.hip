@@ -361,10 +361,12 @@ __device__ __forceinline__ void sum_slots(const float* __restrict__ pt, int cnt,
   for (int c = 0; c < cnt; c += 4) {
     float v[4][E];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      // an existing slot whatever i, so that the loads are unconditional
+      const int ci = c + i < cnt ? c + i : cnt - 1;
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        v[i][e] = c + i < cnt ? pt[(int64_t)(c + i) * SLOT + threadIdx.x + 256 * e] : 0.0f;
+      for (int e = 0; e < E; ++e) v[i][e] = pt[(int64_t)ci * SLOT + threadIdx.x + 256 * e];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -401,7 +403,8 @@ __global__ __launch_bounds__(256) void rowred_finish_kernel(const float* __restr
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t jj = jc + (uint32_t)e, j = jj >= (uint32_t)Rp ? jj - (uint32_t)Rp : jj;
-      w[e] = j < (uint32_t)r ? (uint32_t)br[j] : 0u;
+      w[e] = br[j < (uint32_t)r ? j : 0u];  // unconditional: the 8 loads in flight together
+      if (j >= (uint32_t)r) w[e] = 0u;
     }
     u32x4_t o;
 #pragma unroll
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(256) void colred_finish_kernel(ColredFinishJob f0, 
 // (no blocks when T is null); [b1, b2): BT [Rp, Np] = Bᵀ zero-padded;
 // [b2, ...): AT2 [K, 2Rp], AT2[k][j] = A[j mod Rp][k] for (j mod Rp) < r,
 // else 0.  Lane l of the block handles column l & 63 of rows
-// 4i + (l >> 6), i = 0..15.
+// 4i + (l >> 6), i = 0..15, the loads of all 16 rows issued together.
 template <bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ T, int64_t M, int64_t Mp,
                                                        int r, int64_t Rp, float scale, uint16_t* __restrict__ sT,
@@ -507,11 +510,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   if (b < b1) {
     // rows m, columns j of T
     const int64_t m0 = (int64_t)(b / jb) * 64, j = (int64_t)(b % jb) * 64 + col;
-#pragma unroll 4
+    float tv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + 4 * i + row;
+      const bool ok = m < M && j < r;
+      tv[i] = T[ok ? m * r + j : 0];  // unconditional: all 16 loads in flight
+      if (!ok) tv[i] = 0.0f;
+    }
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t m = m0 + 4 * i + row;
       uint16_t hi = 0, lo = 0;
-      if (m < M && j < r) split_hilo16<F16>(__fmul_rn(scale, T[m * r + j]), hi, lo);
+      if (m < M && j < r) split_hilo16<F16>(__fmul_rn(scale, tv[i]), hi, lo);
       if (m < M && j < Rp) {
         sT[m * 2 * Rp + j] = hi;
         sT[m * 2 * Rp + Rp + j] = lo;
@@ -520,7 +531,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     }
     __syncthreads();
     const int64_t j0 = (int64_t)(b % jb) * 64, m = m0 + col;
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t jj = j0 + 4 * i + row;
       if (jj < Rp && m < Mp) {
@@ -533,13 +544,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     // rows n, columns j of B
     const unsigned bb = b - b1;
     const int64_t n0 = (int64_t)(bb / jb) * 64, j0 = (int64_t)(bb % jb) * 64;
-#pragma unroll 4
+    uint32_t v[16];
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t n = n0 + 4 * i + row, j = j0 + col;
-      sh[col][4 * i + row] = (n < N && j < r) ? (uint32_t)B[n * r + j] : 0u;
+      const bool ok = n < N && j < r;
+      v[i] = B[ok ? n * r + j : 0];
+      if (!ok) v[i] = 0u;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sh[col][4 * i + row] = v[i];
     __syncthreads();
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t j = j0 + 4 * i + row, n = n0 + col;
       if (j < Rp && n < Np) BT[j * Np + n] = (uint16_t)sh[4 * i + row][col];
@@ -548,13 +564,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     // rows j, columns k of A
     const unsigned bb = b - b2;
     const int64_t k0 = (int64_t)(bb / jb) * 64, j0 = (int64_t)(bb % jb) * 64;
-#pragma unroll 4
+    uint32_t v[16];
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t j = j0 + 4 * i + row, k = k0 + col;
-      sh[col][4 * i + row] = (j < r && k < K) ? (uint32_t)A[j * K + k] : 0u;
+      const bool ok = j < r && k < K;
+      v[i] = A[ok ? j * K + k : 0];
+      if (!ok) v[i] = 0u;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sh[col][4 * i + row] = v[i];
     __syncthreads();
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int64_t k = k0 + 4 * i + row, j = j0 + col;
       if (k < K && j < Rp) {

@@ -22,8 +22,11 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const f32
     for (int s = 1; s < splits; s += 4) {
       f32x4_t b[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (s + q < splits) b[q] = __builtin_nontemporal_load(P + (int64_t)(s + q) * n4 + i);
+      for (int q = 0; q < 4; ++q) {
+        // an existing partial whatever q, so that the loads are unconditional
+        const int sq = s + q < splits ? s + q : splits - 1;
+        b[q] = __builtin_nontemporal_load(P + (int64_t)sq * n4 + i);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (s + q < splits) {
