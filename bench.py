@@ -370,6 +370,7 @@ def run_m_sweep(torch, q, args):
         fl = linear_flops(M, N, K, r)
         out[f"M{M}"] = {"fwd_ms": round(f_ms, 4), "fwd_bwd_ms": round(fb_ms, 4),
                         "fwd_bwd_TFLOP/s": round(fl / (fb_ms * 1e-3) / 1e12, 2),
+                        "fwd_bwd_frac_of_peak": round(fl / (fb_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                         "path": "dequant-GEMV" if M <= 16 else "dequant-in-tile GEMM"}
         log(f"[bench] gate M={M}: fwd {f_ms * 1e3:.1f} us, fwd+bwd {fb_ms * 1e3:.1f} us")
     return out
