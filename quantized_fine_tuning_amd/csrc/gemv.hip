@@ -25,12 +25,18 @@
 //                           combined in a fixed order, one thread per output,
 //                           which also adds s·Σ_j T[m][j]·B[n][j] in fp32, T
 //                           summed from the split kernel's partial tiles in
-//                           slice order (requested at the kernel's start).
+//                           slice order.
 //
-// Measured on the 4096x4096 q_proj weight (M = 1): computing T inside every
-// workgroup (each reading all of A) delayed the data by ~3.4 us; summing the
-// partial tiles with loads issued one after the other in the epilogue cost
-// ~3.7 us; the X fragments loaded by every wave from global memory ~1.6 us.
+// Measured on the 4096x4096 q_proj weight (M = 1, graph-replayed forwards):
+// computing T inside every workgroup (each reading all of A) delayed the data
+// by ~3.4 us; summing the partial tiles with loads issued one after the other
+// in the epilogue cost ~3.7 us; the X fragments loaded by every wave from
+// global memory ~1.6 us.  The partial tiles, written by the launch just
+// before, arrive late when requested at the kernel's start (the forward took
+// 10.8 us with them first, 9.1 us with them requested right after the codes
+// and summed in the epilogue; 8.0 us without them at all).  Nothing that the
+// first barrier waits for is requested after the codes: loads complete in
+// issue order, so such a wait would also wait for them.
 #include "host.h"
 
 namespace qnf4 {
@@ -76,55 +82,33 @@ __global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __
   P[(slice * JT + jt) * 256 + 16 * m + j] = t;
 }
 
-// The adapter term of the GEMV.  gemv_t_reduce: T[m][j] = Σ_s P[s][m][j] in
-// slice order into t_fin (stride 257 floats per token row), written to
-// T_out by workgroup 0; the thread's first (m, j) has its first 16 slices
-// already in `pre` (requested at the start of the kernel), other slices are
-// loaded 16 at a time, all independent.  gemv_lora: lora[m][c] =
-// fl32(s · Σ_j T[m][j]·B[n0 + c][j]) in fp32, the B rows staged in s_b
-// [16][r].  Both run before the main loop, while the codes stream in.
+// The adapter term of the GEMV, T[m][j] = Σ_s P[s][m][j] summed in slice
+// order into t_fin (stride 257 floats per token row); workgroup 0 also
+// writes T_out.  With at most kPre slices and one entry per thread the
+// thread's partials were requested at the start of the kernel (`pre`);
+// otherwise gemv_t_reduce loads them, 16 at a time, all independent.
 constexpr int kPre = 16;
+__device__ __forceinline__ void gemv_t_store(int r, int idx, float t, float* t_fin, float* __restrict__ T_out) {
+  t_fin[(idx / r) * 257 + idx % r] = t;
+  if (T_out && blockIdx.x == 0) T_out[idx] = t;
+}
 __device__ __forceinline__ void gemv_t_reduce(int nthreads, int M, int r, const float* __restrict__ P, int S,
-                                              int JT, const float* pre, float* t_fin, float* __restrict__ T_out) {
-  const int tid = threadIdx.x;
+                                              int JT, float* t_fin, float* __restrict__ T_out) {
   const int64_t sstride = (int64_t)JT * 256;
-  for (int idx = tid; idx < M * r; idx += nthreads) {
+  for (int idx = threadIdx.x; idx < M * r; idx += nthreads) {
     const int m = idx / r, j = idx % r;
     const float* p = P + (int64_t)(j >> 4) * 256 + 16 * m + (j & 15);
     float t = 0.0f;
     for (int s0 = 0; s0 < S; s0 += kPre) {
       float v[kPre];
 #pragma unroll
-      for (int i = 0; i < kPre; ++i)
-        v[i] = (idx == tid && s0 == 0) ? pre[i] : (s0 + i < S ? p[(int64_t)(s0 + i) * sstride] : 0.0f);
+      for (int i = 0; i < kPre; ++i) v[i] = s0 + i < S ? p[(int64_t)(s0 + i) * sstride] : 0.0f;
 #pragma unroll
       for (int i = 0; i < kPre; ++i)
         if (s0 + i < S) t = (s0 + i == 0) ? v[i] : __fadd_rn(t, v[i]);
     }
-    t_fin[m * 257 + j] = t;
-    if (T_out && blockIdx.x == 0) T_out[(int64_t)m * r + j] = t;
+    gemv_t_store(r, idx, t, t_fin, T_out);
   }
-}
-__device__ __forceinline__ void gemv_lora(int nthreads, int M, int r, const float* t_fin, const float* s_b,
-                                          float scale, float* s_lora) {
-  for (int idx = threadIdx.x; idx < 16 * GEMV_ROWS; idx += nthreads) {
-    const int m = idx >> 4, c = idx & 15;
-    if (m < M) {
-      float dot = 0.0f;
-      for (int j = 0; j < r; ++j) dot = __fadd_rn(dot, __fmul_rn(t_fin[m * 257 + j], s_b[c * r + j]));
-      s_lora[idx] = __fmul_rn(scale, dot);
-    }
-  }
-}
-
-// B rows [n0, n0 + 16) of the adapter, widened to fp32 into s_b [16][r]
-// (rows past N read as zero).
-template <bool F16>
-__device__ __forceinline__ void stage_b_rows(const uint16_t* __restrict__ B, int64_t N, int64_t n0, int r,
-                                             float* s_b, int nthreads) {
-  const rsrc_t rb = make_rsrc(B + n0 * r, (N - n0) * r * 2);
-  for (int idx = threadIdx.x; idx < GEMV_ROWS * r; idx += nthreads)
-    s_b[idx] = widen16<F16>(buf_load2(rb, (uint32_t)(idx * 2), 0u));
 }
 
 constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
@@ -144,7 +128,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
                                                             int y_bf16, float* __restrict__ T_out, Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) char sx[];  // X [M][K] bf16 (XL)
   __shared__ __attribute__((aligned(256))) float sq[16];  // low address byte free for 4·code
-  __shared__ float s_lora[16 * GEMV_ROWS];
   __shared__ f32x4_t s_acc[kGemvWaves][64];
   __shared__ float t_fin[16 * 257];
   __shared__ float s_b[16 * 256];
@@ -217,28 +200,62 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     }
   };
 
-  Group ga, gb;
-  load(ga, wave);
-  // this thread's first T entry (token tid / r, rank tid % r): its partial
-  // tiles from the split kernel (finished before this launch) requested now
-  float pre[kPre];
-  {
-    const int tm = tid / r, tj = tid % r;
-    const bool has = tid < M * r;
-    const float* pb = P + (int64_t)(tj >> 4) * 256 + 16 * tm + (tj & 15);
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) pre[i] = (has && i < S) ? pb[(int64_t)i * JT * 256] : 0.0f;
-  }
+  // Requested first, so that waiting for them does not wait for the codes
+  // (loads complete in issue order): 8 values of the workgroup's B rows
+  // (16·r contiguous bf16), and X when staged.
+  const rsrc_t rbr = make_rsrc(B + n0 * r, (N - n0) * r * 2);
+  const u32x4_t braw = buf_load16(rbr, tid < 2 * r ? (uint32_t)(16 * tid) : 0x7fffffffu, 0u);
+  constexpr int kXVec = kGemvXLdsBytes / 16 / kGemvThreads;  // 16-byte X pieces per thread
+  u32x4_t xs[XL ? kXVec : 1];
   if constexpr (XL) {
     const int nvec = (M * (int)K * 2) / 16;
-    for (int v = tid; v < nvec; v += kGemvThreads)
-      *reinterpret_cast<u32x4_t*>(sx + 16 * v) = buf_load16(rx, (uint32_t)(16 * v), 0u);
+#pragma unroll
+    for (int i = 0; i < kXVec; ++i) {
+      const int v = tid + i * kGemvThreads;
+      xs[i] = buf_load16(rx, v < nvec ? (uint32_t)(16 * v) : 0x7fffffffu, 0u);
+    }
   }
-  stage_b_rows<F16>(B, N, n0, r, s_b, kGemvThreads);
-  if (tid < 16) sq[tid] = cb.q[tid];
-  gemv_t_reduce(kGemvThreads, M, r, P, S, JT, pre, t_fin, T_out);
-  __syncthreads();  // codebook, B rows, X, T
-  gemv_lora(kGemvThreads, M, r, t_fin, s_b, scale, s_lora);
+  // (the codebook is indexed per thread, so it is read from memory too)
+  const float cbq = cb.q[tid & 15];
+  __builtin_amdgcn_sched_barrier(0);
+  Group ga, gb;
+  load(ga, wave);
+  __builtin_amdgcn_sched_barrier(0);
+  // This thread's T entry (token tid / r, rank tid % r): its partial tiles,
+  // written by the split kernel just before this launch, requested after
+  // the codes (read at the start of the kernel, they took ~1.5 us longer to
+  // arrive than the codes themselves) and summed in the epilogue.
+  const bool t_pre = XL && S <= kPre && M * r <= kGemvThreads;
+  float pre[kPre];
+  if (t_pre && wave * 64 < M * r) {
+    const int tm = tid / r, tj = tid % r;
+    const rsrc_t rp = make_rsrc(P, (int64_t)S * JT * 256 * 4);
+    const uint32_t po = (uint32_t)(((tj >> 4) * 256 + 16 * tm + (tj & 15)) * 4);
+    // (the whole offset in the lane's register: it alone is range-checked)
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+      pre[i] = __uint_as_float(
+          buf_load4(rp, tid < M * r && i < S ? po + (uint32_t)(i * JT * 256 * 4) : 0x7fffffffu, 0u));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+    const int nvec = (M * (int)K * 2) / 16;
+#pragma unroll
+    for (int i = 0; i < kXVec; ++i) {
+      const int v = tid + i * kGemvThreads;
+      if (v < nvec) *reinterpret_cast<u32x4_t*>(sx + 16 * v) = xs[i];
+    }
+  }
+  if (tid < 16) sq[tid] = cbq;
+  // the B rows widened to fp32 into s_b [16][r]; T from `pre`
+  if (tid < 2 * r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s_b[8 * tid + 2 * i] = widen16<F16>(braw[i] & 0xffffu);
+      s_b[8 * tid + 2 * i + 1] = widen16<F16>(braw[i] >> 16);
+    }
+  }
+  __syncthreads();  // codebook, X, B rows
 
   // two groups per iteration, alternating buffers: the loads of the next
   // group are issued (and kept above the barrier to the scheduler) before
@@ -253,9 +270,21 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     consume(gb, grp + kGemvWaves);
   }
   s_acc[wave][lane] = acc;
+  if (t_pre) {
+    if (tid < M * r) {
+      float t = pre[0];
+#pragma unroll
+      for (int i = 1; i < kPre; ++i)
+        if (i < S) t = __fadd_rn(t, pre[i]);
+      gemv_t_store(r, tid, t, t_fin, T_out);
+    }
+  } else {
+    gemv_t_reduce(kGemvThreads, M, r, P, S, JT, t_fin, T_out);
+  }
   __syncthreads();
   // one thread per output (token m, weight row n0 + c): the 16 partial
   // tiles in a fixed order, then the adapter term
+  // fl32(s · Σ_j T[m][j]·B[n0 + c][j]) in fp32, j in order
   if (tid < 16 * GEMV_ROWS) {
     const int m = tid >> 4, c = tid & 15;
     const int64_t nn = n0 + c;
@@ -263,7 +292,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
       float y = s_acc[0][16 * (m >> 2) + c][m & 3];
 #pragma unroll
       for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
-      y = __fadd_rn(y, s_lora[tid]);
+      float dot = 0.0f;
+      for (int j = 0; j < r; ++j) dot = __fadd_rn(dot, __fmul_rn(t_fin[m * 257 + j], s_b[c * r + j]));
+      y = __fadd_rn(y, __fmul_rn(scale, dot));
       if (y_bf16)
         static_cast<uint16_t*>(Y)[(int64_t)m * N + nn] = (uint16_t)(pack16<F16>(y, 0.0f) & 0xffffu);
       else
