@@ -17,7 +17,7 @@
 //                           taking one each, and feeds 8
 //                           v_mfma_f32_16x16x32_bf16: MFMA t takes codes
 //                           8t..8t+7 of every lane's block (the A operand, X
-//                           padded to 16 rows and staged in LDS when small,
+//                           padded to 16 rows and staged in LDS up to 128 KB,
 //                           uses the same k slots).  Each value is
 //                           RNE_bf16(fl32(q_c * c')) with q_c read from a
 //                           16-entry LDS codebook (one address per code: no
@@ -37,6 +37,8 @@
 // and summed in the epilogue; 8.0 us without them at all).  Nothing that the
 // first barrier waits for is requested after the codes: loads complete in
 // issue order, so such a wait would also wait for them.
+#include <algorithm>
+
 #include "host.h"
 
 namespace qnf4 {
@@ -112,25 +114,35 @@ __device__ __forceinline__ void gemv_t_reduce(int nthreads, int M, int r, const 
 }
 
 constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
-constexpr int kGemvXLdsBytes = 32 * 1024;  // X staged in LDS up to this size
+constexpr int kGemvXLdsBytes = 128 * 1024;  // X staged in LDS up to this size
+// The adapter term's t_fin [16][257] and s_b [16][256]: arrays of their own,
+// except with X of more than 32 KB staged (up to 128 KB), where they take
+// X's place after the main loop.
+constexpr int kTfinFloats = 16 * 257, kSbFloats = 16 * 256;
+constexpr size_t kGemvEpiBytes = (size_t)(kTfinFloats + kSbFloats) * 4;
 
 // 16 waves per 16 weight rows; each wave's next block group is requested
-// before the current one is dequantized.  XL: X (M x K bf16) is staged in LDS
-// once per workgroup (when it fits) and the MFMA fragments are read from
-// there; otherwise every wave loads its fragments from global memory (the
-// same few bytes requested by every wave of every workgroup at once cost
-// ~1.6 us at M = 1 on the q_proj weight, measured).
-template <bool F16, bool XL>
+// before the current one is dequantized.  XV > 0: X (M x K bf16) is staged
+// in LDS once per workgroup, XV 16-byte pieces per thread (2: up to 32 KB,
+// 8: up to 128 KB), and the MFMA fragments are read from there; XV = 0:
+// every wave loads its fragments from global memory (the same few bytes
+// requested by every wave of every workgroup at once cost ~1.6 us at M = 1
+// on the q_proj weight, ~2 us at M = 16, measured).
+template <bool F16, int XV>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
                                                             int M, const float* __restrict__ P, int S, int JT,
                                                             const uint16_t* __restrict__ B, int r,
                                                             float scale, void* __restrict__ Y,
                                                             int y_bf16, float* __restrict__ T_out, Codebook cb) {
+  constexpr bool XL = XV > 0;  // X staged: XV 16-byte pieces per thread
+  constexpr bool epi_late = XV > 2;  // t_fin and s_b in X's place
   extern __shared__ __attribute__((aligned(16))) char sx[];  // X [M][K] bf16 (XL)
+  __shared__ float t_fin_own[epi_late ? 1 : kTfinFloats];
+  __shared__ float s_b_own[epi_late ? 1 : kSbFloats];
+  float* const t_fin = epi_late ? reinterpret_cast<float*>(sx) : t_fin_own;
+  float* const s_b = epi_late ? reinterpret_cast<float*>(sx) + kTfinFloats : s_b_own;
   __shared__ __attribute__((aligned(256))) float sq[16];  // low address byte free for 4·code
   __shared__ f32x4_t s_acc[kGemvWaves][64];
-  __shared__ float t_fin[16 * 257];
-  __shared__ float s_b[16 * 256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t K = W.K, N = W.N;
@@ -205,12 +217,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
   // (16·r contiguous bf16), and X when staged.
   const rsrc_t rbr = make_rsrc(B + n0 * r, (N - n0) * r * 2);
   const u32x4_t braw = buf_load16(rbr, tid < 2 * r ? (uint32_t)(16 * tid) : 0x7fffffffu, 0u);
-  constexpr int kXVec = kGemvXLdsBytes / 16 / kGemvThreads;  // 16-byte X pieces per thread
-  u32x4_t xs[XL ? kXVec : 1];
+  u32x4_t xs[XL ? XV : 1];
   if constexpr (XL) {
     const int nvec = (M * (int)K * 2) / 16;
 #pragma unroll
-    for (int i = 0; i < kXVec; ++i) {
+    for (int i = 0; i < XV; ++i) {
       const int v = tid + i * kGemvThreads;
       xs[i] = buf_load16(rx, v < nvec ? (uint32_t)(16 * v) : 0x7fffffffu, 0u);
     }
@@ -241,20 +252,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
   if constexpr (XL) {
     const int nvec = (M * (int)K * 2) / 16;
 #pragma unroll
-    for (int i = 0; i < kXVec; ++i) {
+    for (int i = 0; i < XV; ++i) {
       const int v = tid + i * kGemvThreads;
       if (v < nvec) *reinterpret_cast<u32x4_t*>(sx + 16 * v) = xs[i];
     }
   }
   if (tid < 16) sq[tid] = cbq;
-  // the B rows widened to fp32 into s_b [16][r]; T from `pre`
-  if (tid < 2 * r) {
+  // the B rows widened to fp32 into s_b [16][r] (after the main loop when
+  // s_b lies in X's place)
+  auto stage_b = [&]() __attribute__((always_inline)) {
+    if (tid < 2 * r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_b[8 * tid + 2 * i] = widen16<F16>(braw[i] & 0xffffu);
-      s_b[8 * tid + 2 * i + 1] = widen16<F16>(braw[i] >> 16);
+      for (int i = 0; i < 4; ++i) {
+        s_b[8 * tid + 2 * i] = widen16<F16>(braw[i] & 0xffffu);
+        s_b[8 * tid + 2 * i + 1] = widen16<F16>(braw[i] >> 16);
+      }
     }
-  }
+  };
+  if (!epi_late) stage_b();
   __syncthreads();  // codebook, X, B rows
 
   // two groups per iteration, alternating buffers: the loads of the next
@@ -270,6 +285,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     consume(gb, grp + kGemvWaves);
   }
   s_acc[wave][lane] = acc;
+  if (epi_late) {
+    __syncthreads();  // X read by every wave: its region takes t_fin and s_b
+    stage_b();
+  }
   if (t_pre) {
     if (tid < M * r) {
       float t = pre[0];
@@ -322,15 +341,19 @@ hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uin
   const unsigned grid = (unsigned)((W.N + GEMV_ROWS - 1) / GEMV_ROWS);
   const int yb = y16 ? 1 : 0;
   const size_t xb = (size_t)M * W.K * 2;
-  if (xb <= (size_t)kGemvXLdsBytes)
-    return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, true>, dim3(grid), dim3(kGemvThreads), xb, st, W, X,
-                                  (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
-               : timed_launch_shm(kKernGemv, gemv_kernel<false, true>, dim3(grid), dim3(kGemvThreads), xb, st, W, X,
-                                  (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook());
-  return f16 ? timed_launch(kKernGemv, gemv_kernel<true, false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
-                            (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
-             : timed_launch(kKernGemv, gemv_kernel<false, false>, dim3(grid), dim3(kGemvThreads), st, W, X, (int)M,
-                            (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook());
+  const bool xl = xb <= (size_t)kGemvXLdsBytes;
+  const bool x2 = xb <= (size_t)kGemvThreads * 16 * 2;
+  const size_t shm = x2 ? xb : (xl ? std::max(xb, kGemvEpiBytes) : 0);
+#define QNF4_GEMV_LAUNCH(XV)                                                                                    \
+  return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, XV>, dim3(grid), dim3(kGemvThreads), shm, st, W, X, \
+                                (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())      \
+             : timed_launch_shm(kKernGemv, gemv_kernel<false, XV>, dim3(grid), dim3(kGemvThreads), shm, st, W, X, \
+                                (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
+  // X staged with 2 or 8 pieces of 16 bytes per thread (up to 32 or 128 KB)
+  if (x2) QNF4_GEMV_LAUNCH(2);
+  if (xl) QNF4_GEMV_LAUNCH(8);
+  QNF4_GEMV_LAUNCH(0);
+#undef QNF4_GEMV_LAUNCH
 }
 
 }  // namespace qnf4
