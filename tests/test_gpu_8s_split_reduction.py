@@ -27,10 +27,12 @@ from workloads import Inputs
 pytestmark = pytest.mark.gpu
 
 
-# (2, 1): the GEMV with X staged in LDS and 43 partial slices of T, summed
-# after the main loop (the staged forward sums at most 16 slices up front)
-@pytest.mark.parametrize("layer,M", [(0, 1), (0, 17), (0, 130), (0, 300), (2, 1), (2, 5), (2, 64), (2, 100),
-                                     (1, 256)])
+# The GEMV's X staging: (0, 1) 8 KB, (2, 1) 22 KB, (2, 5) 110 KB staged (the
+# adapter term's arrays then take X's place after the main loop), (2, 16)
+# 352 KB not staged; (2, *) with 43 partial slices of T, summed after the
+# main loop (at most 16 are summed from registers)
+@pytest.mark.parametrize("layer,M", [(0, 1), (0, 17), (0, 130), (0, 300), (2, 1), (2, 5), (2, 16), (2, 64),
+                                     (2, 100), (1, 256)])
 def test_split_reduction_every_element(layer, M):
     compare_every_element(layer, M)
 
