@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   int tmi, tki, sp;
   if (!tile_of(blockIdx.x, tiles_m, tiles_k, splits, tmi, tki, sp)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index in a scalar register: the LDS addresses and offsets of
+  // the copies derived from it are then formed by scalar instructions)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = lane >> 3, cg = lane & 7;
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, k0 = (int64_t)tki * TK;

@@ -82,7 +82,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   int tmi, tni, sp;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, splits, tmi, tni, sp)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index in a scalar register: the LDS addresses and offsets of
+  // the copies derived from it are then formed by scalar instructions)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, n0 = (int64_t)tni * TN;
   // this workgroup's K steps [kfirst, kfirst + ksteps) (step indices below
