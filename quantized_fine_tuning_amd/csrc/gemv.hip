@@ -120,6 +120,12 @@ constexpr int kGemvXLdsBytes = 128 * 1024;  // X staged in LDS up to this size
 // X's place after the main loop.
 constexpr int kTfinFloats = 16 * 257, kSbFloats = 16 * 256;
 constexpr size_t kGemvEpiBytes = (size_t)(kTfinFloats + kSbFloats) * 4;
+// LDS of a workgroup (the device's 160 KB): s_acc (16 KB) and the codebook
+// (256 bytes with its alignment) beside the X region; beside X of up to
+// 32 KB also t_fin and s_b.
+constexpr size_t kGemvAccBytes = (size_t)16 * 64 * 16 + 256;
+static_assert(kGemvAccBytes + kGemvXLdsBytes <= 160 * 1024, "X staged up to 128 KB fits the LDS");
+static_assert(kGemvAccBytes + 32 * 1024 + kGemvEpiBytes <= 160 * 1024, "X of 32 KB fits beside the epilogue arrays");
 
 // 16 waves per 16 weight rows; each wave's next block group is requested
 // before the current one is dequantized.  XV > 0: X (M x K bf16) is staged
