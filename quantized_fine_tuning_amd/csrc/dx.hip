@@ -26,7 +26,14 @@
 //     column into one 16-byte store: the values come out already
 //     transposed.  Table slots, tile swizzles and lane maps are chosen so
 //     that lookups, stores and fragment reads are free of LDS bank conflicts
-//     (32 banks of 4 bytes).  Rows past N get an all-zero table.
+//     (32 banks of 4 bytes; the measured conflict count is 32 cycles per
+//     step, from 256 when 8 consecutive lanes stored to 4 chunk positions).
+//     Rows past N get an all-zero table.
+//   * The producers move the codes into LDS transposed as dwords: a lane
+//     loads 16 bytes of each of two consecutive weight rows and stores, per
+//     column group, both rows' 2 bytes with one byte permute (8 stores per
+//     lane and step; 2-byte stores of one row at a time took 16 and cost
+//     3-4% of the kernel).
 //   * One barrier per step: after it the MFMA waves use dY(s) and Ŵᵀ(s)
 //     while the other buffers fill with dY(s+1) and Ŵᵀ(s+1).
 //   * The LoRA term is 2*Rp/64 extra steps with A = [sU_hi | sU_lo] and B from
@@ -68,6 +75,13 @@ __device__ __forceinline__ int wswz(int row, int chunk) {
   return row * 128 + ((chunk ^ wsw(row)) << 4);
 }
 
+// Lane of a dequantization slice -> (row group rg, column group cg):
+// lane bits 0..5 are cg0, rg0, rg1, cg1, cg2, rg2.  Each half-wave then
+// reads the tables of 4 row groups (32 banks once), and each 8 consecutive
+// lanes store their 16-byte chunks to 8 distinct chunk positions.
+__device__ __forceinline__ int dq_rg(int l) { return ((l >> 1) & 3) | ((l >> 3) & 4); }
+__device__ __forceinline__ int dq_cg(int l) { return (l & 1) | ((l >> 2) & 6); }
+
 template <int LSTEPS, bool F16>
 __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const uint16_t* __restrict__ dY,
                                                               int64_t M, const uint16_t* __restrict__ sU,
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // (the wave index in a scalar register: the LDS addresses and offsets of
   // the copies derived from it are then formed by scalar instructions)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = lane >> 3, cg = lane & 7;
+  const int rg = dq_rg(lane), cg = dq_cg(lane);
   const int64_t K = W.K, N = W.N;
   const int64_t m0 = (int64_t)tmi * TM, k0 = (int64_t)tki * TK;
   // this workgroup's n steps [nfirst, nfirst + nsteps) (step indices below
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       // lane offsets recomputed here from an opaque copy of the lane index
       // (kept from being hoisted out of the MFMA waves' loop, where they
       // would hold registers through the MFMAs)
-      const int ln = opaque(lane), lrg = ln >> 3, lcg = ln & 7;
+      const int ln = opaque(lane), lrg = dq_rg(ln), lcg = dq_cg(ln);
       const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)lrg;
       const uint32_t st0 =
           (uint32_t)((32 * sigma + 4 * lcg) * 128 + ((lrg ^ ((lcg >> 1) & 1) ^ (4 * (lcg & 1))) << 4));
@@ -207,8 +221,11 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     // MFMA group g (0..15) of a step: n-half ks = g / 8, token block i = g % 8.
     // A fragments are read one group ahead: group g first reads the A
     // fragment of group g + 1, so the read's latency overlaps this group's
-    // MFMAs.  The B fragments of the second n-half are read right after the
-    // MFMAs of group 7.
+    // MFMAs.  At a step's start the A fragment of group 0 is requested before
+    // the four B fragments, so that its first MFMA waits for two reads, not
+    // five (LDS reads return in order; about 1% on the step).  The B
+    // fragments of the second n-half are read right after the MFMAs of
+    // group 7.
     const int arow = 128 * wm + lr, brow = 64 * wk + lr;
     u32x4_t bfr[4], anext;
     auto read_b = [&](const char* wb, int ks, u32x4_t* b) __attribute__((always_inline)) {
@@ -220,8 +237,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       return *reinterpret_cast<const u32x4_t*>(ya + xswz(arow + 16 * (g & 7), 2 * kq + (g >> 3)));
     };
     auto mfma_step = [&](const char* ya, const char* wb) __attribute__((always_inline)) {
-      read_b(wb, 0, bfr);
       anext = read_a(ya, 0);
+      read_b(wb, 0, bfr);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         const int i = g & 7;
@@ -240,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     __syncthreads();  // codes and tables of steps 0 and 1 in place
     auto read_codes_mfma = [&](int t) __attribute__((always_inline)) {
       const int ln = opaque(lane);
-      return *reinterpret_cast<const u32x4_t*>(scode[t & 1][2 * wave] + 16 * (8 * (ln >> 3) + ((ln & 7) ^ (ln >> 3))));
+      return *reinterpret_cast<const u32x4_t*>(scode[t & 1][2 * wave] + 16 * (8 * dq_rg(ln) + (dq_cg(ln) ^ dq_rg(ln))));
     };
     if (dq) dequant_slice(std::false_type(), 0, 2 * wave, read_codes_mfma(0), no_issue);
     __syncthreads();  // step 0 in place
@@ -344,25 +361,31 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
     }
   };
 
-  // Codes of weight row t*64 + l, columns [64p, +64) of the tile: 32 bytes,
-  // the first 16 for slice 2p, the rest for slice 2p + 1.
-  const uint32_t vcode = (uint32_t)((uint32_t)lane * (uint32_t)(K / 2) + (uint32_t)(k0 / 2) + 32u * (uint32_t)p);
+  // Codes of weight rows t*64 + 2m and 2m + 1 (m = lane & 31), columns
+  // [64p + 32h, +32) of the tile (h = lane >> 5, slice 2p + h): 16 bytes of
+  // each row.  A column group (4 columns, 2 bytes) of both rows is one
+  // dword, stored at byte 4(m & 3) of slot 8rg + (cg ^ rg), rg = m >> 2: the
+  // 32 lanes of each half-wave cover the 32 banks once.
+  const int cm = lane & 31, ch = lane >> 5;
+  const uint32_t vcode =
+      (uint32_t)(2 * cm) * (uint32_t)(K / 2) + (uint32_t)(k0 / 2) + 32u * (uint32_t)p + 16u * (uint32_t)ch;
   const uint32_t code_sstride = (uint32_t)(NSTEP * (K / 2));
   struct Codes {
     u32x4_t c0, c1;
   };
   auto load_codes = [&](Codes& r, int t) __attribute__((always_inline)) {
     r.c0 = buf_load16(rc, vcode, (uint32_t)(nfirst + t) * code_sstride);
-    r.c1 = buf_load16(rc, vcode + 16u, (uint32_t)(nfirst + t) * code_sstride);
+    r.c1 = buf_load16(rc, vcode + (uint32_t)(K / 2), (uint32_t)(nfirst + t) * code_sstride);
   };
-  const uint32_t code_wbase = (uint32_t)((lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7));
+  const int crg = cm >> 2;
+  const uint32_t code_wbase = (uint32_t)(crg * 128 + 4 * (cm & 3));
   auto store_codes = [&](int t, const Codes& r) __attribute__((always_inline)) {
+    char* const base = scode[t & 1][2 * p + ch];
 #pragma unroll
     for (int pc = 0; pc < 8; ++pc) {
-      const uint32_t off = code_wbase ^ (uint32_t)(pc << 4);
-      *reinterpret_cast<uint16_t*>(scode[t & 1][2 * p] + off) = (uint16_t)(r.c0[pc >> 1] >> (16 * (pc & 1)));
-      *reinterpret_cast<uint16_t*>(scode[t & 1][2 * p + 1] + off) =
-          (uint16_t)(r.c1[pc >> 1] >> (16 * (pc & 1)));
+      const uint32_t off = code_wbase + (uint32_t)(((pc ^ crg) & 7) << 4);
+      *reinterpret_cast<uint32_t*>(base + off) =
+          __builtin_amdgcn_perm(r.c1[pc >> 1], r.c0[pc >> 1], (pc & 1) ? 0x07060302u : 0x05040100u);
     }
   };
 

@@ -178,6 +178,32 @@ def wswz(row, chunk):
     return row * 128 + ((chunk ^ wsw(row)) << 4)
 
 
+def dq_rg(l):
+    """Row group of lane l in a dequantization slice (lane bits 1, 2, 5)."""
+    return ((l >> 1) & 3) | ((l >> 3) & 4)
+
+
+def dq_cg(l):
+    """Column group of lane l in a dequantization slice (lane bits 0, 3, 4)."""
+    return (l & 1) | ((l >> 2) & 6)
+
+
+def test_dq_lane_map_is_a_bijection():
+    assert {(dq_rg(l), dq_cg(l)) for l in range(64)} == {(rg, cg) for rg in range(8) for cg in range(8)}
+
+
+@pytest.mark.parametrize("sigma", range(8))
+def test_dx_slice_stores_of_8_lanes_hit_8_chunk_positions(sigma):
+    # one store instruction (column c of the lanes' 4): each run of 8
+    # consecutive lanes writes 8 distinct 16-byte chunk positions of the
+    # 128-byte rows (the map that took the measured LDS bank conflicts of
+    # the dX GEMM from 256 to 32 cycles per step)
+    for c in range(4):
+        for g in range(8):
+            chunks = {(wswz(32 * sigma + 4 * dq_cg(l) + c, dq_rg(l)) % 128) // 16 for l in range(8 * g, 8 * g + 8)}
+            assert len(chunks) == 8
+
+
 def test_wswz_is_a_bijection_on_a_tile():
     offs = {wswz(r, c) for r in range(256) for c in range(8)}
     assert offs == set(range(0, 256 * 128, 16))
@@ -217,7 +243,7 @@ def test_dx_slice_store_identity(sigma):
     seen = set()
     for c in range(4):
         for lane in range(64):
-            rg, cg = lane >> 3, lane & 7
+            rg, cg = dq_rg(lane), dq_cg(lane)
             st0 = (32 * sigma + 4 * cg) * 128 + ((rg ^ ((cg >> 1) & 1) ^ (4 * (cg & 1))) << 4)
             a = (st0 ^ (16 * (c & 2))) + 128 * c
             assert a == wswz(32 * sigma + 4 * cg + c, rg)
@@ -226,30 +252,44 @@ def test_dx_slice_store_identity(sigma):
 
 
 def test_dx_code_transpose_meets_its_readers():
-    # writer: lane l holds weight row l; its 2 bytes of column group pc go to
-    # code_wbase ^ (pc << 4); reader (rg, cg) reads the 16-byte slot
-    # 8rg + (cg ^ rg), whose byte 2i holds row 8rg + i
-    where = {}
-    for lane in range(64):
-        wbase = (lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7)
-        for pc in range(8):
-            off = wbase ^ (pc << 4)
-            assert off not in where
-            where[off] = (lane, pc)
-    assert sorted(where) == list(range(0, 64 * 16, 2))
-    for lane in range(64):
-        rg, cg = lane >> 3, lane & 7
-        slot = 8 * rg + (cg ^ rg)
-        for i in range(8):
-            assert where[16 * slot + 2 * i] == (8 * rg + i, cg)
-    # the 16-bit writes of one instruction (fixed pc): 32 lanes per cycle
+    # writer: lane l (m = l & 31, h = l >> 5) holds 16 bytes of weight rows
+    # 2m and 2m + 1 for slice h; per column group pc it stores one dword (2
+    # bytes of row 2m, then 2 bytes of row 2m + 1) at byte 4(m & 3) of slot
+    # 8rg + (pc ^ rg), rg = m >> 2.  Reader (rg, cg) reads the 16-byte slot
+    # 8rg + (cg ^ rg), whose byte 2i holds row 8rg + i.
+    for h in range(2):
+        where = {}
+        for lane in range(32 * h, 32 * h + 32):
+            m = lane & 31
+            rg = m >> 2
+            for pc in range(8):
+                off = rg * 128 + (((pc ^ rg) & 7) << 4) + 4 * (m & 3)
+                for half, row in ((0, 2 * m), (1, 2 * m + 1)):
+                    assert off + 2 * half not in where
+                    where[off + 2 * half] = (row, pc)
+        assert sorted(where) == list(range(0, 64 * 16, 2))
+        for lane in range(64):
+            rg, cg = dq_rg(lane), dq_cg(lane)
+            slot = 8 * rg + (cg ^ rg)
+            for i in range(8):
+                assert where[16 * slot + 2 * i] == (8 * rg + i, cg)
+    # the 4-byte writes of one instruction (fixed pc): 32 lanes per cycle
     for pc in range(8):
         for half in range(2):
             addrs = []
             for lane in range(32 * half, 32 * half + 32):
-                wbase = (lane >> 3) * 128 + ((lane >> 3) << 4) + 2 * (lane & 7)
-                addrs.append(wbase ^ (pc << 4))
+                m = lane & 31
+                rg = m >> 2
+                addrs.append(rg * 128 + (((pc ^ rg) & 7) << 4) + 4 * (m & 3))
             assert conflict_free_small(addrs)
+    # the byte permute puts row 2m's 2 bytes low and row 2m + 1's high
+    rnd = random.Random(3)
+    for _ in range(100):
+        c0, c1 = rnd.getrandbits(32), rnd.getrandbits(32)
+        for odd, sel in ((0, 0x05040100), (1, 0x07060302)):
+            w = perm(c1, c0, sel)
+            assert w & 0xFFFF == (c0 >> (16 * odd)) & 0xFFFF
+            assert w >> 16 == (c1 >> (16 * odd)) & 0xFFFF
 
 
 def test_dx_table_writers_cover_the_tables_without_conflicts():
@@ -302,6 +342,6 @@ def test_dx_lookups_are_conflict_free_for_any_codes():
         for p in range(4):
             for h in range(2):
                 for half in range(2):
-                    addrs = [256 * (2 * p + h) + 32 * (l >> 3) + 2 * codes[l]
+                    addrs = [256 * (2 * p + h) + 32 * dq_rg(l) + 2 * codes[l]
                              for l in range(32 * half, 32 * half + 32)]
                     assert conflict_free_small(addrs)
