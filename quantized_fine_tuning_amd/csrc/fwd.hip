@@ -4,25 +4,35 @@
 // matmul and the LoRA path is added to the output.)
 //
 // Design
-//   * 256x256 output tile per workgroup of 12 waves, three per SIMD, in two
-//     roles.  Waves 0..7 only multiply: wave (wm, wn) owns token rows
-//     [128wm, +128) and weight rows [64wn, +64) of the tile, 64
+//   * One output tile per workgroup of 12 waves, three per SIMD, in two
+//     roles; the tile is 256x256, or 512x128 from 2048 tokens on (one
+//     kernel template, TMV = 256 or 512 token rows).  Waves 0..7 only
+//     multiply: wave (wm, wn) owns token rows [128wm, +128) and weight rows
+//     [64wn, +64) of the tile (2 x 4 waves, or 4 x 2), 64
 //     v_mfma_f32_16x16x32_bf16 per 64-wide reduction step, operands read
 //     from LDS one MFMA group ahead.  Waves 8..11 (one per SIMD) produce the
 //     operands of the next step: each copies a quarter of the X tile
-//     straight into LDS and dequantizes 64 of the tile's 256 weight rows into
-//     the shared bf16 tile Ŵ[n][k].  Their arithmetic and copies overlap the
-//     MFMAs of the other two waves of their SIMD.
-//   * Dequantization in registers: lane l of producer p owns tile row
-//     64p + l.  Per step it builds that row's table of the 16 values
-//     RNE_bf16(fl32(q_j * c')) of the step's block (bit-identical to
-//     multiplying per element, since the value depends only on code and
-//     row), held as four byte planes (low bytes of values 0-3, 4-7, 8-11,
-//     12-15, likewise the high bytes), and decodes the row's 64 codes with
-//     byte permutes: four codes per permute pair, the code's low three bits
-//     selecting within 8 bytes and its top bit between the two halves; the
-//     low and high bytes are then interleaved into bf16 pairs and the row's
-//     eight 16-byte chunks stored.  No LDS lookups, no tables in LDS.
+//     straight into LDS and dequantizes a quarter of the tile's weight rows
+//     into the shared bf16 tile Ŵ[n][k].  Their arithmetic and copies
+//     overlap the MFMAs of the other two waves of their SIMD.
+//   * The 512x128 tile decodes each weight row of a step once for 512
+//     tokens: half the producers' decode per MFMA for twice their X copy
+//     (64 KB of X and 16 KB of Ŵ per step, 160 KB of LDS with both
+//     buffers).  On the 7B MLP shapes it takes the forward GEMM from ≈322 to
+//     ≈310 µs (bit-identical output); below 2048 tokens, or with a split
+//     reduction, its 512-row tiles would be mostly padding.
+//   * Dequantization in registers: producer p owns tile rows
+//     [WR p, +WR) (WR = 64 or 32): lane l takes row WR p + l % WR and, when
+//     two lanes share a row, half l / WR of its 64 codes.  Per step a lane
+//     builds its row's table of the 16 values RNE_bf16(fl32(q_j * c')) of
+//     the step's block (bit-identical to multiplying per element, since the
+//     value depends only on code and row), held as four byte planes (low
+//     bytes of values 0-3, 4-7, 8-11, 12-15, likewise the high bytes), and
+//     decodes its codes with byte permutes: four codes per permute pair,
+//     the code's low three bits selecting within 8 bytes and its top bit
+//     between the two halves; the low and high bytes are then interleaved
+//     into bf16 pairs and the row's 16-byte chunks stored.  No LDS lookups,
+//     no tables in LDS.
 //   * Each producer step first waits for the codes and constants it loaded a
 //     step earlier, then issues the X copy of the next step, then the loads
 //     of the step after (into the other of two register sets, so that no
@@ -53,10 +63,10 @@
 namespace qnf4 {
 namespace {
 
-constexpr int TM = 256, TN = 256, KSTEP = 64;
+constexpr int TM = 256, TN = 256, KSTEP = 64;  // the square tile (split plans)
 constexpr int kMfmaWaves = 8, kProdWaves = 4, kWaves = kMfmaWaves + kProdWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kProdRows = TN / kProdWaves;  // weight rows per producer wave
+constexpr int64_t kTallMinTokens = 2048;  // 512 x 128 tiles from here on
 
 // A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
 // physical chunk c ^ sw(r & 7), where sw swaps bits 0 and 1 of its argument.
@@ -69,7 +79,10 @@ __device__ __forceinline__ int xswz(int row, int chunk) {
   return row * 128 + ((chunk ^ rsw(row & 7)) << 4);
 }
 
-template <int LSTEPS, bool F16>
+// TMV x (65536 / TMV) output tiles: 256 x 256, or 512 x 128 (the weight
+// rows of a step decoded once for twice the tokens: half the producers'
+// decode per MFMA, twice their X copy).
+template <int LSTEPS, bool F16, int TMV>
 __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const uint16_t* __restrict__ X,
                                                                int64_t M, const uint16_t* __restrict__ sT,
                                                                const uint16_t* __restrict__ B2,
@@ -77,6 +90,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
                                                                int y_bf16, int tiles_m, int tiles_n,
                                                                int splits, float* __restrict__ P,
                                                                Codebook cb) {
+  constexpr int TM = TMV, TN = 65536 / TMV;
+  constexpr int WGN = TN / 64;           // MFMA waves along N (4 or 2), each 128 x 64
+  constexpr int XR = TM / kProdWaves;    // X rows copied per producer and step (64 or 128)
+  constexpr int WR = TN / kProdWaves;    // weight rows decoded per producer (64 or 32)
+  constexpr int HALVES = 64 / WR;        // lanes per weight row (1 or 2)
+  constexpr int NLOADS = 2 / HALVES + 2;  // vector loads per producer step (codes, e byte, scale)
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
   int tmi, tni, sp;
@@ -107,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   if (wave < kMfmaWaves) {
     // ---------------------------------------------------------------- MFMA
     const int lr = lane & 15, kq = lane >> 4;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / WGN, wn = wave % WGN;
     f32x4_t acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -225,28 +244,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // producer's own LDS reads; the wait before the step's closing barrier is
   // explicit.)
   const int xlch = (lane & 7) ^ rsw(lane >> 3);
-  const uint32_t vx = (uint32_t)(((64 * p + (lane >> 3)) * K + 8 * xlch) * 2);
+  const uint32_t vx = (uint32_t)(((XR * p + (lane >> 3)) * K + 8 * xlch) * 2);
   const uint32_t x_gstride = (uint32_t)(8 * K * 2);
   const i32x4_t rxw = rsrc_words(X + m0 * K, (M - m0) * K * 2);
   auto copy_x_part = [&](char* t, int s, int c) __attribute__((always_inline)) {
-    dma_lds16(rxw, t + (64 * p + 8 * c) * 128, vx + c * x_gstride, (uint32_t)(kfirst + s) * 128u);
+    dma_lds16(rxw, t + (XR * p + 8 * c) * 128, vx + c * x_gstride, (uint32_t)(kfirst + s) * 128u);
   };
   auto copy_x = [&](char* t, int s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) copy_x_part(t, s, c);
+    for (int c = 0; c < XR / 8; ++c) copy_x_part(t, s, c);
   };
   // LoRA tiles (sT rows, B2 rows), the same pattern over rows of 2Rp bf16.
-  const uint32_t vl = (uint32_t)(((64 * p + (lane >> 3)) * 2 * Rp + 8 * xlch) * 2);
   const uint32_t l_gstride = (uint32_t)(8 * 2 * Rp * 2);
-  auto copy_lora = [&](rsrc_t r, char* t, int l) __attribute__((always_inline)) {
+  auto copy_lora = [&](rsrc_t r, char* t, int l, auto rows) __attribute__((always_inline)) {
+    constexpr int RR = decltype(rows)::value;  // rows per producer
+    const uint32_t vl = (uint32_t)(((RR * p + (lane >> 3)) * 2 * Rp + 8 * xlch) * 2);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      buf_load_lds16(r, t + (64 * p + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
+    for (int c = 0; c < RR / 8; ++c)
+      buf_load_lds16(r, t + (RR * p + 8 * c) * 128, vl, c * l_gstride + (uint32_t)l * 128u);
   };
+  using XRows = std::integral_constant<int, XR>;
+  using WRows = std::integral_constant<int, WR>;
 
   // Row trow = 64p + lane of the tile is this lane's: the dword holding its
   // e4m3 byte and its group scale, its 32 bytes of codes per step.
-  const int trow = 64 * p + lane;
+  const int trow = WR * p + lane % WR, half = lane / WR;
   const uint32_t ve_me = (uint32_t)trow * kpr;
   const uint32_t blk_me = (uint32_t)(n0 + trow) * kpr;
   struct Consts {
@@ -258,8 +280,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   };
   const uint32_t vrow = (uint32_t)trow * (uint32_t)(K / 2);
   auto load_row = [&](u32x4_t* c, int t) __attribute__((always_inline)) {
-    c[0] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u);
-    c[1] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u + 16u);
+    if constexpr (HALVES == 1) {
+      c[0] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u);
+      c[1] = buf_load16(rc, vrow, (uint32_t)(kfirst + t) * 32u + 16u);
+    } else {
+      c[0] = buf_load16(rc, vrow + 16u * (uint32_t)half, (uint32_t)(kfirst + t) * 32u);
+    }
   };
   auto row_table = [&](int t, const Consts& r, uint32_t* L, uint32_t* H) __attribute__((always_inline)) {
     const uint32_t e = (r.e >> (8 * ((ve_me + (uint32_t)(kfirst + t)) & 3u))) & 0xffu;
@@ -294,11 +320,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   auto decode_row = [&](const u32x4_t* c, const uint32_t* L, const uint32_t* H, char* dst, auto&& issue)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int jj = 0; jj < 8 / HALVES; ++jj) {
+      const int j = HALVES == 1 ? jj : 4 * half + jj;  // chunk of the row
       u32x4_t o;
-      decode8(c[j >> 2][j & 3], L, H, o);
+      decode8(c[jj >> 2][jj & 3], L, H, o);
       *reinterpret_cast<u32x4_t*>(dst + xswz(trow, j)) = o;
-      issue(j);
+      issue(jj);
     }
   };
 
@@ -335,12 +362,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
     // (the compiler's waits for them would otherwise also wait for copies
     // issued before them, which it does not track)
     asm volatile("" : "+v"(L[0]), "+v"(L[1]), "+v"(L[2]), "+v"(L[3]), "+v"(H[0]), "+v"(H[1]), "+v"(H[2]),
-                 "+v"(H[3]) : "v"(cur[0]), "v"(cur[1]));
+                 "+v"(H[3]) : "v"(cur[0]), "v"(cur[HALVES == 1 ? 1 : 0]));
     copy_x(sxb((s + 1) & 1), s + 1);
     load_row(nxt, s + 2);
     load_consts(cnxt, s + 2);
     decode_row(cur, L, H, sw[(s + 1) & 1], no_issue);
-    wait_vmem_le<4>();
+    wait_vmem_le<NLOADS>();
     __syncthreads();
   };
 #pragma unroll 1
@@ -351,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   // last weight step: copy LoRA step 0 (sT and B2 tiles) into the other
   // buffers; then the LoRA steps
   if (lsteps > 0) {
-    copy_lora(rt, sxb(ksteps & 1), 0);
-    copy_lora(rb, sw[ksteps & 1], 0);
+    copy_lora(rt, sxb(ksteps & 1), 0, XRows{});
+    copy_lora(rb, sw[ksteps & 1], 0, WRows{});
   }
   wait_vmem();
   __syncthreads();
@@ -360,8 +387,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   for (int l = 0; l < lsteps; ++l) {
     const int s = ksteps + l;
     if (l + 1 < lsteps) {
-      copy_lora(rt, sxb((s + 1) & 1), l + 1);
-      copy_lora(rb, sw[(s + 1) & 1], l + 1);
+      copy_lora(rt, sxb((s + 1) & 1), l + 1, XRows{});
+      copy_lora(rb, sw[(s + 1) & 1], l + 1, WRows{});
     }
     wait_vmem();
     __syncthreads();
@@ -378,16 +405,21 @@ int fwd_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap) {
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B2, int64_t Rp, void* Y, bool y16, int splits, float* P, bool f16,
                            hipStream_t st) {
-  const int tm = (int)((M + TM - 1) / TM), tn = (int)((W.N + TN - 1) / TN);
+  // 512 x 128 tiles from 2048 tokens on (whole 512-row tiles dominate),
+  // 256 x 256 below and whenever the reduction is split
+  const bool tall = splits == 1 && M >= kTallMinTokens;
+  const int tmv = tall ? 512 : 256;
+  const int tm = (int)((M + tmv - 1) / tmv), tn = (int)((W.N + 65536 / tmv - 1) / (65536 / tmv));
   const unsigned grid = tile_grid(tm, tn, splits);
   const int yb = y16 ? 1 : 0;
+#define QNF4_FWD_LAUNCH(LS, F16V, TMV)                                                                        \
+  timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, F16V, TMV>, dim3(grid), dim3(kThreads), st, W, X, M,        \
+               (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, splits, P, codebook())
+#define QNF4_FWD_CASE(LS)                                                                                    \
+  case LS:                                                                                                   \
+    if (tall) return f16 ? QNF4_FWD_LAUNCH(LS, true, 512) : QNF4_FWD_LAUNCH(LS, false, 512);                 \
+    return f16 ? QNF4_FWD_LAUNCH(LS, true, 256) : QNF4_FWD_LAUNCH(LS, false, 256);
   switch (2 * Rp / KSTEP) {
-#define QNF4_FWD_CASE(LS)                                                                   \
-  case LS:                                                                                  \
-    return f16 ? timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, true>, dim3(grid), dim3(kThreads), st, W, X, M, \
-                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, splits, P, codebook()) \
-               : timed_launch(kKernFwdGemm, fwd_gemm_kernel<LS, false>, dim3(grid), dim3(kThreads), st, W, X, M, \
-                              (const uint16_t*)sT, (const uint16_t*)B2, Rp, Y, yb, tm, tn, splits, P, codebook());
     QNF4_FWD_CASE(1)
     QNF4_FWD_CASE(2)
     QNF4_FWD_CASE(3)
@@ -396,11 +428,11 @@ hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const
     QNF4_FWD_CASE(6)
     QNF4_FWD_CASE(7)
     QNF4_FWD_CASE(8)
-#undef QNF4_FWD_CASE
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+#undef QNF4_FWD_CASE
+#undef QNF4_FWD_LAUNCH
 }
 
 }  // namespace qnf4

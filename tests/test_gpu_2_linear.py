@@ -122,6 +122,7 @@ def test_qproj_gemv_m1_m16():
     (3, 136, 320, 3),      # small-M GEMV, 5 blocks per row (a ragged block group)
     (1, 200, 192, 5),
     (4, 24, 64, 1),
+    (2100, 5400, 256, 8),  # 512 x 128 forward tiles, ragged in both directions
 ])
 def test_ragged_shapes(M, N, K, r):
     print(f"ragged M={M} N={N} K={K} r={r}", flush=True)

@@ -87,7 +87,8 @@ def test_tiny_layer_fp16():
 # the last two split the GEMMs' reductions (forward 4 and 8 splits, dX 2 and
 # 4), the last with a ragged weight row count
 @pytest.mark.parametrize("M, N, K, r", [(100, 200, 320, 7), (300, 264, 576, 40), (17, 72, 64, 96),
-                                        (100, 1024, 2048, 16), (40, 2056, 4096, 8)])
+                                        (100, 1024, 2048, 16), (40, 2056, 4096, 8),
+                                        (2100, 5400, 256, 8)])  # 512 x 128 forward tiles
 def test_ragged_shapes_fp16(M, N, K, r):
     print(f"fp16 ragged M={M} N={N} K={K} r={r}", flush=True)
     rng = np.random.default_rng(M + N + K + r)

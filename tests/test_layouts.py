@@ -166,6 +166,45 @@ def test_fwd_producer_stores_cover_the_w_tile():
     assert addrs == list(range(0, 256 * 128, 16))
 
 
+@pytest.mark.parametrize("p", range(4))
+def test_fwd_tall_x_copy_lands_on_the_swizzled_tile(p):
+    # 512 x 128 tile: producer p copies X rows [128p, +128) with 16
+    # instructions of 8 rows; every row's 8 chunks land once
+    seen = set()
+    for c in range(16):
+        for lane in range(64):
+            row = 128 * p + 8 * c + (lane >> 3)
+            logical = (lane & 7) ^ rsw(lane >> 3)
+            a = (128 * p + 8 * c) * 128 + 16 * lane
+            assert a == xswz(row, logical)
+            seen.add(a)
+    assert sorted(seen) == list(range(128 * p * 128, 128 * (p + 1) * 128, 16))
+
+
+def test_fwd_tall_producer_stores_cover_the_w_tile():
+    # 512 x 128 tile: lane l of producer p owns row 32p + l % 32 and stores
+    # its chunks 4h .. 4h + 3, h = l // 32 (16 of the row's 32 bytes of codes)
+    addrs = sorted(xswz(32 * p + lane % 32, 4 * (lane // 32) + jj)
+                   for p in range(4) for lane in range(64) for jj in range(4))
+    assert addrs == list(range(0, 128 * 128, 16))
+
+
+@pytest.mark.parametrize("wave", range(8))
+def test_fwd_tall_fragment_reads_stay_in_the_tiles(wave):
+    # 4 x 2 MFMA waves of 128 x 64: A rows below 512, B rows below 128, the
+    # same measured chunk arrangement as the square tile
+    wm, wn = wave // 2, wave % 2
+    for ks in range(2):
+        for l in range(64):
+            for i in range(8):
+                ra = 128 * wm + (l & 15) + 16 * i
+                assert ra < 512
+                assert xswz(ra, 2 * (l >> 4) + ks) == ra * 128 + (((2 * (l >> 4) + ks) ^ MEASURED_FAST_X[l & 15]) << 4)
+            for j in range(4):
+                rb = 64 * wn + (l & 15) + 16 * j
+                assert rb < 128
+
+
 # ------------------------------------------------------------------- dx.hip
 
 
