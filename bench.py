@@ -451,7 +451,59 @@ def run_gemv(torch, q, args):
         del g
         log(f"[bench] GEMV M={M}: whole forward (graph-replayed) {per:.2f} us, {gbs:.0f} GB/s; "
             f"GEMV kernel {med * 1e3:.2f} us median (events)")
+    out["gate_M1"] = run_gemv_gate(torch, q, args)
     return out
+
+
+def run_gemv_gate(torch, q, args):
+    """The M = 1 forward of the 7B gate linear (11008x4096, r = 64), graph-replayed
+    over 16 quantized copies (0.36 GB, more than the last-level cache)."""
+    from workloads import device_normal
+
+    N, K, r, alpha = 11008, 4096, 64, 16.0
+    Wd = device_normal(torch, (N, K), 77, 0.02, bf16=False)
+    wsq = q.workspace(q.qlora_nf4_sizes(N, K, 0, r)["quantize_ws_bytes"])
+    copies = []
+    for _ in range(16):
+        qt = q.Nf4Tensor.empty(N, K)
+        q.qlora_nf4_quantize(Wd, qt, wsq)
+        copies.append(qt)
+    del Wd
+    A = device_normal(torch, (r, K), 78, 0.02)
+    B = device_normal(torch, (N, r), 79, 0.01)
+    X = device_normal(torch, (1, K), 81)
+    wsf = q.workspace(q.qlora_nf4_sizes(N, K, 1, r)["fwd_ws_bytes"])
+    Y = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
+    T = torch.empty(1, r, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for qt in copies:
+            q.qlora_linear_fwd(qt, X, A, B, r, alpha, Y, T, wsf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            for qt in copies:
+                q.qlora_linear_fwd(qt, X, A, B, r, alpha, Y, T, wsf)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(reps):
+        g.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    per = g0.elapsed_time(g1) / (reps * 4 * len(copies)) * 1e3
+    nbytes = gemv_forward_bytes(1, N, K, r)
+    gbs = nbytes / (per * 1e-6) / 1e9
+    del g
+    log(f"[bench] GEMV gate 11008x4096 M=1: whole forward (graph-replayed) {per:.2f} us, {gbs:.0f} GB/s")
+    return {"N": N, "K": K, "lora_rank": r, "forward_bytes": nbytes, "forward_us": round(per, 3),
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def adamw_bytes(n, param_bytes=2):

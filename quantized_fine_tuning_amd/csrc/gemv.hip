@@ -10,7 +10,15 @@
 //                           waves per 256-wide slice of K and 16 ranks, MFMA
 //                           products, the 4 waves' tiles summed in a fixed
 //                           order; a tiny grid (K/256 x r/16 workgroups).
-//   gemv_kernel             one workgroup of 16 waves per 16 weight rows.
+//   gemv_kernel             one workgroup per 16 weight rows: 16 waves, or 8
+//                           when the weight has more row groups than the
+//                           chip has compute units and X fits 32 KB (two
+//                           workgroups then stay resident per unit, and one
+//                           streams its codes while the other decodes: the
+//                           11008 x 4096 gate forward at M = 1 went from 17.6
+//                           to 15.8 us graph-replayed, M = 4 from 23.0 to
+//                           17.8; each wave then sums two block groups before
+//                           the fixed-order sum over waves).
 //                           Lane (row l % 16, q = l / 16) owns whole NF4 blocks
 //                           (64 codes, one decoded constant c'); a "block
 //                           group" is 4 consecutive blocks of the 16 rows, q
@@ -113,7 +121,7 @@ __device__ __forceinline__ void gemv_t_reduce(int nthreads, int M, int r, const 
   }
 }
 
-constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;
+constexpr int kGemvWaves = 16, kGemvThreads = 64 * kGemvWaves;  // the widest workgroup
 constexpr int kGemvXLdsBytes = 128 * 1024;  // X staged in LDS up to this size
 // The adapter term's t_fin [16][257] and s_b [16][256]: arrays of their own,
 // except with X of more than 32 KB staged (up to 128 KB), where they take
@@ -127,28 +135,29 @@ constexpr size_t kGemvAccBytes = (size_t)16 * 64 * 16 + 256;
 static_assert(kGemvAccBytes + kGemvXLdsBytes <= 160 * 1024, "X staged up to 128 KB fits the LDS");
 static_assert(kGemvAccBytes + 32 * 1024 + kGemvEpiBytes <= 160 * 1024, "X of 32 KB fits beside the epilogue arrays");
 
-// 16 waves per 16 weight rows; each wave's next block group is requested
+// WV waves per 16 weight rows; each wave's next block group is requested
 // before the current one is dequantized.  XV > 0: X (M x K bf16) is staged
 // in LDS once per workgroup, XV 16-byte pieces per thread (2: up to 32 KB,
 // 8: up to 128 KB), and the MFMA fragments are read from there; XV = 0:
 // every wave loads its fragments from global memory (the same few bytes
 // requested by every wave of every workgroup at once cost ~1.6 us at M = 1
 // on the q_proj weight, ~2 us at M = 16, measured).
-template <bool F16, int XV>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
+template <bool F16, int XV, int WV>
+__global__ __launch_bounds__(64 * WV) void gemv_kernel(Nf4View W, const uint16_t* __restrict__ X,
                                                             int M, const float* __restrict__ P, int S, int JT,
                                                             const uint16_t* __restrict__ B, int r,
                                                             float scale, void* __restrict__ Y,
                                                             int y_bf16, float* __restrict__ T_out, Codebook cb) {
+  constexpr int NW = WV, NT = 64 * WV;  // waves and threads of the workgroup
   constexpr bool XL = XV > 0;  // X staged: XV 16-byte pieces per thread
-  constexpr bool epi_late = XV > 2;  // t_fin and s_b in X's place
+  constexpr bool epi_late = XV * NT * 16 > 32 * 1024;  // t_fin and s_b in X's place
   extern __shared__ __attribute__((aligned(16))) char sx[];  // X [M][K] bf16 (XL)
   __shared__ float t_fin_own[epi_late ? 1 : kTfinFloats];
   __shared__ float s_b_own[epi_late ? 1 : kSbFloats];
   float* const t_fin = epi_late ? reinterpret_cast<float*>(sx) : t_fin_own;
   float* const s_b = epi_late ? reinterpret_cast<float*>(sx) + kTfinFloats : s_b_own;
   __shared__ __attribute__((aligned(256))) float sq[16];  // low address byte free for 4·code
-  __shared__ f32x4_t s_acc[kGemvWaves][64];
+  __shared__ f32x4_t s_acc[NW][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int64_t K = W.K, N = W.N;
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     const int nvec = (M * (int)K * 2) / 16;
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-      const int v = tid + i * kGemvThreads;
+      const int v = tid + i * NT;
       xs[i] = buf_load16(rx, v < nvec ? (uint32_t)(16 * v) : 0x7fffffffu, 0u);
     }
   }
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
   // written by the split kernel just before this launch, requested after
   // the codes (read at the start of the kernel, they took ~1.5 us longer to
   // arrive than the codes themselves) and summed in the epilogue.
-  const bool t_pre = XL && S <= kPre && M * r <= kGemvThreads;
+  const bool t_pre = XL && S <= kPre && M * r <= NT;
   float pre[kPre];
   if (t_pre && wave * 64 < M * r) {
     const int tm = tid / r, tj = tid % r;
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     const int nvec = (M * (int)K * 2) / 16;
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-      const int v = tid + i * kGemvThreads;
+      const int v = tid + i * NT;
       if (v < nvec) *reinterpret_cast<u32x4_t*>(sx + 16 * v) = xs[i];
     }
   }
@@ -281,14 +290,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
   // two groups per iteration, alternating buffers: the loads of the next
   // group are issued (and kept above the barrier to the scheduler) before
   // the current group is consumed, and no loaded register is copied
-  for (int64_t grp = wave; grp < ngroups; grp += 2 * kGemvWaves) {
-    load(gb, grp + kGemvWaves);
+  for (int64_t grp = wave; grp < ngroups; grp += 2 * NW) {
+    load(gb, grp + NW);
     __builtin_amdgcn_sched_barrier(0);
     consume(ga, grp);
-    if (grp + kGemvWaves >= ngroups) break;
-    load(ga, grp + 2 * kGemvWaves);
+    if (grp + NW >= ngroups) break;
+    load(ga, grp + 2 * NW);
     __builtin_amdgcn_sched_barrier(0);
-    consume(gb, grp + kGemvWaves);
+    consume(gb, grp + NW);
   }
   s_acc[wave][lane] = acc;
   if (epi_late) {
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
       gemv_t_store(r, tid, t, t_fin, T_out);
     }
   } else {
-    gemv_t_reduce(kGemvThreads, M, r, P, S, JT, t_fin, T_out);
+    gemv_t_reduce(NT, M, r, P, S, JT, t_fin, T_out);
   }
   __syncthreads();
   // one thread per output (token m, weight row n0 + c): the 16 partial
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Nf4View W, const uin
     if (m < M && nn < N) {
       float y = s_acc[0][16 * (m >> 2) + c][m & 3];
 #pragma unroll
-      for (int w = 1; w < kGemvWaves; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
+      for (int w = 1; w < NW; ++w) y = __fadd_rn(y, s_acc[w][16 * (m >> 2) + c][m & 3]);
       float dot = 0.0f;
       for (int j = 0; j < r; ++j) dot = __fadd_rn(dot, __fmul_rn(t_fin[m * 257 + j], s_b[c * r + j]));
       y = __fadd_rn(y, __fmul_rn(scale, dot));
@@ -348,17 +357,22 @@ hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uin
   const int yb = y16 ? 1 : 0;
   const size_t xb = (size_t)M * W.K * 2;
   const bool xl = xb <= (size_t)kGemvXLdsBytes;
-  const bool x2 = xb <= (size_t)kGemvThreads * 16 * 2;
+  const bool x2 = xb <= 32 * 1024;
   const size_t shm = x2 ? xb : (xl ? std::max(xb, kGemvEpiBytes) : 0);
-#define QNF4_GEMV_LAUNCH(XV)                                                                                    \
-  return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, XV>, dim3(grid), dim3(kGemvThreads), shm, st, W, X, \
+  // More row groups than compute units: workgroups of 8 waves, two resident
+  // per compute unit, so that the next workgroup's codes stream while one
+  // decodes; otherwise 16 waves, one workgroup per unit.
+  const bool narrow = grid > 256 && xb <= 32 * 1024;
+#define QNF4_GEMV_LAUNCH(XV, WV)                                                                                \
+  return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, XV, WV>, dim3(grid), dim3(64 * WV), shm, st, W, X, \
                                 (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())      \
-             : timed_launch_shm(kKernGemv, gemv_kernel<false, XV>, dim3(grid), dim3(kGemvThreads), shm, st, W, X, \
+             : timed_launch_shm(kKernGemv, gemv_kernel<false, XV, WV>, dim3(grid), dim3(64 * WV), shm, st, W, X, \
                                 (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
   // X staged with 2 or 8 pieces of 16 bytes per thread (up to 32 or 128 KB)
-  if (x2) QNF4_GEMV_LAUNCH(2);
-  if (xl) QNF4_GEMV_LAUNCH(8);
-  QNF4_GEMV_LAUNCH(0);
+  if (narrow) QNF4_GEMV_LAUNCH(4, 8);
+  if (x2) QNF4_GEMV_LAUNCH(2, 16);
+  if (xl) QNF4_GEMV_LAUNCH(8, 16);
+  QNF4_GEMV_LAUNCH(0, 16);
 #undef QNF4_GEMV_LAUNCH
 }
 

@@ -105,6 +105,36 @@ def test_identity_input_gives_weight_bit_exact():
     assert np.all(G.host(dA) == 0)
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_gemv_eight_wave_workgroups(M):
+    # more 16-row groups than compute units (N = 4104: 257 groups) with X of
+    # at most 32 KB: the 8-wave workgroups; K = 2368 is 37 blocks, 10 block
+    # groups per row (the last of one block), so waves 0 and 1 sum two
+    N, K, r = 4104, 2368, 12
+    print(f"8-wave GEMV N={N} K={K} M={M} r={r}", flush=True)
+    W = random_f32((N, K), seed=41 + M, scale=0.02)
+    L = Layer(W, random_bf16((M, K), seed=42 + M), random_bf16((r, K), seed=43, scale=0.02),
+              random_bf16((N, r), seed=44, scale=0.01))
+    run_fwd(L, r, 2.0 * r)
+
+
+def test_gemv_eight_wave_identity_bit_exact():
+    # one-hot rows of X and B = 0 through the 8-wave workgroups: every output
+    # is one exact product, Y[m][n] = Ŵ[n][k_m]
+    t = torch()
+    N, K = 4104, 2368
+    W = random_f32((N, K), seed=45, scale=0.02)
+    ks = [0, 63, 64, 1000, 2303, 2367]
+    from workloads import to_bf16_bits
+    X = np.zeros((len(ks), K), np.float32)
+    for i, k in enumerate(ks):
+        X[i, k] = 1.0
+    L = Layer(W, to_bf16_bits(X), random_bf16((4, K), seed=46, scale=0.02), np.zeros((N, 4), np.uint16))
+    Y, _ = G.gpu_forward(L.qt, L.Xd, L.Ad, L.Bd, 4, 8.0, t.bfloat16)
+    w_hat_bits = G.oracle_w_hat(L.ref).reshape(N, K)
+    assert np.array_equal(G.host_bf16(Y), w_hat_bits[:, ks].T)
+
+
 def test_qproj_gemv_m1_m16():
     w = Inputs(2)
     for M in (1, 3, 4, 5, 16):  # the 4-wave kernel takes M <= 4, the 16-wave one the rest
