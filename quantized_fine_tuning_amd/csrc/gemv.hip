@@ -7,7 +7,11 @@
 // Two launches:
 //
 //   lora_down_split_kernel  partial products of T = X·Aᵀ: one workgroup of 4
-//                           waves per 256-wide slice of K and 16 ranks, MFMA
+//                           waves per slice of K (256 wide, wider above
+//                           K = 4096 so that there are at most 16 slices:
+//                           768 at K = 11008, where the down projection's
+//                           forward at M = 4 went from 16.4 to 15.0 us) and
+//                           16 ranks, MFMA
 //                           products, the 4 waves' tiles summed in a fixed
 //                           order; a tiny grid (K/256 x r/16 workgroups).
 //   gemv_kernel             one workgroup per 16 weight rows: 16 waves, or 8
@@ -53,13 +57,21 @@ namespace qnf4 {
 namespace {
 
 constexpr int GEMV_ROWS = 16;
-constexpr int kTSlice = 256;  // reduction elements per T partial tile
+constexpr int kTSlice = 256;  // reduction elements per T partial tile (the narrowest)
+constexpr int kPre = 16;       // partial tiles a GEMV thread requests at its start
+// Slice width for a reduction of K: 256, or a multiple of 256 that keeps
+// the slice count within kPre (up to 1024, K <= 16384), so that every GEMV
+// thread requests its partial tiles right after its codes.
+inline int t_slice(int64_t K) {
+  const int64_t u = (K + (int64_t)kTSlice * kPre - 1) / ((int64_t)kTSlice * kPre);
+  return kTSlice * (int)(u < 1 ? 1 : (u > 4 ? 4 : u));
+}
 
 // Partial tiles of T = X·Aᵀ: workgroup (s, jt) sums k in [256s, 256s + 256)
 // for ranks [16jt, +16) and all 16 token rows (rows past M and ranks past r
 // read as zero), 4 waves of 64 k each, and writes the 16 x 16 tile
 // P[(s * JT + jt) * 256 + 16m + j] (fp32).
-template <bool F16>
+template <bool F16, int UC>
 __global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
                                                               const uint16_t* __restrict__ A, int r,
                                                               float* __restrict__ P) {
@@ -71,16 +83,17 @@ __global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __
   const int64_t j0 = 16 * jt;
   const rsrc_t ra = make_rsrc(A + j0 * K, ((int64_t)r - j0) * K * 2);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4_t xa[2], ab[2];
+  // slice of 128·UC reduction elements: wave w takes [32·UC·w, +32·UC)
+  u32x4_t xa[UC], ab[UC];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t k = slice * kTSlice + 64 * wave + 32 * u + 8 * kq;
+  for (int u = 0; u < UC; ++u) {
+    const int64_t k = slice * (128 * UC) + 32 * UC * wave + 32 * u + 8 * kq;
     const uint32_t off = k < K ? (uint32_t)((lr * K + k) * 2) : 0x7fffffffu;
     xa[u] = buf_load16(rx, off, 0u);
     ab[u] = buf_load16(ra, off, 0u);
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) acc = mfma16<F16>(xa[u], ab[u], acc);
+  for (int u = 0; u < UC; ++u) acc = mfma16<F16>(xa[u], ab[u], acc);
   s_acc[wave][lane] = acc;
   __syncthreads();
   // thread (m, j): lane 16(m/4) + j holds token m in component m%4
@@ -97,7 +110,6 @@ __global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __
 // writes T_out.  With at most kPre slices and one entry per thread the
 // thread's partials were requested at the start of the kernel (`pre`);
 // otherwise gemv_t_reduce loads them, 16 at a time, all independent.
-constexpr int kPre = 16;
 __device__ __forceinline__ void gemv_t_store(int r, int idx, float t, float* t_fin, float* __restrict__ T_out) {
   t_fin[(idx / r) * 257 + idx % r] = t;
   if (T_out && blockIdx.x == 0) T_out[idx] = t;
@@ -340,17 +352,28 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(Nf4View W, const uint16_t
 }  // namespace
 
 size_t gemv_partial_bytes(int64_t K, int32_t r) {
-  return (size_t)((K + kTSlice - 1) / kTSlice) * (size_t)((r + 15) / 16) * 256 * 4;
+  const int sl = t_slice(K);
+  return (size_t)((K + sl - 1) / sl) * (size_t)((r + 15) / 16) * 256 * 4;
 }
 
 hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
                        int32_t r, float scale, void* Y, bool y16, float* T, float* P, bool f16, hipStream_t st) {
-  const int S = (int)((W.K + kTSlice - 1) / kTSlice), JT = (r + 15) / 16;
+  const int sl = t_slice(W.K);
+  const int S = (int)((W.K + sl - 1) / sl), JT = (r + 15) / 16;
   const dim3 tg((unsigned)S, (unsigned)JT);
-  if (f16)
-    lora_down_split_kernel<true><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);
-  else
-    lora_down_split_kernel<false><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);
+  // 128·UC reduction elements per slice: UC = 2, 4, 6 or 8
+#define QNF4_SPLIT_LAUNCH(UC)                                                                  \
+  if (f16)                                                                                     \
+    lora_down_split_kernel<true, UC><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);             \
+  else                                                                                         \
+    lora_down_split_kernel<false, UC><<<tg, 256, 0, st>>>(X, (int)M, W.K, A, r, P);
+  switch (sl / 128) {
+    case 2: QNF4_SPLIT_LAUNCH(2) break;
+    case 4: QNF4_SPLIT_LAUNCH(4) break;
+    case 6: QNF4_SPLIT_LAUNCH(6) break;
+    default: QNF4_SPLIT_LAUNCH(8) break;
+  }
+#undef QNF4_SPLIT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((W.N + GEMV_ROWS - 1) / GEMV_ROWS);
