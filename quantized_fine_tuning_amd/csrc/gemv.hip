@@ -11,9 +11,9 @@
 //                           K = 4096 so that there are at most 16 slices:
 //                           768 at K = 11008, where the down projection's
 //                           forward at M = 4 went from 16.4 to 15.0 us) and
-//                           16 ranks, MFMA
-//                           products, the 4 waves' tiles summed in a fixed
-//                           order; a tiny grid (K/256 x r/16 workgroups).
+//                           16 ranks, MFMA products, the 4 waves' tiles
+//                           summed in a fixed order; a tiny grid
+//                           (K/slice x r/16 workgroups).
 //   gemv_kernel             one workgroup per 16 weight rows: 16 waves, or 8
 //                           when the weight has more row groups than the
 //                           chip has compute units and X fits 32 KB (two
@@ -67,10 +67,10 @@ inline int t_slice(int64_t K) {
   return kTSlice * (int)(u < 1 ? 1 : (u > 4 ? 4 : u));
 }
 
-// Partial tiles of T = X·Aᵀ: workgroup (s, jt) sums k in [256s, 256s + 256)
-// for ranks [16jt, +16) and all 16 token rows (rows past M and ranks past r
-// read as zero), 4 waves of 64 k each, and writes the 16 x 16 tile
-// P[(s * JT + jt) * 256 + 16m + j] (fp32).
+// Partial tiles of T = X·Aᵀ: workgroup (s, jt) sums k in [128·UC·s, +128·UC)
+// for ranks [16jt, +16) and all 16 token rows (rows past M, ranks past r and
+// k past K read as zero), 4 waves of 32·UC k each, and writes the 16 x 16
+// tile P[(s * JT + jt) * 256 + 16m + j] (fp32).
 template <bool F16, int UC>
 __global__ __launch_bounds__(256) void lora_down_split_kernel(const uint16_t* __restrict__ X, int M, int64_t K,
                                                               const uint16_t* __restrict__ A, int r,
