@@ -5,8 +5,9 @@
 //
 // Design
 //   * One output tile per workgroup of 12 waves, three per SIMD, in two
-//     roles; the tile is 256x256, or 512x128 from 2048 tokens on (one
-//     kernel template, TMV = 256 or 512 token rows).  Waves 0..7 only
+//     roles; the tile is 256x256, or 512x128 from 2048 tokens on and from
+//     512 on where it adds no padding rows (one kernel template, TMV = 256 or
+//     512 token rows).  Waves 0..7 only
 //     multiply: wave (wm, wn) owns token rows [128wm, +128) and weight rows
 //     [64wn, +64) of the tile (2 x 4 waves, or 4 x 2), 64
 //     v_mfma_f32_16x16x32_bf16 per 64-wide reduction step, operands read
@@ -19,8 +20,8 @@
 //     tokens: half the producers' decode per MFMA for twice their X copy
 //     (64 KB of X and 16 KB of Ŵ per step, 160 KB of LDS with both
 //     buffers).  On the 7B MLP shapes it takes the forward GEMM from ≈322 to
-//     ≈310 µs (bit-identical output); below 2048 tokens, or with a split
-//     reduction, its 512-row tiles would be mostly padding.
+//     ≈310 µs (bit-identical output), at 1,024–1,536 tokens by 4-6 % (with
+//     or without a split reduction).
 //   * Dequantization in registers: producer p owns tile rows
 //     [WR p, +WR) (WR = 64 or 32): lane l takes row WR p + l % WR and, when
 //     two lanes share a row, half l / WR of its 64 codes.  Per step a lane
@@ -66,7 +67,12 @@ namespace {
 constexpr int TM = 256, TN = 256, KSTEP = 64;  // the square tile (split plans)
 constexpr int kMfmaWaves = 8, kProdWaves = 4, kWaves = kMfmaWaves + kProdWaves;
 constexpr int kThreads = 64 * kWaves;
-constexpr int64_t kTallMinTokens = 2048;  // 512 x 128 tiles from here on
+// 512 x 128 tiles from 2048 tokens on, and from 512 tokens on where they
+// add no padding rows over 256-row tiles
+constexpr int64_t kTallMinTokens = 512, kTallAlwaysTokens = 2048;
+inline bool fwd_tall(int64_t M) {
+  return M >= kTallAlwaysTokens || (M >= kTallMinTokens && ((M + 255) / 256) % 2 == 0);
+}
 
 // A tile row = 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at
 // physical chunk c ^ sw(r & 7), where sw swaps bits 0 and 1 of its argument.
@@ -405,9 +411,9 @@ int fwd_gemm_splits(int64_t M, int64_t N, int64_t K, size_t cap) {
 hipError_t launch_fwd_gemm(const Nf4View& W, const uint16_t* X, int64_t M, const uint16_t* sT,
                            const uint16_t* B2, int64_t Rp, void* Y, bool y16, int splits, float* P, bool f16,
                            hipStream_t st) {
-  // 512 x 128 tiles from 2048 tokens on (whole 512-row tiles dominate),
-  // 256 x 256 below and whenever the reduction is split
-  const bool tall = splits == 1 && M >= kTallMinTokens;
+  // 512 x 128 tiles (also with a split reduction: the split ranges, and so
+  // every output's order of additions, are those of the square tile)
+  const bool tall = fwd_tall(M);
   const int tmv = tall ? 512 : 256;
   const int tm = (int)((M + tmv - 1) / tmv), tn = (int)((W.N + 65536 / tmv - 1) / (65536 / tmv));
   const unsigned grid = tile_grid(tm, tn, splits);

@@ -153,6 +153,7 @@ def test_qproj_gemv_m1_m16():
     (1, 200, 192, 5),
     (4, 24, 64, 1),
     (2100, 5400, 256, 8),  # 512 x 128 forward tiles, ragged in both directions
+    (1024, 1000, 1024, 8),  # 512 x 128 forward tiles with a 2-way split reduction
 ])
 def test_ragged_shapes(M, N, K, r):
     print(f"ragged M={M} N={N} K={K} r={r}", flush=True)

@@ -88,7 +88,8 @@ def test_tiny_layer_fp16():
 # 4), the last with a ragged weight row count
 @pytest.mark.parametrize("M, N, K, r", [(100, 200, 320, 7), (300, 264, 576, 40), (17, 72, 64, 96),
                                         (100, 1024, 2048, 16), (40, 2056, 4096, 8),
-                                        (2100, 5400, 256, 8)])  # 512 x 128 forward tiles
+                                        (2100, 5400, 256, 8),  # 512 x 128 forward tiles
+                                        (1024, 1000, 1024, 8)])  # the same with a split reduction
 def test_ragged_shapes_fp16(M, N, K, r):
     print(f"fp16 ragged M={M} N={N} K={K} r={r}", flush=True)
     rng = np.random.default_rng(M + N + K + r)
@@ -96,6 +97,27 @@ def test_ragged_shapes_fp16(M, N, K, r):
     h = lambda a: nf4.f16_bits(a.astype(np.float32))  # noqa: E731
     run_layer(W32, h(rng.standard_normal((M, K))), h(rng.standard_normal((r, K)) * 0.02),
               h(rng.standard_normal((N, r)) * 0.01), h(rng.standard_normal((M, N))), r, 2.0 * r)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_gemv_eight_wave_workgroups_fp16(M):
+    # the 8-wave GEMV workgroups (257 row groups, X within 32 KB) in fp16;
+    # ragged last row group and block groups (K = 2368: 37 blocks)
+    t = torch()
+    N, K, r = 4104, 2368, 12
+    print(f"fp16 8-wave GEMV N={N} K={K} M={M}", flush=True)
+    rng = np.random.default_rng(N + K + M)
+    W32 = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    h = lambda a: nf4.f16_bits(a.astype(np.float32))  # noqa: E731
+    X, A, B = h(rng.standard_normal((M, K))), h(rng.standard_normal((r, K)) * 0.02), h(rng.standard_normal((N, r)) * 0.01)
+    qt = G.gpu_quantize(G.dev_f32(W32))
+    W_hat = w_hat_f16(nf4.quantize(W32), W32.shape)
+    Yh, _ = G.gpu_forward(qt, dev_f16(X), dev_f16(A), dev_f16(B), r, 2.0 * r, t.float16)
+    Yf, _ = G.gpu_forward(qt, dev_f16(X), dev_f16(A), dev_f16(B), r, 2.0 * r, t.float32)
+    Y_ref, _ = linalg.linear_fwd(f64(X), W_hat, f64(A), f64(B), 2.0 * r, r)
+    e2 = G.assert_close(G.out_f64(Yf), Y_ref, G.TOL_F32, "Y fp32")
+    e1 = G.assert_close(G.out_f64(Yh), Y_ref, G.TOL_BF16, "Y fp16")
+    print(f"  Y fp16 {e1:.2e} fp32 {e2:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("M", [1, 16])
