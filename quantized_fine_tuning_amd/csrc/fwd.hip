@@ -232,8 +232,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   }
 
   // ------------------------------------------------------------ producers
-  // Producer p dequantizes weight rows [64p, 64p + 64) and copies X rows
-  // [64p, +64) of every step.
+  // Producer p dequantizes weight rows [WR p, +WR) and copies X rows
+  // [XR p, +XR) of every step (WR = XR = 64 on the square tile; WR = 32,
+  // XR = 128 on the tall one).
   const int p = wave - kMfmaWaves;
   const uint32_t kpr = (uint32_t)(K / kBlock);  // blocks per weight row
   const float mu = *W.mu;
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   const rsrc_t rs = make_rsrc(W.s, ((N * kpr + kDqBlock - 1) / kDqBlock) * 4);
   const rsrc_t rb = make_rsrc(B2 + n0 * 2 * Rp, (N - n0) * 2 * Rp * 2);
 
-  // X rows [64p, +64) of a step, copied straight into LDS: part c
-  // moves rows 64p + 8c + (l >> 3), lane l into physical chunk l & 7, so it
+  // X rows [XR p, +XR) of a step, copied straight into LDS: part c
+  // moves rows XR p + 8c + (l >> 3), lane l into physical chunk l & 7, so it
   // fetches logical chunk (l & 7) ^ sw(l >> 3) (row & 7 = l >> 3).  Each
   // instruction fills 1 KB of LDS contiguously.  (Written as assembly: the
   // compiler then inserts no wait for these copies in front of the
@@ -272,8 +273,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   using XRows = std::integral_constant<int, XR>;
   using WRows = std::integral_constant<int, WR>;
 
-  // Row trow = 64p + lane of the tile is this lane's: the dword holding its
-  // e4m3 byte and its group scale, its 32 bytes of codes per step.
+  // Row trow = WR p + lane % WR of the tile is this lane's: the dword
+  // holding its e4m3 byte and its group scale, and per step its 32 bytes of
+  // codes (the 16 of half lane / WR when two lanes share the row).
   const int trow = WR * p + lane % WR, half = lane / WR;
   const uint32_t ve_me = (uint32_t)trow * kpr;
   const uint32_t blk_me = (uint32_t)(n0 + trow) * kpr;
