@@ -154,6 +154,8 @@ def test_qproj_gemv_m1_m16():
     (4, 24, 64, 1),
     (2100, 5400, 256, 8),  # 512 x 128 forward tiles, ragged in both directions
     (1024, 1000, 1024, 8),  # 512 x 128 forward tiles with a 2-way split reduction
+    (1536, 200, 192, 5),   # 512 x 128 forward tiles, rank padded to 32 (one LoRA step)
+    (2048, 520, 320, 40),  # 512 x 128 forward tiles, rank padded to 64 (two LoRA steps)
     (5, 136, 8192, 16),    # GEMV, T from 16 slices of 512 (65B q_proj width)
     (2, 264, 22016, 8),    # GEMV, T from 22 slices of 1024, summed in the epilogue
 ])
