@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
   // at a time) plus the constant 256i.  Column pair cp2 = columns 2cp2,
   // 2cp2 + 1: with `overlap` (producers) the lookups of the second pair are
   // in flight while the first is packed and stored; the MFMA waves, short of
-  // registers, take the pairs one after the other.
+  // registers, keep one column's lookups in flight while the previous column
+  // is packed and stored.
   const int code_rslot = 8 * rg + (cg ^ rg);
   const uint32_t rg32x4 = (uint32_t)rg * 0x20202020u;
   auto read_codes = [&](int t, int sigma) __attribute__((always_inline)) {
@@ -179,22 +180,32 @@ __global__ __launch_bounds__(kThreads, 1) void dx_gemm_kernel(Nf4View W, const u
       store_cols(sw[t & 1], st0, 0, v0);
       store_cols(sw[t & 1], st0, 1, v1);
     } else {
-      // one column at a time, addresses straight from the code dwords and
-      // lane offsets recomputed here from an opaque copy of the lane index
-      // (kept from being hoisted out of the MFMA waves' loop, where they
-      // would hold registers through the MFMAs)
+      // addresses straight from the code dwords and lane offsets recomputed
+      // here from an opaque copy of the lane index (kept from being hoisted
+      // out of the MFMA waves' loop, where they would hold registers through
+      // the MFMAs)
       const int ln = opaque(lane), lrg = dq_rg(ln), lcg = dq_cg(ln);
       const uint32_t lb = lds_offset(stab[t & 1][sigma >> 1]) + 32u * (uint32_t)lrg;
       const uint32_t st0 =
           (uint32_t)((32 * sigma + 4 * lcg) * 128 + ((lrg ^ ((lcg >> 1) & 1) ^ (4 * (lcg & 1))) << 4));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t v[8];
+      // column c + 1's lookups are issued before column c is packed and
+      // stored; each lookup address leaves its row offset 256i to the
+      // instruction's offset field (the opaque copy keeps the compiler from
+      // folding it into eight per-row base registers, which the second
+      // column's values need; ≈0.7 % on the kernel)
+      auto look_col = [&](int c, uint32_t* v) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            v[2 * p + h] = lds_read_u16((lb | code_x2(cw[p], 16 * h + 4 * c)) + 256u * (2 * p + h));
+            v[2 * p + h] = lds_read_u16(opaque(lb | code_x2(cw[p], 16 * h + 4 * c)) + 256u * (2 * p + h));
+      };
+      uint32_t va[8], vb[8];
+      look_col(0, va);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t* const v = (c & 1) ? vb : va;
+        if (c < 3) look_col(c + 1, (c & 1) ? va : vb);
         issue(c);
         __builtin_amdgcn_sched_barrier(0x8 | 0x4 | 0x10);
         asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),
