@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gemm_kernel(Nf4View W, const 
   __shared__ __attribute__((aligned(16))) char sx0[TM * 128], sx1[TM * 128];  // A tiles: X, then sT
   __shared__ __attribute__((aligned(16))) char sw[2][TN * 128];  // B tiles: Ŵ, then B2
   int tmi, tni, sp;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_n, splits, tmi, tni, sp)) return;
+  if (!tile_of<TMV == 512 ? 2 : kGroupM>(blockIdx.x, tiles_m, tiles_n, splits, tmi, tni, sp)) return;
 
   // (the wave index in a scalar register: the LDS addresses and offsets of
   // the copies derived from it are then formed by scalar instructions)
