@@ -14,15 +14,18 @@
 //                           16 ranks, MFMA products, the 4 waves' tiles
 //                           summed in a fixed order; a tiny grid
 //                           (K/slice x r/16 workgroups).
-//   gemv_kernel             one workgroup per 16 weight rows: 16 waves, or 8
+//   gemv_kernel             one workgroup per 16 weight rows: 16 waves, or,
 //                           when the weight has more row groups than the
-//                           chip has compute units and X fits 32 KB (two
-//                           workgroups then stay resident per unit, and one
-//                           streams its codes while the other decodes: the
-//                           11008 x 4096 gate forward at M = 1 went from 17.6
-//                           to 15.8 us graph-replayed, M = 4 from 23.0 to
-//                           17.8; each wave then sums two block groups before
-//                           the fixed-order sum over waves).
+//                           chip has compute units, 8 waves if X fits 32 KB
+//                           (two workgroups resident per unit, one streaming
+//                           its codes while the other decodes: the 11008 x
+//                           4096 gate forward at M = 4 went from 23.0 to
+//                           17.8 us graph-replayed) and 4 waves if it fits
+//                           8 KB (three per unit: all 688 row groups of the
+//                           gate resident at once; M = 1 went from 17.6 us
+//                           with 16 waves and 15.7 with 8 to 14.4).  Each
+//                           wave sums its block groups in order before the
+//                           fixed-order sum over waves.
 //                           Lane (row l % 16, q = l / 16) owns whole NF4 blocks
 //                           (64 codes, one decoded constant c'); a "block
 //                           group" is 4 consecutive blocks of the 16 rows, q
@@ -382,16 +385,21 @@ hipError_t launch_gemv(const Nf4View& W, const uint16_t* X, int64_t M, const uin
   const bool xl = xb <= (size_t)kGemvXLdsBytes;
   const bool x2 = xb <= 32 * 1024;
   const size_t shm = x2 ? xb : (xl ? std::max(xb, kGemvEpiBytes) : 0);
-  // More row groups than compute units: workgroups of 8 waves, two resident
+  // More row groups than compute units: workgroups of 8 waves (two resident
   // per compute unit, so that the next workgroup's codes stream while one
-  // decodes; otherwise 16 waves, one workgroup per unit.
+  // decodes), or of 4 with X within 8 KB (three resident: every row group
+  // of a 688-group weight at once) and r <= 128 (the workgroup's 16 B rows
+  // are staged 16 bytes a thread); otherwise 16 waves, one workgroup per
+  // unit.
   const bool narrow = grid > 256 && xb <= 32 * 1024;
+  const bool four = narrow && xb <= 8 * 1024 && 2 * r <= 64 * 4;
 #define QNF4_GEMV_LAUNCH(XV, WV)                                                                                \
   return f16 ? timed_launch_shm(kKernGemv, gemv_kernel<true, XV, WV>, dim3(grid), dim3(64 * WV), shm, st, W, X, \
                                 (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())      \
              : timed_launch_shm(kKernGemv, gemv_kernel<false, XV, WV>, dim3(grid), dim3(64 * WV), shm, st, W, X, \
                                 (int)M, (const float*)P, S, JT, B, r, scale, Y, yb, T, codebook())
   // X staged with 2 or 8 pieces of 16 bytes per thread (up to 32 or 128 KB)
+  if (four) QNF4_GEMV_LAUNCH(2, 4);
   if (narrow) QNF4_GEMV_LAUNCH(4, 8);
   if (x2) QNF4_GEMV_LAUNCH(2, 16);
   if (xl) QNF4_GEMV_LAUNCH(8, 16);

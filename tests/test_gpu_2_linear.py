@@ -105,22 +105,26 @@ def test_identity_input_gives_weight_bit_exact():
     assert np.all(G.host(dA) == 0)
 
 
-@pytest.mark.parametrize("M", [1, 3])
-def test_gemv_eight_wave_workgroups(M):
-    # more 16-row groups than compute units (N = 4104: 257 groups) with X of
-    # at most 32 KB: the 8-wave workgroups; K = 2368 is 37 blocks, 10 block
-    # groups per row (the last of one block), so waves 0 and 1 sum two
-    N, K, r = 4104, 2368, 12
-    print(f"8-wave GEMV N={N} K={K} M={M} r={r}", flush=True)
+@pytest.mark.parametrize("M,r", [(1, 12), (3, 12), (1, 128), (1, 256)])
+def test_gemv_narrow_workgroups(M, r):
+    # more 16-row groups than compute units (N = 4104: 257 groups): 4-wave
+    # workgroups with X within 8 KB and r <= 128 (M = 1), else 8-wave ones
+    # with X within 32 KB (M = 3, and r = 256, whose B rows need 512
+    # threads to stage); K = 2368 is 37 blocks, 10 block groups per row (the
+    # last of one block), so the waves sum two or three each
+    N, K = 4104, 2368
+    print(f"narrow GEMV N={N} K={K} M={M} r={r}", flush=True)
     W = random_f32((N, K), seed=41 + M, scale=0.02)
     L = Layer(W, random_bf16((M, K), seed=42 + M), random_bf16((r, K), seed=43, scale=0.02),
               random_bf16((N, r), seed=44, scale=0.01))
     run_fwd(L, r, 2.0 * r)
 
 
-def test_gemv_eight_wave_identity_bit_exact():
-    # one-hot rows of X and B = 0 through the 8-wave workgroups: every output
-    # is one exact product, Y[m][n] = Ŵ[n][k_m]
+@pytest.mark.parametrize("rows", [6, 1])
+def test_gemv_narrow_identity_bit_exact(rows):
+    # one-hot rows of X and B = 0 through the 8-wave workgroups (6 rows per
+    # call) and the 4-wave ones (one row per call): every output is one
+    # exact product, Y[m][n] = Ŵ[n][k_m]
     t = torch()
     N, K = 4104, 2368
     W = random_f32((N, K), seed=45, scale=0.02)
@@ -130,14 +134,15 @@ def test_gemv_eight_wave_identity_bit_exact():
     for i, k in enumerate(ks):
         X[i, k] = 1.0
     L = Layer(W, to_bf16_bits(X), random_bf16((4, K), seed=46, scale=0.02), np.zeros((N, 4), np.uint16))
-    Y, _ = G.gpu_forward(L.qt, L.Xd, L.Ad, L.Bd, 4, 8.0, t.bfloat16)
     w_hat_bits = G.oracle_w_hat(L.ref).reshape(N, K)
-    assert np.array_equal(G.host_bf16(Y), w_hat_bits[:, ks].T)
+    for i0 in range(0, len(ks), rows):
+        Y, _ = G.gpu_forward(L.qt, L.Xd[i0:i0 + rows], L.Ad, L.Bd, 4, 8.0, t.bfloat16)
+        assert np.array_equal(G.host_bf16(Y), w_hat_bits[:, ks[i0:i0 + rows]].T)
 
 
 def test_qproj_gemv_m1_m16():
     w = Inputs(2)
-    for M in (1, 3, 4, 5, 16):  # the 4-wave kernel takes M <= 4, the 16-wave one the rest
+    for M in (1, 3, 4, 5, 16):  # X staged 2 pieces a thread up to M = 4, 8 above
         print(f"q_proj 4096x4096 M={M} r=16", flush=True)
         L = Layer.from_workload(2, 0, M)
         run_fwd(L, w.w.rank, w.w.alpha)

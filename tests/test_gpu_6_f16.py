@@ -100,12 +100,13 @@ def test_ragged_shapes_fp16(M, N, K, r):
 
 
 @pytest.mark.parametrize("M", [1, 3])
-def test_gemv_eight_wave_workgroups_fp16(M):
-    # the 8-wave GEMV workgroups (257 row groups, X within 32 KB) in fp16;
-    # ragged last row group and block groups (K = 2368: 37 blocks)
+def test_gemv_narrow_workgroups_fp16(M):
+    # the narrow GEMV workgroups (257 row groups) in fp16: 4 waves at M = 1
+    # (X within 8 KB), 8 at M = 3 (within 32 KB); ragged last row group and
+    # block groups (K = 2368: 37 blocks)
     t = torch()
     N, K, r = 4104, 2368, 12
-    print(f"fp16 8-wave GEMV N={N} K={K} M={M}", flush=True)
+    print(f"fp16 narrow GEMV N={N} K={K} M={M}", flush=True)
     rng = np.random.default_rng(N + K + M)
     W32 = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     h = lambda a: nf4.f16_bits(a.astype(np.float32))  # noqa: E731
