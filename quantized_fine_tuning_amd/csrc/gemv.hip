@@ -152,8 +152,9 @@ static_assert(kGemvAccBytes + 32 * 1024 + kGemvEpiBytes <= 160 * 1024, "X of 32 
 
 // WV waves per 16 weight rows; each wave's next block group is requested
 // before the current one is dequantized.  XV > 0: X (M x K bf16) is staged
-// in LDS once per workgroup, XV 16-byte pieces per thread (2: up to 32 KB,
-// 8: up to 128 KB), and the MFMA fragments are read from there; XV = 0:
+// in LDS once per workgroup, XV 16-byte pieces per thread (XV·WV KB: 32 KB
+// for (2, 16) and (4, 8), 8 KB for (2, 4), 128 KB for (8, 16)), and the
+// MFMA fragments are read from there; XV = 0:
 // every wave loads its fragments from global memory (the same few bytes
 // requested by every wave of every workgroup at once cost ~1.6 us at M = 1
 // on the q_proj weight, ~2 us at M = 16, measured).
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(Nf4View W, const uint16_t
                                                             float scale, void* __restrict__ Y,
                                                             int y_bf16, float* __restrict__ T_out, Codebook cb) {
   constexpr int NW = WV, NT = 64 * WV;  // waves and threads of the workgroup
+  static_assert(NT >= 16 * GEMV_ROWS, "one thread per output of a 16-token x 16-row tile");
   constexpr bool XL = XV > 0;  // X staged: XV 16-byte pieces per thread
   constexpr bool epi_late = XV * NT * 16 > 32 * 1024;  // t_fin and s_b in X's place
   extern __shared__ __attribute__((aligned(16))) char sx[];  // X [M][K] bf16 (XL)
